@@ -1,0 +1,18 @@
+// Version and status strings of the C ABI declared in include/moe_ffn.h.
+#include "common.h"
+
+extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+extern "C" const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range";
+    case MOE_ERR_ALIGN: return "a size is not a multiple of what the layout requires";
+    case MOE_ERR_CAPACITY: return "M_cap cannot hold the worst-case grouped layout";
+    case MOE_ERR_UNSUPPORTED: return "unsupported enum or parameter value";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}

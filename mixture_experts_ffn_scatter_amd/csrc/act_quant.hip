@@ -1,0 +1,193 @@
+// moe_act_quant_liverows: SiLU(gate)*up + FP8/UE8M0 quantisation of the
+// live rows of the grouped layout, on gfx950.
+//
+// "Blackwell FP4 MoE: live-row boundary", sections 1-3: the activation kernel
+// receives the same int32 endpoints as the GEMMs, visits only [start, end)
+// of each expert and leaves padding unwritten. "Blackwell DeepGEMM FusedMoE
+// (sglang)", section 2.4: activation and quantisation are fused so gate/up
+// is read once and FP8 + packed scales are written once; SiLU stays fp32.
+//
+// Work decomposition: a persistent grid walks 16-row units of
+// [0, end of the last expert). Each wave takes 4 rows of a unit; a row is
+// processed only if it lies inside some [start_e, end_e) (wave-uniform test).
+// A lane owns 8 consecutive columns of each 512-column chunk (16-byte loads
+// of gate and up, 8-byte stores of codes), a 32-column group spans 4 lanes
+// (amax by two shuffles), a packed scale word spans 16 lanes. The words of
+// the unit's 16 rows are staged in LDS and stored MN-major so that each
+// scale row receives one contiguous 64-byte run.
+//
+// Arithmetic per element, all IEEE fp32 with no contraction:
+//   g = bf16 gate, u = bf16 up; optional clamp g = min(g, L), u = med3(u, -L, L)
+//   sig = sigma(g) correctly rounded (looked up in LDS by g's bf16 pattern)
+//   h = (g * sig) * u
+// and per 32-column group: b = UE8M0 round-up of amax/448, code =
+// e4m3_rne(h * 2^(127-b)).
+#include <cstring>
+
+#include "common.h"
+
+namespace moe {
+
+// sigma(g) for every bf16 g, generated at build time (gen_sigmoid_table.cpp)
+#define MOE_SIGMOID_TABLE_STORAGE __device__ const
+#include "sigmoid_table.inc"
+
+constexpr int kActThreads = 256;
+constexpr int kActUnitRows = 16;
+constexpr int kActMaxE = 1024;
+constexpr int kActMaxWordsPerRow = 64;  // I <= 8192
+
+__device__ __forceinline__ float sigmoid_lookup(const float* tab, float g) {
+  const uint32_t bits = __float_as_uint(g) >> 16;  // g is an exact bf16 value
+  uint32_t a = bits & 0x7FFFu;
+  a = min(max(a, (uint32_t)(MOE_SIGMOID_EXP_LO << 7)), (uint32_t)((MOE_SIGMOID_EXP_HI << 7) | 127));
+  const uint32_t idx = a - (MOE_SIGMOID_EXP_LO << 7) +
+                       ((bits >> 15) ? (uint32_t)((MOE_SIGMOID_EXP_HI - MOE_SIGMOID_EXP_LO + 1) * 128) : 0u);
+  return tab[idx];
+}
+
+// largest e with start_e <= r (starts are non-decreasing; an expert sharing
+// its start with a later one is empty)
+__device__ __forceinline__ int expert_of_row(const int* s_start, int E, int r) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_start[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool CLAMP>
+__global__ __launch_bounds__(kActThreads) void act_quant_kernel(
+    const uint16_t* __restrict__ gateup, const int32_t* __restrict__ expert_ends, int E_local,
+    int A, int M_cap, int I, float L, uint8_t* __restrict__ hq, int32_t* __restrict__ hs) {
+  __shared__ float s_tab[MOE_SIGMOID_TABLE_SIZE];
+  __shared__ int s_start[kActMaxE];
+  __shared__ int s_end[kActMaxE];
+  __shared__ uint32_t s_words[kActMaxWordsPerRow * kActUnitRows];
+  __shared__ int s_live[kActUnitRows];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  for (int i = tid; i < MOE_SIGMOID_TABLE_SIZE; i += kActThreads)
+    s_tab[i] = __uint_as_float(g_sigmoid_table[i]);
+  for (int e = tid; e < E_local; e += kActThreads) {
+    int s, en;
+    expert_range(expert_ends, e, A, M_cap, s, en);
+    s_start[e] = s;
+    s_end[e] = en;
+  }
+  __syncthreads();
+  // ends are monotone in a valid layout; the running max keeps the walk
+  // bounded by the farthest end even for inconsistent metadata
+  int last = 0;
+  for (int e = 0; e < E_local; ++e) last = max(last, s_end[e]);
+  const int n_units = (last + kActUnitRows - 1) / kActUnitRows;
+  const int words = I >> 7;
+  const int nchunks = (I + 511) >> 9;
+  const uint16_t* __restrict__ base_g = gateup;
+
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    const int r0 = unit * kActUnitRows;
+    for (int j = 0; j < kActUnitRows / 4; ++j) {
+      const int rl = wid * (kActUnitRows / 4) + j;
+      const int r = r0 + rl;
+      bool live = false;
+      if (r < last) {
+        const int e = expert_of_row(s_start, E_local, r);
+        live = r >= s_start[e] && r < s_end[e];
+      }
+      if (lane == 0) s_live[rl] = live ? 1 : 0;
+      if (!live) continue;  // wave-uniform
+      const uint16_t* grow = base_g + (size_t)r * (2 * I);
+      const uint16_t* urow = grow + I;
+      for (int c = 0; c < nchunks; ++c) {
+        const int col = c * 512 + lane * 8;
+        const bool act = col < I;
+        v4i gv4 = v4i{0, 0, 0, 0}, uv4 = v4i{0, 0, 0, 0};
+        if (act) {
+          // gate/up are read exactly once: stream them past the caches
+          gv4 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(grow + col));
+          uv4 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(urow + col));
+        }
+        const uint4 gr = make_uint4(gv4.x, gv4.y, gv4.z, gv4.w);
+        const uint4 ur = make_uint4(uv4.x, uv4.y, uv4.z, uv4.w);
+        float g[8] = {bf16_lo(gr.x), bf16_hi(gr.x), bf16_lo(gr.y), bf16_hi(gr.y),
+                      bf16_lo(gr.z), bf16_hi(gr.z), bf16_lo(gr.w), bf16_hi(gr.w)};
+        float u[8] = {bf16_lo(ur.x), bf16_hi(ur.x), bf16_lo(ur.y), bf16_hi(ur.y),
+                      bf16_lo(ur.z), bf16_hi(ur.z), bf16_lo(ur.w), bf16_hi(ur.w)};
+        float h[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float gv = g[q], uv = u[q];
+          if (CLAMP) {
+            gv = fminf(gv, L);
+            uv = fminf(fmaxf(uv, -L), L);
+          }
+          const float sig = sigmoid_lookup(s_tab, gv);
+          const float s = gv * sig;
+          h[q] = s * uv;
+          amax = fmaxf(amax, fabsf(h[q]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        const uint32_t b = ue8m0_ceil_byte(amax / 448.0f);
+        const float inv = e8m0_reciprocal(b);
+        uint32_t lo = 0, hi = 0;
+        lo = cvt_e4m3x2<false>(h[0] * inv, h[1] * inv, lo);
+        lo = cvt_e4m3x2<true>(h[2] * inv, h[3] * inv, lo);
+        hi = cvt_e4m3x2<false>(h[4] * inv, h[5] * inv, hi);
+        hi = cvt_e4m3x2<true>(h[6] * inv, h[7] * inv, hi);
+        uint32_t word = b << (8 * ((lane >> 2) & 3));
+        word |= __shfl_xor(word, 4, 64);
+        word |= __shfl_xor(word, 8, 64);
+        if (act) {
+          *reinterpret_cast<uint2*>(hq + (size_t)r * I + col) = make_uint2(lo, hi);
+          if ((lane & 15) == 0) s_words[(col >> 7) * kActUnitRows + rl] = word;
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < words * kActUnitRows; i += kActThreads) {
+      const int c = i / kActUnitRows;
+      const int rl = i % kActUnitRows;
+      if (s_live[rl]) hs[(size_t)c * M_cap + r0 + rl] = (int32_t)s_words[i];
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace moe
+
+extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends,
+                                      int E_local, int A, int M_cap, int I, float clamp_limit,
+                                      uint8_t* hq, int32_t* hs, void* stream) {
+  using namespace moe;
+  if (E_local < 0 || E_local > kActMaxE || A < 1 || M_cap < 0 || I <= 0) return MOE_ERR_SHAPE;
+  if (I % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
+  if (I / 128 > kActMaxWordsPerRow) return MOE_ERR_SHAPE;
+  bool clamp = false;
+  if (clamp_limit > 0.f && clamp_limit < __builtin_inff()) {
+    uint32_t bits;
+    std::memcpy(&bits, &clamp_limit, 4);
+    if (bits & 0xFFFFu) return MOE_ERR_UNSUPPORTED;  // the limit must be an exact bf16 value
+    clamp = true;
+  } else if (!(clamp_limit <= 0.f) && !(clamp_limit == __builtin_inff())) {
+    return MOE_ERR_UNSUPPORTED;  // NaN
+  }
+  if (E_local == 0 || M_cap == 0) return MOE_OK;
+  if (!gateup || !expert_ends || !hq || !hs) return MOE_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  const int max_units = (M_cap + kActUnitRows - 1) / kActUnitRows;
+  const int grid = max_units < 1024 ? max_units : 1024;
+  if (clamp)
+    hipLaunchKernelGGL(act_quant_kernel<true>, dim3(grid), dim3(kActThreads), 0, st, gateup,
+                       expert_ends, E_local, A, M_cap, I, clamp_limit, hq, hs);
+  else
+    hipLaunchKernelGGL(act_quant_kernel<false>, dim3(grid), dim3(kActThreads), 0, st, gateup,
+                       expert_ends, E_local, A, M_cap, I, 0.f, hq, hs);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

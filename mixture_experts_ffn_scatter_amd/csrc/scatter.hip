@@ -1,0 +1,227 @@
+// moe_scatter_endpoints: grouped-layout scatter with int32 expert ends and
+// fused per-32 FP8/UE8M0 quantisation of the routed token rows, on gfx950.
+//
+// The layout is the live-row layout of "Blackwell FP4 MoE: live-row
+// boundary", section 2: start_e = align_up(end_{e-1}, A), end_e = start_e +
+// count_e; the scatter writes the int32 ends itself, with no device-to-host
+// read of the counts. Rows of one expert follow the flattened route order
+// t*k+s, so the permutation is unique.
+//
+// Three launches, none of which depends on a host-visible count:
+//   1. count  - one block per 32-token block: LDS histogram of its local
+//               routes, written to workspace[w][e].
+//   2. scan   - one block: per-expert totals, the aligned exclusive scan
+//               over experts (the endpoint recurrence), expert_ends, and the
+//               per-token-block row offsets (in place over the counts).
+//   3. rows   - one block per token: the rank of each of its routes among
+//               earlier routes of the same expert in its token block, the
+//               route row, and the quantised copy of x[t] into every
+//               destination row (codes coalesced 8 bytes per lane, packed
+//               scales assembled across 16 lanes and stored MN-major).
+#include "common.h"
+
+namespace moe {
+
+constexpr int kTokBlock = 32;      // tokens per histogram block
+constexpr int kScatterMaxE = 1024;
+constexpr int kScatterMaxK = 32;
+
+__global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t* __restrict__ ids, int T,
+                                                            int k, int expert_start, int E_local,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int hist[kScatterMaxE];
+  const int w = blockIdx.x;
+  for (int e = threadIdx.x; e < E_local; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int r0 = w * kTokBlock * k;
+  const int r1 = min(T, (w + 1) * kTokBlock) * k;
+  for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
+    const int e = ids[r] - expert_start;
+    if (e >= 0 && e < E_local) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E_local; e += blockDim.x) counts[(size_t)w * E_local + e] = hist[e];
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads).
+__device__ int block_exclusive_scan_1024(int v, int* wave_tot) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    int x = lane < 16 ? wave_tot[lane] : 0;
+    int ix = x;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int o = __shfl_up(ix, d, 64);
+      if (lane >= d) ix += o;
+    }
+    if (lane < 16) wave_tot[16 + lane] = ix - x;  // exclusive wave offsets
+  }
+  __syncthreads();
+  return wave_tot[16 + wid] + incl - v;
+}
+
+__global__ __launch_bounds__(1024) void scatter_scan_kernel(int W, int E_local, int A,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ expert_ends) {
+  __shared__ int wave_tot[32];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E_local)
+    for (int w = 0; w < W; ++w) total += counts[(size_t)w * E_local + e];
+  const int aligned = e < E_local ? align_up_dev(total, A) : 0;
+  const int start = block_exclusive_scan_1024(aligned, wave_tot);
+  if (e < E_local) {
+    expert_ends[e] = start + total;
+    int run = start;
+    for (int w = 0; w < W; ++w) {
+      int32_t* p = counts + (size_t)w * E_local + e;
+      const int c = *p;
+      *p = run;
+      run += c;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_rows_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int M_cap,
+    const uint16_t* __restrict__ x, int H, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ route_row, uint8_t* __restrict__ xq, int32_t* __restrict__ xs) {
+  __shared__ int s_e[kScatterMaxK];
+  __shared__ int s_cnt[kScatterMaxK];
+  __shared__ int s_row[kScatterMaxK];
+  __shared__ int s_any;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = t / kTokBlock;
+  if (tid < k) {
+    const int e = ids[(size_t)t * k + tid] - expert_start;
+    s_e[tid] = (e >= 0 && e < E_local) ? e : -1;
+    s_cnt[tid] = 0;
+  }
+  if (tid == 0) s_any = 0;
+  __syncthreads();
+  // rank of route (t, s) among earlier routes of the same expert in the
+  // token block: count matches over [block start, t*k + s)
+  const int rb = w * kTokBlock * k;
+  const int rt = t * k;
+  for (int r = rb + tid; r < rt + k; r += blockDim.x) {
+    const int e = ids[r] - expert_start;
+    for (int s = 0; s < k; ++s)
+      if (r < rt + s && e == s_e[s] && e >= 0) atomicAdd(&s_cnt[s], 1);
+  }
+  __syncthreads();
+  if (tid < k) {
+    const int e = s_e[tid];
+    const int row = e >= 0 ? offsets[(size_t)w * E_local + e] + s_cnt[tid] : -1;
+    s_row[tid] = row;
+    route_row[(size_t)t * k + tid] = row;
+    if (row >= 0) atomicOr(&s_any, 1);
+  }
+  __syncthreads();
+  if (!s_any) return;  // block-uniform: no local route for this token
+
+  // quantised copy: each lane owns 8 consecutive columns per 2048-wide chunk;
+  // a 32-column group spans 4 lanes, a packed word (128 columns) 16 lanes
+  const uint16_t* xr = x + (size_t)t * H;
+  const int nchunks = (H + 2047) / 2048;
+  for (int i = 0; i < nchunks; ++i) {
+    const int base = tid * 8 + i * 2048;
+    const bool act = base < H;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (act) raw = *reinterpret_cast<const uint4*>(xr + base);
+    float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                  bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const uint32_t b = ue8m0_ceil_byte(amax / 448.0f);
+    const float inv = e8m0_reciprocal(b);
+    uint32_t lo = 0, hi = 0;
+    lo = cvt_e4m3x2<false>(v[0] * inv, v[1] * inv, lo);
+    lo = cvt_e4m3x2<true>(v[2] * inv, v[3] * inv, lo);
+    hi = cvt_e4m3x2<false>(v[4] * inv, v[5] * inv, hi);
+    hi = cvt_e4m3x2<true>(v[6] * inv, v[7] * inv, hi);
+    uint32_t word = b << (8 * ((tid >> 2) & 3));
+    word |= __shfl_xor(word, 4, 64);
+    word |= __shfl_xor(word, 8, 64);
+    if (act) {
+      const int c = base >> 7;
+      for (int s = 0; s < k; ++s) {
+        const int row = s_row[s];
+        if (row < 0 || row >= M_cap) continue;
+        *reinterpret_cast<uint2*>(xq + (size_t)row * H + base) = make_uint2(lo, hi);
+        if ((tid & 15) == 0) xs[(size_t)c * M_cap + row] = (int32_t)word;
+      }
+    }
+  }
+}
+
+// Plain fill used for the degenerate cases (a kernel, not a memset node, so
+// that graph capture of the call stays safe).
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+static int fill_i32(int32_t* p, int n, int32_t v, hipStream_t st) {
+  if (n <= 0) return MOE_OK;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_scatter_workspace_bytes(int T, int k, int E_local) {
+  (void)k;
+  if (T <= 0 || E_local <= 0) return 0;
+  const size_t W = (size_t)(T + moe::kTokBlock - 1) / moe::kTokBlock;
+  return W * (size_t)E_local * sizeof(int32_t);
+}
+
+extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_start,
+                                     int E_local, int A, int M_cap, const uint16_t* x, int H,
+                                     int32_t* expert_ends, int32_t* route_row, uint8_t* xq,
+                                     int32_t* xs, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  using namespace moe;
+  if (T < 0 || k < 1 || k > kScatterMaxK || E_local < 0 || E_local > kScatterMaxE || A < 1 ||
+      M_cap < 0 || H <= 0)
+    return MOE_ERR_SHAPE;
+  if (H % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
+  if ((long long)M_cap < (long long)T * k + (long long)E_local * A) return MOE_ERR_CAPACITY;
+  if (E_local == 0 && T == 0) return MOE_OK;
+  if (!expert_ends && E_local > 0) return MOE_ERR_NULL;
+  if (T == 0) {
+    // no routes: every expert is empty, ends are all zero
+    return fill_i32(expert_ends, E_local, 0, (hipStream_t)stream);
+  }
+  if (!topk_ids || !x || !route_row || !xq || !xs) return MOE_ERR_NULL;
+  if (E_local == 0) return fill_i32(route_row, T * k, -1, (hipStream_t)stream);
+  const size_t need = moe_scatter_workspace_bytes(T, k, E_local);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int W = (T + kTokBlock - 1) / kTokBlock;
+  int32_t* counts = (int32_t*)workspace;
+  hipLaunchKernelGGL(scatter_count_kernel, dim3(W), dim3(256), 0, st, topk_ids, T, k, expert_start,
+                     E_local, counts);
+  MOE_CHECK_LAUNCH();
+  hipLaunchKernelGGL(scatter_scan_kernel, dim3(1), dim3(1024), 0, st, W, E_local, A, counts,
+                     expert_ends);
+  MOE_CHECK_LAUNCH();
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3(T), dim3(256), 0, st, topk_ids, T, k, expert_start,
+                     E_local, M_cap, x, H, counts, route_row, xq, xs);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

@@ -1,0 +1,51 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest)."""
+import sys
+
+import numpy as np
+import torch
+
+from oracle import formats as F
+
+BF16_SENT = 0x7FC1
+BYTE_SENT = 0xA5
+WORD_SENT = np.uint32(0xA5A5A5A5).view(np.int32)
+
+
+def say(msg: str) -> None:
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def gemm_within_bound(gpu_bits: np.ndarray, exact: np.ndarray, tsum: np.ndarray, K: int):
+    """GPU bf16 result vs the exact sum: one bf16 rounding on the GPU side
+    plus fp32 accumulation over K/128 MFMA steps (with a 4x margin)."""
+    g = F.bf16_to_f32(gpu_bits).astype(np.float64)
+    bound = 2.0 ** -8 * np.abs(exact) + 4.0 * (K / 128 + 1) * 2.0 ** -24 * tsum
+    err = np.abs(g - exact)
+    ok = (err <= bound) | (np.isnan(g) & np.isnan(exact))
+    return ok, err, bound
+
+
+def end_to_end_ok(y_bits: np.ndarray, ref_bits: np.ndarray, max_rel=2e-2, mean_rel=1e-2):
+    """max|d| / max|ref| <= 2e-2 and mean|d| <= 1e-2 * rms(ref)."""
+    y = F.bf16_to_f32(y_bits).astype(np.float64)
+    r = F.bf16_to_f32(ref_bits).astype(np.float64)
+    d = np.abs(y - r)
+    mx = d.max() / max(np.abs(r).max(), 1e-30)
+    mean = d.mean() / max(np.sqrt((r ** 2).mean()), 1e-30)
+    return (mx <= max_rel and mean <= mean_rel), mx, mean

@@ -1,0 +1,116 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function
+declared in include/*.h with the right ABI version, validates arguments on
+the host (these calls return before any GPU work), and the HIP side's
+build-time sigmoid table equals the oracle's correctly rounded sigmoid."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "mixture_experts_ffn_scatter_amd", "libmoe_ffn.so")
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from mixture_experts_ffn_scatter_amd import build
+        build.build(verbose=False)
+    from mixture_experts_ffn_scatter_amd import _lib
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"moe_route", "moe_scatter_endpoints", "moe_grouped_gemm1", "moe_act_quant_liverows",
+            "moe_grouped_gemm2", "moe_combine", "moe_sparse_gemv"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    from mixture_experts_ffn_scatter_amd import _lib
+    assert names == set(_lib.SIGNATURES)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    for s in range(0, -8, -1):
+        assert lib.moe_status_string(s).decode()
+    assert lib.moe_status_string(5).decode() == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.moe_scatter_workspace_bytes(4096, 6, 32) == 128 * 32 * 4
+    assert lib.moe_scatter_workspace_bytes(0, 6, 32) == 0
+
+
+NULL = None
+
+
+def test_host_validation_returns_errors_without_gpu_work(lib):
+    # each call below fails a host-side check before anything is enqueued
+    assert lib.moe_route(NULL, 4, 8, 0, 0, NULL, NULL, NULL, NULL) == -2          # k = 0
+    assert lib.moe_route(NULL, 4, 8, 9, 0, NULL, NULL, NULL, NULL) == -2          # k > E
+    assert lib.moe_route(NULL, 4, 8, 2, 7, NULL, NULL, NULL, NULL) == -5          # bad score fn
+    assert lib.moe_route(NULL, 4, 8, 2, 1, NULL, NULL, NULL, NULL) == -1          # bias missing
+    assert lib.moe_route(NULL, 0, 8, 2, 0, NULL, NULL, NULL, NULL) == 0           # T = 0: no-op
+    # scatter: H not a multiple of 128, capacity too small, workspace too small
+    args = [NULL, 64, 2, 0, 8, 128, 1152, NULL, 200, NULL, NULL, NULL, NULL, NULL, 0, NULL]
+    assert lib.moe_scatter_endpoints(*args) == -3
+    args[8] = 256
+    args[6] = 1024
+    assert lib.moe_scatter_endpoints(*args) == -4
+    args[6] = 1152
+    assert lib.moe_scatter_endpoints(*args) == -1                                 # NULL pointers
+    # act-quant: clamp limit that is not a bf16 value
+    assert lib.moe_act_quant_liverows(NULL, NULL, 8, 128, 1152, 128, ctypes.c_float(7.3),
+                                      NULL, NULL, NULL) == -5
+    assert lib.moe_act_quant_liverows(NULL, NULL, 8, 128, 1152, 100, ctypes.c_float(0.0),
+                                      NULL, NULL, NULL) == -3
+    # GEMMs: K not a multiple of 128
+    assert lib.moe_grouped_gemm1(NULL, NULL, NULL, 8, 128, 1152, 192, 128, NULL, NULL, NULL,
+                                 NULL) == -3
+    assert lib.moe_grouped_gemm2(NULL, NULL, NULL, 8, 128, 1152, 100, 256, NULL, NULL, NULL,
+                                 NULL) == -3
+    # combine: H not a multiple of 8
+    assert lib.moe_combine(NULL, 0, NULL, NULL, 4, 2, 12, ctypes.c_float(1.0), NULL, NULL) == -3
+    # sparse GEMV: too many slots, unsupported format
+    assert lib.moe_sparse_gemv(NULL, 0, NULL, 17, 4, 0, 32, 5760, 2880, 0, NULL, NULL, NULL, 1,
+                               ctypes.c_float(1.702), ctypes.c_float(1.0), ctypes.c_float(7.0),
+                               NULL, NULL, NULL) == -2
+    assert lib.moe_sparse_gemv(NULL, 0, NULL, 1, 4, 0, 32, 5760, 2880, 3, NULL, NULL, NULL, 1,
+                               ctypes.c_float(1.702), ctypes.c_float(1.0), ctypes.c_float(7.0),
+                               NULL, NULL, NULL) == -5
+
+
+def test_hip_side_sigmoid_table_equals_oracle(tmp_path):
+    """The HIP build's sigmoid table (own generator, long-double arithmetic)
+    against the oracle's correctly rounded sigmoid, for every bf16 input."""
+    from oracle import formats as F
+    exe = tmp_path / "gen"
+    src = os.path.join(ROOT, "mixture_experts_ffn_scatter_amd", "csrc", "gen_sigmoid_table.cpp")
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-ffp-contract=off", src, "-o", str(exe)])
+    txt = subprocess.check_output([str(exe)], text=True)
+    lo = int(re.search(r"MOE_SIGMOID_EXP_LO (\d+)", txt).group(1))
+    hi = int(re.search(r"MOE_SIGMOID_EXP_HI (\d+)", txt).group(1))
+    tab = np.array([int(v, 16) for v in re.findall(r"0x([0-9a-f]{8})u", txt)], np.uint32)
+    rows = hi - lo + 1
+    assert tab.size == 2 * rows * 128
+    b = np.arange(65536, dtype=np.uint32)
+    ex = (b >> 7) & 0xFF
+    finite = ex != 0xFF
+    b, ex = b[finite], ex[finite]
+    idx = (b >> 15) * rows * 128 + (np.clip(ex, lo, hi) - lo) * 128 + (b & 0x7F)
+    want = F.sigmoid_f32(F.bf16_to_f32(b.astype(np.uint16))).view(np.uint32)
+    assert np.array_equal(tab[idx], want)

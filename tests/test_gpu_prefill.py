@@ -1,0 +1,315 @@
+"""GPU parity of the prefill path (route, scatter, GEMM1, act-quant, GEMM2,
+combine) against the CPU oracle, through the C ABI.
+
+Each stage is fed the GPU's own input to that stage (which earlier tests
+pin bit-exactly), so integer and byte outputs must match the oracle bit for
+bit and float GEMM outputs must sit within the accumulation bound. Padding
+of every grouped buffer is seeded with sentinels that must survive."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as F
+from oracle import moe as M
+from tests.gpu_helpers import (BF16_SENT, BYTE_SENT, WORD_SENT, dev, dev_bf16, end_to_end_ok,
+                               gemm_within_bound, host, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import mixture_experts_ffn_scatter_amd as pkg
+    pkg.lib()
+    return pkg.ops
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("case", ["tiny", "prefill-own", "prefill-group", "decode", "large"])
+def test_route_ids_bitexact(ops, case):
+    say(f"route {case}")
+    bias = None
+    if case == "tiny":
+        c = W.tiny(); logits, k = c.logits, c.k
+    elif case == "prefill-own":
+        c = W.prefill(with_weights=False); logits, k = c.logits[:512], c.k
+    elif case == "prefill-group":
+        c = W.prefill(with_weights=False); logits, k = c.logits, c.k
+    elif case == "decode":
+        c = W.decode(T=8, H=64, experts=1); logits, k = c.logits, c.k
+    else:
+        c = W.large(with_weights=False); logits, k, bias = c.logits, c.k, c.bias
+    if bias is None:
+        ids_o, w_o = M.route_softmax(logits, k)
+        ids, w = ops.moe_route(dev(logits), k, "softmax")
+    else:
+        ids_o, w_o = M.route_sigmoid_bias(logits, bias, k)
+        ids, w = ops.moe_route(dev(logits), k, "sigmoid_bias", dev(bias))
+    ids, w = host(ids), host(w)
+    assert np.array_equal(ids, ids_o)
+    assert np.allclose(w, w_o, rtol=4 * 2.0 ** -23, atol=0)
+
+
+# ------------------------------------------------------------------ scatter
+
+def _run_scatter(ops, ids, x_bits, expert_start, E_local, A, M_cap):
+    T, k = ids.shape
+    H = x_bits.shape[1]
+    ends = torch.full((E_local,), -7, dtype=torch.int32, device="cuda")
+    rr = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    xq = torch.full((M_cap, H), BYTE_SENT, dtype=torch.uint8, device="cuda")
+    xs = torch.full((H // 128, M_cap), int(WORD_SENT), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(ops.moe_scatter_workspace_bytes(T, k, E_local), 1), dtype=torch.uint8,
+                     device="cuda")
+    ops.moe_scatter_endpoints(dev(ids.astype(np.int32)), expert_start, E_local, A,
+                              dev_bf16(x_bits), ends, rr, xq, xs, ws)
+    return host(ends), host(rr), host(xq), host(xs)
+
+
+def _check_scatter(ids, x_bits, expert_start, E_local, A, M_cap, got):
+    ends, rr, xq, xs = got
+    sc = M.scatter_routes(ids, expert_start, E_local, A)
+    assert np.array_equal(ends, sc.end.astype(np.int32))
+    assert np.array_equal(rr, sc.route_row)
+    k = ids.shape[1]
+    rows = sc.route_row[sc.local_routes]
+    q, b = M.quant_rows(x_bits[sc.local_routes // k])
+    assert np.array_equal(xq[rows], q)
+    words = F.pack_ue8m0_words(b) if b.size else np.zeros((0, x_bits.shape[1] // 128), np.int32)
+    assert np.array_equal(xs[:, rows].T, words)
+    live = M.live_row_mask(sc.start, sc.end, M_cap)
+    assert np.all(xq[~live] == BYTE_SENT)
+    assert np.all(xs[:, ~live] == WORD_SENT)
+
+
+def test_scatter_tiny(ops):
+    say("scatter tiny")
+    c = W.tiny()
+    ids, _ = M.route_softmax(c.logits, c.k)
+    got = _run_scatter(ops, ids, c.x, 0, c.E, c.A, c.M_cap)
+    _check_scatter(ids, c.x, 0, c.E, c.A, c.M_cap, got)
+
+
+def test_scatter_window_negative_ids_small_alignment(ops):
+    say("scatter window/-1/A=16")
+    c = W.tiny(seed=77, T=40)
+    ids, _ = M.route_softmax(c.logits, c.k)
+    ids = ids.copy()
+    ids[3, 1] = -1
+    ids[7, 0] = -1
+    M_cap = W.capacity(40, 2, 4, 16)
+    got = _run_scatter(ops, ids, c.x, 2, 4, 16, M_cap)
+    _check_scatter(ids, c.x, 2, 4, 16, M_cap, got)
+
+
+def test_scatter_all_nonlocal_and_duplicate_ids(ops):
+    say("scatter all-nonlocal / duplicates")
+    c = W.tiny(seed=5, T=20)
+    ids = np.full((20, 2), 50, np.int32)
+    M_cap = W.capacity(20, 2, 8, 128)
+    got = _run_scatter(ops, ids, c.x, 0, 8, 128, M_cap)
+    _check_scatter(ids, c.x, 0, 8, 128, M_cap, got)
+    ids = np.stack([np.arange(20) % 3, np.arange(20) % 3], axis=1).astype(np.int32)  # both slots equal
+    got = _run_scatter(ops, ids, c.x, 0, 8, 128, M_cap)
+    _check_scatter(ids, c.x, 0, 8, 128, M_cap, got)
+
+
+def test_scatter_fp8_rounding_edges(ops):
+    """Inputs built so that v / 2^(b-127) lands on E4M3 midpoints, on codes,
+    in the subnormal range and on zeros, to pin the hardware conversion."""
+    say("scatter fp8 rounding edges")
+    rng = np.random.default_rng(21)
+    T, H = 48, 512
+    pos = F.E4M3_VALUES[:127]
+    mids = (pos[:-1] + pos[1:]) / 2
+    x = np.empty((T, H), np.float64)
+    for t in range(T):
+        for g in range(H // 32):
+            j = int(rng.integers(-30, 20))
+            sf = 2.0 ** j
+            vals = rng.choice(np.concatenate([mids, pos, mids[:16] * 1.0078125]), 32)
+            vals *= rng.choice([-1.0, 1.0], 32)
+            vals[int(rng.integers(0, 32))] = 448.0 * rng.choice([-1, 1])
+            if g % 5 == 0:
+                vals[:] = 0.0
+            x[t, g * 32:(g + 1) * 32] = vals * sf
+    xb = F.round_to_bf16(x)
+    ids = np.stack([np.arange(T) % 4, 4 + np.arange(T) % 3], axis=1).astype(np.int32)
+    M_cap = W.capacity(T, 2, 8, 128)
+    got = _run_scatter(ops, ids, xb, 0, 8, 128, M_cap)
+    _check_scatter(ids, xb, 0, 8, 128, M_cap, got)
+
+
+def test_scatter_prefill_group_full_size(ops):
+    say("scatter prefill EP group 4096x6 -> 32 local experts")
+    c = W.prefill(with_weights=False)
+    ids, _ = M.route_softmax(c.logits, c.k)
+    got = _run_scatter(ops, ids, c.x, 0, c.E_local, c.A, c.M_cap)
+    _check_scatter(ids, c.x, 0, c.E_local, c.A, c.M_cap, got)
+
+
+# ---------------------------------------------------------------- act-quant
+
+def _run_act(ops, case, clamp=0.0):
+    start, end = M.endpoints(case.counts, case.A)
+    hq = torch.full((case.M_cap, case.I), BYTE_SENT, dtype=torch.uint8, device="cuda")
+    hs = torch.full((case.I // 128, case.M_cap), int(WORD_SENT), dtype=torch.int32, device="cuda")
+    ops.moe_act_quant_liverows(dev_bf16(case.gateup), dev(end.astype(np.int32)), case.A, clamp,
+                               hq, hs)
+    return start, end, host(hq), host(hs)
+
+
+def _check_act(case, start, end, hq, hs, rows, clamp=0.0):
+    q, b = M.act_quant_rows(case.gateup[rows], case.I, clamp)
+    assert np.array_equal(hq[rows], q), "FP8 codes differ"
+    assert np.array_equal(hs[:, rows].T, F.pack_ue8m0_words(b)), "packed scales differ"
+    live = M.live_row_mask(start, end, case.M_cap)
+    assert np.all(hq[~live] == BYTE_SENT)
+    assert np.all(hs[:, ~live] == WORD_SENT)
+
+
+def test_act_quant_liverows_3072_of_28672(ops):
+    say("act-quant 3072 live of 28672")
+    case = W.actquant()
+    start, end, hq, hs = _run_act(ops, case)
+    live = np.flatnonzero(M.live_row_mask(start, end, case.M_cap))
+    assert live.size == 3072
+    _check_act(case, start, end, hq, hs, live)
+
+
+def test_act_quant_full_buffer_sampled(ops):
+    say("act-quant full buffer 28672 rows")
+    case = W.actquant(full=True)
+    start, end, hq, hs = _run_act(ops, case)
+    rows = np.sort(np.random.default_rng(3).choice(case.M_cap, 1024, replace=False))
+    _check_act(case, start, end, hq, hs, rows)
+
+
+def test_act_quant_clamp_small_I_odd_alignment(ops):
+    say("act-quant clamp 25, I=384, A=8")
+    rng = np.random.default_rng(9)
+    counts = np.array([5, 0, 17, 1, 0, 9], np.int64)
+    case = W.actquant(counts=counts, E_local=6, I=384, A=8, M_cap=64)
+    # scale live rows so that the clamp engages on both sides
+    live = M.live_row_mask(*M.endpoints(counts, 8), 64)
+    g = F.bf16_to_f32(case.gateup).astype(np.float64) * 30.0
+    g[~live] = np.nan
+    case.gateup = F.round_to_bf16(g)
+    start, end, hq, hs = _run_act(ops, case, clamp=25.0)
+    _check_act(case, start, end, hq, hs, np.flatnonzero(live), clamp=25.0)
+
+
+def test_act_quant_empty_and_all_empty(ops):
+    say("act-quant all-empty")
+    case = W.actquant(counts=np.zeros(4, np.int64), E_local=4, I=256, A=128, M_cap=512)
+    start, end, hq, hs = _run_act(ops, case)
+    assert np.all(hq == BYTE_SENT) and np.all(hs == WORD_SENT)
+
+
+# -------------------------------------------------------------------- GEMMs
+
+def _tiny_state(ops, c, clamp=0.0):
+    ids, wts = M.route_softmax(c.logits, c.k)
+    buf = ops.alloc_grouped(c.T, c.k, c.E, c.M_cap, c.H, c.I, fill=True)
+    w = c.weights
+    dw = dict(w13=dev(w.w13), s13=dev(w.s13), w2=dev(w.w2), s2=dev(w.s2))
+    ops.moe_scatter_endpoints(dev(ids), 0, c.E, c.A, dev_bf16(c.x), buf.expert_ends, buf.route_row,
+                              buf.xq, buf.xs, buf.workspace)
+    return ids, wts, buf, dw
+
+
+def _expert_rows(ends, A):
+    prev = 0
+    out = []
+    for e in ends:
+        s = ((prev + A - 1) // A) * A
+        out.append(np.arange(s, e))
+        prev = e
+    return out
+
+
+def test_gemm1_gemm2_combine_tiny_stagewise(ops):
+    c = W.tiny()
+    ids, wts, buf, dw = _tiny_state(ops, c)
+    say("gemm1 tiny")
+    ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, dw["w13"], dw["s13"], buf.gateup)
+    ends = host(buf.expert_ends)
+    xq, xs, gu = host(buf.xq), host(buf.xs), host(buf.gateup)
+    live = np.zeros(c.M_cap, bool)
+    for e, rows in enumerate(_expert_rows(ends, c.A)):
+        if rows.size == 0:
+            continue
+        live[rows] = True
+        ab = F.unpack_ue8m0_words(xs[:, rows].T)
+        _, exact, tsum = M.mx_gemm(xq[rows], ab, c.weights.w13[e], c.weights.s13[e])
+        ok, err, bound = gemm_within_bound(gu[rows], exact, tsum, c.H)
+        assert ok.all(), f"expert {e}: {np.count_nonzero(~ok)} of {ok.size} outside bound"
+    assert np.all(gu[~live] == BF16_SENT)
+
+    say("act-quant on GPU gateup")
+    ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, 0.0, buf.hq, buf.hs)
+    hq, hs = host(buf.hq), host(buf.hs)
+    rows = np.flatnonzero(live)
+    q, b = M.act_quant_rows(gu[rows], c.I)
+    assert np.array_equal(hq[rows], q) and np.array_equal(hs[:, rows].T, F.pack_ue8m0_words(b))
+
+    say("gemm2 tiny")
+    ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, dw["w2"], dw["s2"], buf.down)
+    dn = host(buf.down)
+    for e, rows_e in enumerate(_expert_rows(ends, c.A)):
+        if rows_e.size == 0:
+            continue
+        _, exact, tsum = M.mx_gemm(hq[rows_e], F.unpack_ue8m0_words(hs[:, rows_e].T),
+                                   c.weights.w2[e], c.weights.s2[e])
+        ok, _, _ = gemm_within_bound(dn[rows_e], exact, tsum, c.I)
+        assert ok.all(), f"expert {e}: {np.count_nonzero(~ok)} outside bound"
+    assert np.all(dn[~live] == BF16_SENT)
+
+    say("combine tiny")
+    ops.moe_combine(buf.down, buf.route_row, dev(wts), 1.0, buf.out)
+    out = host(buf.out)
+    rows_f32 = F.bf16_to_f32(dn)
+    ref = M.combine(rows_f32, host(buf.route_row), wts, 1.0)
+    assert np.array_equal(out, ref)
+
+
+def test_prefill_chain_tiny_end_to_end_and_deterministic(ops):
+    c = W.tiny()
+    ids, wts = M.route_softmax(c.logits, c.k)
+    w = c.weights
+    say("prefill chain tiny")
+    ref = M.prefill_expert_major(c.x, ids, wts, 0, c.E, c.A, c.I, w.w13, w.s13, w.w2, w.s2)
+    outs = []
+    for _ in range(2):
+        buf = ops.alloc_grouped(c.T, c.k, c.E, c.M_cap, c.H, c.I, fill=True)
+        y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A, dev(w.w13), dev(w.s13),
+                                dev(w.w2), dev(w.s2), buf)
+        outs.append(host(y))
+    assert np.array_equal(outs[0], outs[1])
+    ok, mx, mean = end_to_end_ok(outs[0], ref.out)
+    assert ok, (mx, mean)
+
+
+def test_prefill_chain_window_clamp_scale(ops):
+    """Local window of 4 of 8 experts, -1 slots, A=16, clamp 6, routed scale 0.5."""
+    c = W.tiny(seed=77, T=40)
+    ids, wts = M.route_softmax(c.logits, c.k)
+    ids = ids.copy()
+    ids[3, 1] = -1
+    w = c.weights
+    E_local, es, A = 4, 2, 16
+    M_cap = W.capacity(c.T, c.k, E_local, A)
+    sl = slice(es, es + E_local)
+    say("prefill chain window/clamp")
+    ref = M.prefill_expert_major(c.x, ids, wts, es, E_local, A, c.I, w.w13[sl], w.s13[sl],
+                                 w.w2[sl], w.s2[sl], clamp=6.0, routed_scale=0.5)
+    buf = ops.alloc_grouped(c.T, c.k, E_local, M_cap, c.H, c.I, fill=True)
+    y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), es, A, dev(w.w13[sl]),
+                            dev(w.s13[sl]), dev(w.w2[sl]), dev(w.s2[sl]), buf, clamp_limit=6.0,
+                            routed_scale=0.5)
+    ok, mx, mean = end_to_end_ok(host(y), ref.out)
+    assert ok, (mx, mean)
+    no_local = ~np.any((ids >= es) & (ids < es + E_local), axis=1)
+    assert np.all(host(y)[no_local] == 0)
