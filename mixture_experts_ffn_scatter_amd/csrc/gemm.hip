@@ -12,13 +12,16 @@
 // int32 expert ends; rows outside [start_e, end_e) are neither read nor
 // written.
 //
-// Mapping onto V_MFMA_SCALE_F32_16X16X128_F8F6F4: the weight tile is the A
-// operand (16 output columns x 128 k, E2M1, 16 bytes per lane) and the
-// activation tile the B operand (128 k x 16 rows, E4M3, 32 bytes per lane);
-// lane l holds k-slice [32*(l/16), +32) of row/column l%16 plus that slice's
-// E8M0 scale, so per-32 block scaling is exactly the MX definition. The
-// 16x16 fp32 result gives lane l four consecutive output columns of one row,
-// stored as one 8-byte bf16 write.
+// Mapping onto V_MFMA_SCALE_F32_16X16X128_F8F6F4 (lane layout measured on
+// gfx950 with a one-instruction probe): the weight tile is the A operand
+// (16 output columns x 128 k, E2M1, 16 bytes per lane) and the activation
+// tile the B operand (128 k x 16 rows, E4M3, 32 bytes per lane). With
+// g = lane/16, an E2M1 operand holds k-slice [32g, 32g+32) of row lane%16 in
+// order (low nibble first), while an E4M3 operand holds k [16g, 16g+16) in
+// its first four dwords and k [64+16g, 64+16g+16) in the last four. The
+// E8M0 scale of row r and 32-wide k-block b is read from lane r + 16b. The
+// 16x16 fp32 result gives lane l four consecutive output columns of row
+// l%16, stored as one 8-byte bf16 write.
 //
 // Scheduling: the tile list (expert, n-tile, m-tile) is rebuilt inside every
 // block from expert_ends (a block-wide scan of ceil(count_e/128) * N/128),
@@ -147,8 +150,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_mx_gemm_kernel(
           const int m = row0 + mb * 16 + l16;
           const bool ok = (mb < nblk) && (m < end);
           if (ok) {
-            const v4i* p = reinterpret_cast<const v4i*>(X + (size_t)m * K + k0 + kq * 32);
-            const v4i lo4 = p[0], hi4 = p[1];
+            const uint8_t* px = X + (size_t)m * K + k0 + kq * 16;
+            const v4i lo4 = *reinterpret_cast<const v4i*>(px);
+            const v4i hi4 = *reinterpret_cast<const v4i*>(px + 64);
             b[mb] = v8i{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
             const uint32_t xw = (uint32_t)Xs[(size_t)(k0 >> 7) * M_cap + m];
             sb[mb] = (int)(xw >> (8 * kq));

@@ -225,6 +225,19 @@ def _lsb_exponent_min(v: np.ndarray) -> np.ndarray:
     return lsb.min(axis=-1)
 
 
+def block_max_bound(aq, ab, wq_packed, wb, block: int = 128):
+    """sum over 128-wide k blocks of max|a| * max|w| in the block, per output:
+    an upper bound on the sum over blocks of the largest single product,
+    used to bound hardware dot products that align each block's products to
+    its largest one."""
+    A = np.abs(dequant_e4m3_rows(aq, ab))
+    W = np.abs(dequant_mxfp4_rows(wq_packed, wb))
+    K = A.shape[1]
+    am = A.reshape(A.shape[0], K // block, block).max(-1)
+    wm = W.reshape(W.shape[0], K // block, block).max(-1)
+    return am @ wm.T
+
+
 def mx_gemm(aq, ab, wq_packed, wb, check_exact: bool = True):
     """One expert's MX GEMM: out[r, n] = bf16_rne( sum_k a[r,k] * w[n,k] ) with
     a = e4m3(aq) * 2^(ab-127) per 32 columns and w = e2m1(wq) * 2^(wb-127)
@@ -433,9 +446,10 @@ def decode_chain(case, expert_start: int = 0, E_local: int = None, ids=None, wei
     rows = np.zeros((T * k, H), np.float32)
     for t in range(T):
         for s in range(k):
-            e = int(ids[t, s]) - expert_start
-            if not (0 <= e < E_local):
+            g = int(ids[t, s])                    # global expert id; the case holds all experts
+            if not (0 <= g - expert_start < E_local):
                 continue
+            e = g
             slot_row[t * k + s] = t * k + s
             if case.wfmt == "fp8":
                 g, _ = gemv_fp8(case.x[t:t + 1], case.w_gu[e], case.s_gu[e], case.b_gu[e])

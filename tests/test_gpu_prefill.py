@@ -244,7 +244,8 @@ def test_gemm1_gemm2_combine_tiny_stagewise(ops):
         live[rows] = True
         ab = F.unpack_ue8m0_words(xs[:, rows].T)
         _, exact, tsum = M.mx_gemm(xq[rows], ab, c.weights.w13[e], c.weights.s13[e])
-        ok, err, bound = gemm_within_bound(gu[rows], exact, tsum, c.H)
+        bm = M.block_max_bound(xq[rows], ab, c.weights.w13[e], c.weights.s13[e])
+        ok, err, bound = gemm_within_bound(gu[rows], exact, tsum, c.H, bm)
         assert ok.all(), f"expert {e}: {np.count_nonzero(~ok)} of {ok.size} outside bound"
     assert np.all(gu[~live] == BF16_SENT)
 
@@ -261,9 +262,10 @@ def test_gemm1_gemm2_combine_tiny_stagewise(ops):
     for e, rows_e in enumerate(_expert_rows(ends, c.A)):
         if rows_e.size == 0:
             continue
-        _, exact, tsum = M.mx_gemm(hq[rows_e], F.unpack_ue8m0_words(hs[:, rows_e].T),
-                                   c.weights.w2[e], c.weights.s2[e])
-        ok, _, _ = gemm_within_bound(dn[rows_e], exact, tsum, c.I)
+        hb_e = F.unpack_ue8m0_words(hs[:, rows_e].T)
+        _, exact, tsum = M.mx_gemm(hq[rows_e], hb_e, c.weights.w2[e], c.weights.s2[e])
+        bm = M.block_max_bound(hq[rows_e], hb_e, c.weights.w2[e], c.weights.s2[e])
+        ok, _, _ = gemm_within_bound(dn[rows_e], exact, tsum, c.I, bm)
         assert ok.all(), f"expert {e}: {np.count_nonzero(~ok)} outside bound"
     assert np.all(dn[~live] == BF16_SENT)
 

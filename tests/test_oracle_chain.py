@@ -67,9 +67,14 @@ def test_decode_sparse_equals_dense_small():
         dense[e] = d
     for (t, s), d in sp.down.items():
         assert np.array_equal(d, dense[int(ids[t, s])][t])
-    # a window that holds only half the experts skips the other slots
-    half = M.decode_chain(c, 0, 4, ids=ids, weights=wts)
-    assert np.all((half.slot_row >= 0) == (ids.reshape(-1) < 4))
+    # a window that holds only half the experts skips the other slots, and
+    # its per-slot results are the full chain's results for those slots
+    for es in (0, 4):
+        half = M.decode_chain(c, es, 4, ids=ids, weights=wts)
+        flat = ids.reshape(-1)
+        assert np.all((half.slot_row >= 0) == ((flat >= es) & (flat < es + 4)))
+        for key, d in half.down.items():
+            assert np.array_equal(d, sp.down[key])
 
 
 def test_glu_special_cases():

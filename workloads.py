@@ -257,7 +257,8 @@ def _e4m3_normal_table() -> np.ndarray:
     normal shape. Built with torch's e4m3 cast."""
     from scipy.special import ndtri
     u = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
-    z = (ndtri(u) * 112.0).astype(np.float32)
+    # the two extreme tails (|z| > 448) saturate to +-448, the largest finite code
+    z = np.clip(ndtri(u) * 112.0, -448.0, 448.0).astype(np.float32)
     return torch.from_numpy(z).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
