@@ -1,0 +1,316 @@
+"""Benchmark of the MI355X MoE expert FFN hot path.
+
+Headline (one JSON line on stdout): microseconds per MoE FFN layer at 512
+tokens per GPU -- one GPU's share of an EP8 DeepSeek-V4-style layer
+(route 512 own tokens; scatter, GEMM1, live-row act-quant, GEMM2 and
+combine for the 8x512-token group's routes to this GPU's 32 experts).
+Inputs are seeded synthetic data already resident in HBM when the timed
+region starts. A step is one pass of route -> scatter -> GEMM1 -> act-quant
+-> GEMM2 -> combine.
+
+The same line carries:
+  roofline      the dominant kernel (GEMM1) against HBM peak, with its
+                duration measured by HIP events around it in the timed loop
+  kernels       per-kernel durations, algorithmic bytes / FLOP, GB/s, TFLOP/s
+  actquant      the standalone live-row act-quant benchmark (3,072 live of
+                28,672 rows, width 2,048) and its full-buffer control, cold
+  decode        the sparse decode path at 1 and 8 tokens (FP8 and MXFP4)
+  cpu_baseline  the CPU oracle timed on the host on the same layer
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 / MXFP8 matrix peak
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix peak
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is "
+              "built for one GPU's expert share; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_ffn_scatter_amd as pkg
+    import workloads as W
+
+    ops = pkg.ops
+    pkg.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def up_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
+
+    # ------------------------------------------------------------ workload
+    log("generating the prefill EP-share workload")
+    c = W.prefill()
+    w = c.weights
+    x = up_bf16(c.x)
+    logits_group = up(c.logits)
+    logits_own = up(c.logits[: c.own_tokens])
+    w13, s13, w2, s2 = up(w.w13), up(w.s13), up(w.w2), up(w.s2)
+    # the group's routes (every rank routes its own 512 tokens; the 4096
+    # tokens' ids are what this GPU receives)
+    ids, wts = ops.moe_route(logits_group, c.k, "softmax")
+    own_ids = torch.empty((c.own_tokens, c.k), dtype=torch.int32, device=dev)
+    own_w = torch.empty((c.own_tokens, c.k), dtype=torch.float32, device=dev)
+    buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ops.moe_route(logits_own, c.k, "softmax", None, own_ids, own_w)
+        mark(1)
+        ops.moe_scatter_endpoints(ids, 0, c.E_local, c.A, x, buf.expert_ends, buf.route_row,
+                                  buf.xq, buf.xs, buf.workspace)
+        mark(2)
+        ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13, buf.gateup)
+        mark(3)
+        ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, 0.0, buf.hq, buf.hs)
+        mark(4)
+        ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, w2, s2, buf.down)
+        mark(5)
+        ops.moe_combine(buf.down, buf.route_row, wts, c.routed_scale, buf.out)
+        mark(6)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    names = ["route", "scatter", "gemm1", "act_quant", "gemm2", "combine"]
+    dur_us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in
+                                range(args.steps)])) * 1e3 for j, n in enumerate(names)}
+    log(f"ms/step {ms_per_step:.4f}", {k: round(v, 2) for k, v in dur_us.items()})
+
+    # algorithmic work per launch, from the routed counts of this input
+    ends = buf.expert_ends.cpu().numpy().astype(np.int64)
+    starts = np.concatenate([[0], ((ends[:-1] + c.A - 1) // c.A) * c.A])
+    counts = ends - starts
+    R = int(counts.sum())
+    E_ne = int(np.count_nonzero(counts))
+    H, I, T, k, E = c.H, c.I, c.T, c.k, c.E
+    ids_h = ids.cpu().numpy()
+    U_tok = int(np.count_nonzero(np.any((ids_h >= 0) & (ids_h < c.E_local), axis=1)))
+    bytes_ = {
+        "route": c.own_tokens * E * 4 + c.own_tokens * k * 8,
+        "scatter": U_tok * H * 2 + R * (H + H // 32) + T * k * 8 + 4 * c.E_local,
+        "gemm1": E_ne * (2 * I * H // 2 + 2 * I * H // 32) + R * (H + H // 32) + R * 2 * I * 2,
+        "act_quant": R * (2 * I * 2 + I + I // 32) + 4 * c.E_local,
+        "gemm2": E_ne * (H * I // 2 + H * I // 32) + R * (I + I // 32) + R * H * 2,
+        "combine": R * H * 2 + T * k * 8 + T * H * 2,
+    }
+    flops = {"gemm1": 2.0 * R * 2 * I * H, "gemm2": 2.0 * R * H * I}
+    kernels = {}
+    for n in names:
+        t = dur_us[n] * 1e-6
+        kernels[n] = {"us": round(dur_us[n], 3), "alg_bytes": int(bytes_[n]),
+                      "GBps": round(bytes_[n] / t / 1e9, 1),
+                      "hbm_frac": round(bytes_[n] / t / 1e9 / HBM_PEAK_GBS, 4)}
+        if n in flops:
+            tf = flops[n] / t / 1e12
+            kernels[n].update({"flop": flops[n], "TFLOPs": round(tf, 1),
+                               "mfma_frac_fp8_peak": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
+                               "mfma_frac_fp4_peak": round(tf / FP4_MFMA_PEAK_TFLOPS, 4)})
+    dom = "gemm1"
+    ach = bytes_[dom] / (dur_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "grouped_mx_gemm_kernel (moe_grouped_gemm1)",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "alg_bytes_per_launch": int(bytes_[dom]), "avg_launch_us": round(dur_us[dom], 3)}
+
+    result = {
+        "metric": "MoE FFN us/layer @512 tok; live-row act-quant GB/s; % of HBM/MFMA roofline",
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us/layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 x mxfp4 (fp32 accum), bf16 io",
+        "data": "synthetic",
+        "config": {"workload": "prefill EP share: 512 tok/GPU x EP8 = 4096-token group, top-6 of "
+                               "256 experts, 32 local experts, H=4096, I=2048, A=128, MXFP4 "
+                               "weights, FP8 e4m3 + UE8M0 group-32 activations",
+                   "live_rows": R, "nonempty_experts": E_ne, "M_cap": c.M_cap},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    del buf
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        result["actquant"] = bench_actquant(ops, torch, up, up_bf16, log)
+        result["decode"] = bench_decode(ops, torch, up, up_bf16, log)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(c, log)
+    print(json.dumps(result), flush=True)
+
+
+def _flush_caches(torch, scratch):
+    scratch.zero_()  # 512 MB write evicts the L2s and the 256 MB Infinity Cache
+
+
+def bench_actquant(ops, torch, up, up_bf16, log, iters=20):
+    import workloads as W
+    out = {}
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for full in (False, True):
+        case = W.actquant(full=full)
+        ends_h = np.zeros(case.E_local, np.int64)
+        pos = 0
+        for e, cnt in enumerate(case.counts):
+            pos = ((pos + case.A - 1) // case.A) * case.A + int(cnt)
+            ends_h[e] = pos
+        gate = up_bf16(case.gateup)
+        ends = up(ends_h.astype(np.int32))
+        hq = torch.empty((case.M_cap, case.I), dtype=torch.uint8, device="cuda")
+        hs = torch.empty((case.I // 128, case.M_cap), dtype=torch.int32, device="cuda")
+        R = int(case.counts.sum())
+        B = R * (2 * case.I * 2 + case.I + case.I // 32) + 4 * case.E_local
+        for _ in range(3):
+            ops.moe_act_quant_liverows(gate, ends, case.A, 0.0, hq, hs)
+        cold, warm = [], []
+        for i in range(iters):
+            _flush_caches(torch, scratch)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ops.moe_act_quant_liverows(gate, ends, case.A, 0.0, hq, hs)
+            e1.record()
+            e2 = torch.cuda.Event(enable_timing=True)
+            ops.moe_act_quant_liverows(gate, ends, case.A, 0.0, hq, hs)
+            e2.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1) * 1e3)
+            warm.append(e1.elapsed_time(e2) * 1e3)
+        t = float(np.median(cold))
+        key = "full_28672_rows" if full else "live_3072_of_28672"
+        out[key] = {"us_cold_median": round(t, 3), "us_warm_median": round(float(np.median(warm)), 3),
+                    "alg_bytes": int(B), "GBps_cold": round(B / (t * 1e-6) / 1e9, 1),
+                    "hbm_frac_cold": round(B / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "live_rows": R}
+        log("actquant", key, out[key])
+        del gate, hq, hs
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode(ops, torch, up, up_bf16, log, iters=20):
+    import workloads as W
+    out = {}
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for wfmt in ("fp8", "mxfp4"):
+        base = None
+        for T in (1, 8):
+            cse = W.decode(T=T, wfmt=wfmt) if base is None else None
+            if base is None:
+                base = cse
+                dw = [up(cse.w_gu), up(cse.s_gu), up_bf16(cse.b_gu), up(cse.w_d), up(cse.s_d),
+                      up_bf16(cse.b_d)]
+            # activations and routing for this T (weights shared across T)
+            rng = np.random.default_rng(4000 + T)
+            x = up_bf16(W.to_bf16_bits(rng.standard_normal((T, base.H), dtype=np.float32)))
+            logits = up(rng.standard_normal((T, base.E), dtype=np.float32))
+            ids, wts = ops.moe_route(logits, base.k, "softmax")
+            dbuf = ops.alloc_decode(T, base.k, base.H)
+            for _ in range(3):
+                ops.moe_ffn_decode(x, ids, wts, 0, base.E, wfmt, *dw, dbuf)
+            ts, tg = [], []
+            for i in range(iters):
+                _flush_caches(torch, scratch)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                ev[0].record()
+                ops.moe_sparse_gemv(x, False, ids, 0, base.E, wfmt, dw[0], dw[1], dw[2], dbuf.act,
+                                    dbuf.slot_row, glu=True)
+                ev[1].record()
+                ops.moe_sparse_gemv(dbuf.act, True, ids, 0, base.E, wfmt, dw[3], dw[4], dw[5],
+                                    dbuf.down, None, glu=False)
+                ev[2].record()
+                ops.moe_combine(dbuf.down, dbuf.slot_row, wts, 1.0, dbuf.out)
+                ev[3].record()
+                torch.cuda.synchronize()
+                ts.append(ev[0].elapsed_time(ev[3]) * 1e3)
+                tg.append(ev[0].elapsed_time(ev[2]) * 1e3)
+            U = int(np.unique(ids.cpu().numpy()).size)
+            H, N = base.H, base.N_gu
+            if wfmt == "fp8":
+                per_expert = N * H + H * H + 4 * 2
+            else:
+                per_expert = N * H // 2 + N * H // 32 + H * H // 2 + H * H // 32
+            B = U * (per_expert + (N + H) * 2) + T * base.k * H * 2 * 2 + T * H * 2
+            tgm = float(np.median(tg))
+            key = f"{wfmt}_T{T}"
+            out[key] = {"us_layer_cold_median": round(float(np.median(ts)), 3),
+                        "us_gemvs_cold_median": round(tgm, 3), "distinct_experts": U,
+                        "alg_bytes": int(B), "GBps": round(B / (tgm * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(B / (tgm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            log("decode", key, out[key])
+        del dw, base
+        torch.cuda.empty_cache()
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(c, log):
+    """The CPU oracle as it stands, on this GPU's whole layer (4096-token
+    group, 32 local experts), once, on the host cores."""
+    from oracle import moe as M
+    threads = os.cpu_count()
+    log(f"cpu baseline: oracle on the full layer ({threads} host threads)")
+    t0 = time.perf_counter()
+    ids, wts = M.route_softmax(c.logits[: c.own_tokens], c.k)
+    gids, gw = M.route_softmax(c.logits, c.k)
+    w = c.weights
+    M.prefill_expert_major(c.x, gids, gw, 0, c.E_local, c.A, c.I, w.w13, w.s13, w.w2, w.s2)
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline {dt:.1f} s")
+    return {"value": round(dt * 1e6, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "sample": "the whole layer once: route of 512 own tokens + the 4096-token group's "
+                      "scatter, both MX GEMMs (fp64), act-quant and combine; numpy with its BLAS "
+                      "thread pool"}
+
+
+if __name__ == "__main__":
+    main()

@@ -30,8 +30,9 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .formats import (bf16_to_f32, e2m1_decode, e2m1_unpack, e4m3_decode, e8m0_decode,
-                      pack_ue8m0_words, quant_mx_e4m3, round_to_bf16, sigmoid_f32)
+from .formats import (E2M1_VALUES, E4M3_VALUES, bf16_to_f32, e2m1_decode, e2m1_unpack,
+                      e4m3_decode, e8m0_decode, pack_ue8m0_words, quant_mx_e4m3, round_to_bf16,
+                      sigmoid_f32)
 
 GROUP = 32
 
@@ -212,17 +213,28 @@ def dequant_mxfp4_rows(packed, scale_bytes):
     return v * np.repeat(s, GROUP, axis=-1)
 
 
-def _lsb_exponent_min(v: np.ndarray) -> np.ndarray:
-    """Per row: the smallest exponent of the last set mantissa bit among the
-    row's non-zero entries (+large when the row is all zero)."""
-    m, e = np.frexp(v)
-    mi = np.abs(np.ldexp(m, 53)).astype(np.int64)
-    low = mi & (-mi)
-    tz = np.zeros(mi.shape, dtype=np.int64)
-    nz = mi > 0
-    tz[nz] = np.log2(low[nz].astype(np.float64)).astype(np.int64)
-    lsb = np.where(nz, e.astype(np.int64) - 53 + tz, 1 << 30)
-    return lsb.min(axis=-1)
+def _code_lsb_table(values: np.ndarray) -> np.ndarray:
+    """Exponent of the lowest set bit of each code's value (+large for 0)."""
+    out = np.full(values.shape[0], 1 << 20, dtype=np.int64)
+    for c, v in enumerate(values):
+        if v == 0 or not np.isfinite(v):
+            continue
+        m, e = np.frexp(abs(v))
+        mi = int(np.ldexp(m, 53))
+        out[c] = e - 53 + ((mi & -mi).bit_length() - 1)
+    return out
+
+
+_LSB_E4M3 = _code_lsb_table(E4M3_VALUES)
+_LSB_E2M1 = _code_lsb_table(E2M1_VALUES)
+
+
+def _row_lsb_min(code_lsb: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
+    """Per row: the smallest lowest-set-bit exponent over its non-zero
+    entries, where an entry is code * 2^(scale-127) per 32 columns."""
+    s = scale_bytes.astype(np.int64) - 127
+    per_group = code_lsb.reshape(code_lsb.shape[0], -1, GROUP).min(-1) + s
+    return per_group.min(-1)
 
 
 def block_max_bound(aq, ab, wq_packed, wb, block: int = 128):
@@ -254,7 +266,11 @@ def mx_gemm(aq, ab, wq_packed, wb, check_exact: bool = True):
     exact = A @ W.T
     tsum = np.abs(A) @ np.abs(W).T
     if check_exact and A.size and W.size:
-        lsb = _lsb_exponent_min(A)[:, None] + _lsb_exponent_min(W)[None, :]
+        # every term is a multiple of 2^(lsb_a + lsb_w); the fp64 sums are exact
+        # while the sum of magnitudes stays below 2^53 such units
+        la = _row_lsb_min(_LSB_E4M3[np.asarray(aq, np.uint8)], ab)
+        lw = _row_lsb_min(_LSB_E2M1[e2m1_unpack(wq_packed)], wb)
+        lsb = la[:, None] + lw[None, :]
         limit = np.ldexp(1.0, np.minimum(lsb + 53, 1000).astype(np.int64))
         bad = (tsum > 0) & (tsum >= limit)
         assert not bad.any(), "fp64 accumulation of the MX GEMM would round"
