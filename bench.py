@@ -80,7 +80,9 @@ def main():
     x = up_bf16(c.x)
     logits_group = up(c.logits)
     logits_own = up(c.logits[: c.own_tokens])
-    w13, s13, w2, s2 = up(w.w13), up(w.s13), up(w.w2), up(w.s2)
+    # load-time weight preparation: E8M0 weight scales -> packed MN-major words
+    w13, w2 = up(w.w13), up(w.w2)
+    s13, s2 = ops.moe_pack_weight_scales(up(w.s13)), ops.moe_pack_weight_scales(up(w.s2))
     # the group's routes (every rank routes its own 512 tokens; the 4096
     # tokens' ids are what this GPU receives)
     ids, wts = ops.moe_route(logits_group, c.k, "softmax")

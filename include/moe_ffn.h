@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum moe_status {
     MOE_OK = 0,
@@ -150,6 +150,23 @@ int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_star
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_pack_weight_scales - one-time, load-time relayout of MXFP4 weight
+ * scales into the packed MN-major words the grouped GEMMs consume.
+ * [SGL] section 2.1 (weight preparation runs once at load time so that the
+ * run-time GEMM never touches the weight layout) and 2.1.2 (weight scales
+ * become UE8M0 packed four per int32, MN-major).
+ *
+ *   w_scale         u8 [E, N, K/32]: E8M0 byte of columns [32j, 32j+32) of
+ *                   row n at w_scale[(e*N + n)*(K/32) + j]
+ *   w_scale_packed  int32 [E, K/128, N] out: word (e, c, n) holds the bytes
+ *                   of groups 4c..4c+3 of row n in byte 0..3 (little endian)
+ * Pure data movement (bit-exact). Requires K % 128 == 0, E <= 65535,
+ * K/128 <= 65535. The caller owns both buffers.
+ * ------------------------------------------------------------------------ */
+int moe_pack_weight_scales(const uint8_t* w_scale, int E, int N, int K,
+                           int32_t* w_scale_packed, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_gemm1 - gate/up projection of every live row with its expert's
  * MXFP4 w13, on scaled MX MFMA.
  * [SGL] sections 2.3 and 3.3 (contiguous grouped FP8 x FP4 GEMM: lhs
@@ -161,7 +178,8 @@ int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_star
  *   expert_ends  int32 [E_local]
  *   w13          u8 [E_local, 2I, H/2]: two E2M1 codes per byte, low nibble =
  *                even column; rows 0..I-1 gate, I..2I-1 up
- *   w13_scale    u8 [E_local, 2I, H/32]: E8M0 per 32 columns
+ *   w13_scale_packed  int32 [E_local, H/128, 2I]: E8M0 byte per 32 columns
+ *                of each w13 row, packed by moe_pack_weight_scales
  *   gateup       bf16 [M_cap, 2I] out: live rows only,
  *                gateup[r, n] = bf16_rne(sum_k xq*2^(xs-127) * w13*2^(s-127))
  *                accumulated in fp32
@@ -169,7 +187,8 @@ int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_star
  * ------------------------------------------------------------------------ */
 int moe_grouped_gemm1(const uint8_t* xq, const int32_t* xs, const int32_t* expert_ends,
                       int E_local, int A, int M_cap, int H, int I,
-                      const uint8_t* w13, const uint8_t* w13_scale, uint16_t* gateup, void* stream);
+                      const uint8_t* w13, const int32_t* w13_scale_packed, uint16_t* gateup,
+                      void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_act_quant_liverows - SiLU(gate)*up + FP8/UE8M0 quantisation of live
@@ -200,13 +219,16 @@ int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends, i
  * recipe follows K = I); [LIVE] section 2 (FC2 consumes the endpoints).
  *
  *   hq, hs       as produced by moe_act_quant_liverows (K = I)
- *   w2           u8 [E_local, H, I/2], w2_scale u8 [E_local, H, I/32]
+ *   w2           u8 [E_local, H, I/2]
+ *   w2_scale_packed  int32 [E_local, I/128, H]: moe_pack_weight_scales of the
+ *                E8M0 scales u8 [E_local, H, I/32]
  *   down         bf16 [M_cap, H] out: live rows only
  * Requires I % 128 == 0, H % 128 == 0, E_local <= 1024.
  * ------------------------------------------------------------------------ */
 int moe_grouped_gemm2(const uint8_t* hq, const int32_t* hs, const int32_t* expert_ends,
                       int E_local, int A, int M_cap, int I, int H,
-                      const uint8_t* w2, const uint8_t* w2_scale, uint16_t* down, void* stream);
+                      const uint8_t* w2, const int32_t* w2_scale_packed, uint16_t* down,
+                      void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine - unpermute and weighted top-k sum.

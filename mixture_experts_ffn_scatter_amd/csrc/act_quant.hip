@@ -8,9 +8,10 @@
 // is read once and FP8 + packed scales are written once; SiLU stays fp32.
 //
 // Work decomposition: a persistent grid walks 16-row units of
-// [0, end of the last expert). Each wave takes 4 rows of a unit; a row is
-// processed only if it lies inside some [start_e, end_e) (wave-uniform test).
-// A lane owns 8 consecutive columns of each 512-column chunk (16-byte loads
+// [0, end of the last expert). The (row, 512-column chunk) items of a unit
+// are spread over the waves; a row is processed only if it lies inside some
+// [start_e, end_e) (a wave-uniform test). A lane owns 8 consecutive columns
+// of a chunk (16-byte loads
 // of gate and up, 8-byte stores of codes), a 32-column group spans 4 lanes
 // (amax by two shuffles), a packed scale word spans 16 lanes. The words of
 // the unit's 16 rows are staged in LDS and stored MN-major so that each
@@ -29,7 +30,7 @@
 namespace moe {
 
 // sigma(g) for every bf16 g, generated at build time (gen_sigmoid_table.cpp)
-#define MOE_SIGMOID_TABLE_STORAGE __device__ const
+#define MOE_SIGMOID_TABLE_STORAGE __device__ const __attribute__((aligned(16)))
 #include "sigmoid_table.inc"
 
 constexpr int kActThreads = 256;
@@ -61,7 +62,7 @@ template <bool CLAMP>
 __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     const uint16_t* __restrict__ gateup, const int32_t* __restrict__ expert_ends, int E_local,
     int A, int M_cap, int I, float L, uint8_t* __restrict__ hq, int32_t* __restrict__ hs) {
-  __shared__ float s_tab[MOE_SIGMOID_TABLE_SIZE];
+  __shared__ __attribute__((aligned(16))) float s_tab[MOE_SIGMOID_TABLE_SIZE];
   __shared__ int s_start[kActMaxE];
   __shared__ int s_end[kActMaxE];
   __shared__ uint32_t s_words[kActMaxWordsPerRow * kActUnitRows];
@@ -70,8 +71,23 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  for (int i = tid; i < MOE_SIGMOID_TABLE_SIZE; i += kActThreads)
-    s_tab[i] = __uint_as_float(g_sigmoid_table[i]);
+  // table copy with 16-byte loads, all issued before the stores
+  static_assert(MOE_SIGMOID_TABLE_SIZE % 4 == 0, "table copied as 16-byte vectors");
+  constexpr int kVec = MOE_SIGMOID_TABLE_SIZE / 4;
+  constexpr int kPer = (kVec + kActThreads - 1) / kActThreads;
+  {
+    v4i tv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + j * kActThreads;
+      tv[j] = i < kVec ? reinterpret_cast<const v4i*>(g_sigmoid_table)[i] : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + j * kActThreads;
+      if (i < kVec) reinterpret_cast<v4i*>(s_tab)[i] = tv[j];
+    }
+  }
   for (int e = tid; e < E_local; e += kActThreads) {
     int s, en;
     expert_range(expert_ends, e, A, M_cap, s, en);
@@ -86,65 +102,80 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
   const int n_units = (last + kActUnitRows - 1) / kActUnitRows;
   const int words = I >> 7;
   const int nchunks = (I + 511) >> 9;
-  const uint16_t* __restrict__ base_g = gateup;
-
+  // a unit's work is a flat list of (row, 512-column chunk) items; each wave
+  // takes every 4th item and keeps kBatch items' loads in flight before it
+  // computes, so a wave has 8 x 16-byte loads outstanding per lane
+  constexpr int kBatch = 4;
+  const int items = kActUnitRows * nchunks;
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
     const int r0 = unit * kActUnitRows;
-    for (int j = 0; j < kActUnitRows / 4; ++j) {
-      const int rl = wid * (kActUnitRows / 4) + j;
-      const int r = r0 + rl;
+    if (tid < kActUnitRows) {
+      const int r = r0 + tid;
       bool live = false;
       if (r < last) {
         const int e = expert_of_row(s_start, E_local, r);
         live = r >= s_start[e] && r < s_end[e];
       }
-      if (lane == 0) s_live[rl] = live ? 1 : 0;
-      if (!live) continue;  // wave-uniform
-      const uint16_t* grow = base_g + (size_t)r * (2 * I);
-      const uint16_t* urow = grow + I;
-      for (int c = 0; c < nchunks; ++c) {
-        const int col = c * 512 + lane * 8;
-        const bool act = col < I;
-        v4i gv4 = v4i{0, 0, 0, 0}, uv4 = v4i{0, 0, 0, 0};
-        if (act) {
+      s_live[tid] = live ? 1 : 0;
+    }
+    __syncthreads();
+    for (int it0 = wid * kBatch; it0 < items; it0 += 4 * kBatch) {
+      v4i gv4[kBatch], uv4[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int it = it0 + b;
+        const int rl = it / nchunks;
+        const int col = (it - rl * nchunks) * 512 + lane * 8;
+        gv4[b] = v4i{0, 0, 0, 0};
+        uv4[b] = v4i{0, 0, 0, 0};
+        if (it < items && s_live[rl] && col < I) {
           // gate/up are read exactly once: stream them past the caches
-          gv4 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(grow + col));
-          uv4 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(urow + col));
+          const uint16_t* grow = gateup + (size_t)(r0 + rl) * (2 * I);
+          gv4[b] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(grow + col));
+          uv4[b] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(grow + I + col));
         }
-        const uint4 gr = make_uint4(gv4.x, gv4.y, gv4.z, gv4.w);
-        const uint4 ur = make_uint4(uv4.x, uv4.y, uv4.z, uv4.w);
-        float g[8] = {bf16_lo(gr.x), bf16_hi(gr.x), bf16_lo(gr.y), bf16_hi(gr.y),
-                      bf16_lo(gr.z), bf16_hi(gr.z), bf16_lo(gr.w), bf16_hi(gr.w)};
-        float u[8] = {bf16_lo(ur.x), bf16_hi(ur.x), bf16_lo(ur.y), bf16_hi(ur.y),
-                      bf16_lo(ur.z), bf16_hi(ur.z), bf16_lo(ur.w), bf16_hi(ur.w)};
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int it = it0 + b;
+        if (it >= items) break;  // wave-uniform
+        const int rl = it / nchunks;
+        if (!s_live[rl]) continue;  // wave-uniform
+        const int col = (it - rl * nchunks) * 512 + lane * 8;
+        const bool act = col < I;
+        const uint32_t gw[4] = {(uint32_t)gv4[b].x, (uint32_t)gv4[b].y, (uint32_t)gv4[b].z,
+                                (uint32_t)gv4[b].w};
+        const uint32_t uw[4] = {(uint32_t)uv4[b].x, (uint32_t)uv4[b].y, (uint32_t)uv4[b].z,
+                                (uint32_t)uv4[b].w};
         float h[8];
         float amax = 0.f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          float gv = g[q], uv = u[q];
+          float gv = (q & 1) ? bf16_hi(gw[q >> 1]) : bf16_lo(gw[q >> 1]);
+          float uv = (q & 1) ? bf16_hi(uw[q >> 1]) : bf16_lo(uw[q >> 1]);
           if (CLAMP) {
             gv = fminf(gv, L);
             uv = fminf(fmaxf(uv, -L), L);
           }
           const float sig = sigmoid_lookup(s_tab, gv);
-          const float s = gv * sig;
-          h[q] = s * uv;
+          const float sg = gv * sig;
+          h[q] = sg * uv;
           amax = fmaxf(amax, fabsf(h[q]));
         }
         amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-        const uint32_t b = ue8m0_ceil_byte(amax / 448.0f);
-        const float inv = e8m0_reciprocal(b);
+        const uint32_t bsc = ue8m0_ceil_byte(amax / 448.0f);
+        const float inv = e8m0_reciprocal(bsc);
         uint32_t lo = 0, hi = 0;
         lo = cvt_e4m3x2<false>(h[0] * inv, h[1] * inv, lo);
         lo = cvt_e4m3x2<true>(h[2] * inv, h[3] * inv, lo);
         hi = cvt_e4m3x2<false>(h[4] * inv, h[5] * inv, hi);
         hi = cvt_e4m3x2<true>(h[6] * inv, h[7] * inv, hi);
-        uint32_t word = b << (8 * ((lane >> 2) & 3));
+        uint32_t word = bsc << (8 * ((lane >> 2) & 3));
         word |= __shfl_xor(word, 4, 64);
         word |= __shfl_xor(word, 8, 64);
         if (act) {
-          *reinterpret_cast<uint2*>(hq + (size_t)r * I + col) = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(hq + (size_t)(r0 + rl) * I + col) = make_uint2(lo, hi);
           if ((lane & 15) == 0) s_words[(col >> 7) * kActUnitRows + rl] = word;
         }
       }
@@ -180,8 +211,10 @@ extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* exp
   if (E_local == 0 || M_cap == 0) return MOE_OK;
   if (!gateup || !expert_ends || !hq || !hs) return MOE_ERR_NULL;
   hipStream_t st = (hipStream_t)stream;
+  // two resident blocks per CU (the sigmoid table takes 33 KB of LDS per
+  // block, loaded once and reused for every unit the block walks)
   const int max_units = (M_cap + kActUnitRows - 1) / kActUnitRows;
-  const int grid = max_units < 1024 ? max_units : 1024;
+  const int grid = max_units < 512 ? max_units : 512;
   if (clamp)
     hipLaunchKernelGGL(act_quant_kernel<true>, dim3(grid), dim3(kActThreads), 0, st, gateup,
                        expert_ends, E_local, A, M_cap, I, clamp_limit, hq, hs);

@@ -8,7 +8,7 @@
 // t*k+s, so the permutation is unique.
 //
 // Three launches, none of which depends on a host-visible count:
-//   1. count  - one block per 32-token block: LDS histogram of its local
+//   1. count  - one block per 256-token block: LDS histogram of its local
 //               routes, written to workspace[w][e].
 //   2. scan   - one block: per-expert totals, the aligned exclusive scan
 //               over experts (the endpoint recurrence), expert_ends, and the
@@ -22,7 +22,7 @@
 
 namespace moe {
 
-constexpr int kTokBlock = 32;      // tokens per histogram block
+constexpr int kTokBlock = 256;     // tokens per histogram block
 constexpr int kScatterMaxE = 1024;
 constexpr int kScatterMaxK = 32;
 
@@ -75,8 +75,10 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int W, int E_local, 
   __shared__ int wave_tot[32];
   const int e = threadIdx.x;
   int total = 0;
-  if (e < E_local)
+  if (e < E_local) {
+#pragma unroll 8
     for (int w = 0; w < W; ++w) total += counts[(size_t)w * E_local + e];
+  }
   const int aligned = e < E_local ? align_up_dev(total, A) : 0;
   const int start = block_exclusive_scan_1024(aligned, wave_tot);
   if (e < E_local) {
@@ -111,12 +113,26 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
   __syncthreads();
   // rank of route (t, s) among earlier routes of the same expert in the
   // token block: count matches over [block start, t*k + s)
+  // counted in registers per slot, then reduced per wave: one LDS atomic
+  // per wave and slot instead of one per matching route
   const int rb = w * kTokBlock * k;
   const int rt = t * k;
+  int cnt[kScatterMaxK];
+#pragma unroll
+  for (int s = 0; s < kScatterMaxK; ++s) cnt[s] = 0;
   for (int r = rb + tid; r < rt + k; r += blockDim.x) {
     const int e = ids[r] - expert_start;
-    for (int s = 0; s < k; ++s)
-      if (r < rt + s && e == s_e[s] && e >= 0) atomicAdd(&s_cnt[s], 1);
+#pragma unroll
+    for (int s = 0; s < kScatterMaxK; ++s)
+      if (s < k) cnt[s] += (r < rt + s && e == s_e[s] && e >= 0) ? 1 : 0;
+  }
+#pragma unroll
+  for (int s = 0; s < kScatterMaxK; ++s) {
+    if (s >= k) break;  // block-uniform
+    int c = cnt[s];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
+    if ((tid & 63) == 0 && c) atomicAdd(&s_cnt[s], c);
   }
   __syncthreads();
   if (tid < k) {

@@ -214,7 +214,8 @@ def _tiny_state(ops, c, clamp=0.0):
     ids, wts = M.route_softmax(c.logits, c.k)
     buf = ops.alloc_grouped(c.T, c.k, c.E, c.M_cap, c.H, c.I, fill=True)
     w = c.weights
-    dw = dict(w13=dev(w.w13), s13=dev(w.s13), w2=dev(w.w2), s2=dev(w.s2))
+    dw = dict(w13=dev(w.w13), s13=ops.moe_pack_weight_scales(dev(w.s13)), w2=dev(w.w2),
+              s2=ops.moe_pack_weight_scales(dev(w.s2)))
     ops.moe_scatter_endpoints(dev(ids), 0, c.E, c.A, dev_bf16(c.x), buf.expert_ends, buf.route_row,
                               buf.xq, buf.xs, buf.workspace)
     return ids, wts, buf, dw
@@ -286,8 +287,9 @@ def test_prefill_chain_tiny_end_to_end_and_deterministic(ops):
     outs = []
     for _ in range(2):
         buf = ops.alloc_grouped(c.T, c.k, c.E, c.M_cap, c.H, c.I, fill=True)
-        y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A, dev(w.w13), dev(w.s13),
-                                dev(w.w2), dev(w.s2), buf)
+        y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A, dev(w.w13),
+                                ops.moe_pack_weight_scales(dev(w.s13)), dev(w.w2),
+                                ops.moe_pack_weight_scales(dev(w.s2)), buf)
         outs.append(host(y))
     assert np.array_equal(outs[0], outs[1])
     ok, mx, mean = end_to_end_ok(outs[0], ref.out)
@@ -309,9 +311,74 @@ def test_prefill_chain_window_clamp_scale(ops):
                                  w.w2[sl], w.s2[sl], clamp=6.0, routed_scale=0.5)
     buf = ops.alloc_grouped(c.T, c.k, E_local, M_cap, c.H, c.I, fill=True)
     y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), es, A, dev(w.w13[sl]),
-                            dev(w.s13[sl]), dev(w.w2[sl]), dev(w.s2[sl]), buf, clamp_limit=6.0,
+                            ops.moe_pack_weight_scales(dev(w.s13[sl])), dev(w.w2[sl]),
+                            ops.moe_pack_weight_scales(dev(w.s2[sl])), buf, clamp_limit=6.0,
                             routed_scale=0.5)
     ok, mx, mean = end_to_end_ok(host(y), ref.out)
     assert ok, (mx, mean)
     no_local = ~np.any((ids >= es) & (ids < es + E_local), axis=1)
     assert np.all(host(y)[no_local] == 0)
+
+
+# ------------------------------------------------- weight prep + full size
+
+def test_pack_weight_scales_bitexact(ops):
+    """Load-time relayout: byte j of word (e, c, n) is group 4c+j of row n."""
+    rng = np.random.default_rng(2024)
+    for E, N, K in ((3, 300, 512), (1, 128, 128), (2, 4096, 4096)):
+        say(f"pack weight scales E={E} N={N} K={K}")
+        s = rng.integers(0, 256, size=(E, N, K // 32), dtype=np.uint8)
+        got = host(ops.moe_pack_weight_scales(dev(s)))
+        want = np.empty((E, K // 128, N), np.int64)
+        for c in range(K // 128):
+            b = s[:, :, 4 * c: 4 * c + 4].astype(np.int64)
+            want[:, c, :] = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+        assert np.array_equal(got.view(np.uint32).astype(np.int64), want)
+
+
+def test_prefill_group_full_size_gemms_sampled(ops):
+    """Full EP-share shapes (4096 group tokens x top-6 -> 32 local experts,
+    H=4096, I=2048): GEMM1, act-quant, GEMM2 stage by stage on sampled rows
+    (head and tail of the hottest, a middle and the coldest live expert)."""
+    c = W.prefill()
+    ids, wts = M.route_softmax(c.logits, c.k)
+    w = c.weights
+    say("full-size prefill GEMMs: scatter")
+    buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, fill=True)
+    ops.moe_scatter_endpoints(dev(ids), 0, c.E_local, c.A, dev_bf16(c.x), buf.expert_ends,
+                              buf.route_row, buf.xq, buf.xs, buf.workspace)
+    say("full-size prefill GEMMs: gemm1 / act-quant / gemm2")
+    s13 = ops.moe_pack_weight_scales(dev(w.s13))
+    s2 = ops.moe_pack_weight_scales(dev(w.s2))
+    ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, dev(w.w13), s13, buf.gateup)
+    ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, 0.0, buf.hq, buf.hs)
+    ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, dev(w.w2), s2, buf.down)
+    ends = host(buf.expert_ends)
+    segs = _expert_rows(ends, c.A)
+    counts = np.array([r.size for r in segs])
+    live_e = np.flatnonzero(counts)
+    order = live_e[np.argsort(counts[live_e], kind="stable")]
+    picks = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})
+    xq, xs, gu = host(buf.xq), host(buf.xs), host(buf.gateup)
+    hq, hs, dn = host(buf.hq), host(buf.hs), host(buf.down)
+    live = np.zeros(c.M_cap, bool)
+    for rows in segs:
+        live[rows] = True
+    assert np.all(gu[~live] == BF16_SENT) and np.all(dn[~live] == BF16_SENT)
+    for e in picks:
+        rows = segs[e]
+        rows = np.unique(np.concatenate([rows[:8], rows[-8:]]))
+        say(f"  expert {e}: {segs[e].size} rows, checking {rows.size}")
+        ab = F.unpack_ue8m0_words(xs[:, rows].T)
+        _, exact, tsum = M.mx_gemm(xq[rows], ab, w.w13[e], w.s13[e])
+        bm = M.block_max_bound(xq[rows], ab, w.w13[e], w.s13[e])
+        ok, _, _ = gemm_within_bound(gu[rows], exact, tsum, c.H, bm)
+        assert ok.all(), f"gemm1 expert {e}: {np.count_nonzero(~ok)} outside bound"
+        q, b = M.act_quant_rows(gu[rows], c.I)
+        assert np.array_equal(hq[rows], q)
+        assert np.array_equal(hs[:, rows].T, F.pack_ue8m0_words(b))
+        hb = F.unpack_ue8m0_words(hs[:, rows].T)
+        _, exact, tsum = M.mx_gemm(hq[rows], hb, w.w2[e], w.s2[e])
+        bm = M.block_max_bound(hq[rows], hb, w.w2[e], w.s2[e])
+        ok, _, _ = gemm_within_bound(dn[rows], exact, tsum, c.I, bm)
+        assert ok.all(), f"gemm2 expert {e}: {np.count_nonzero(~ok)} outside bound"
