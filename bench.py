@@ -18,11 +18,12 @@ The same line carries:
   cpu_baseline  the CPU oracle timed on the host on the same layer
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--copy-calibration]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,6 +39,37 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 / MXFP8 matrix peak
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix peak
 
 
+# Counter-derived HBM traffic of the dominant kernel is taken from the
+# committed rocprofv3 summary; it is reported only while the kernel's sources
+# still hash to the value recorded when the counters were read.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_mx_gemm1_prefill_ep_share_hbm_traffic.txt")
+GEMM_SOURCES = ("mixture_experts_ffn_scatter_amd/csrc/gemm.hip",
+                "mixture_experts_ffn_scatter_amd/csrc/common.h")
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per GEMM1 launch (FETCH_SIZE + WRITE_SIZE, copy-scaled), or
+    None when no summary matches the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("TRAFFIC "):
+                    rec = json.loads(line[len("TRAFFIC "):])
+                    if rec.get("source_sha256") == gemm_source_hash():
+                        return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+    except OSError:
+        pass
+    return None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -45,7 +77,23 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run 4 plain 1 GiB device copies (the reference kernel that "
+                        "scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration():
+    """Four device-to-device copies of exactly 1 GiB through torch's copy kernel:
+    under rocprofv3 --pmc their FETCH_SIZE and WRITE_SIZE per dispatch give the
+    counter's reading for a known 2^30 bytes read and written."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 4}), flush=True)
 
 
 def main():
@@ -55,6 +103,9 @@ def main():
               "built for one GPU's expert share; see the sharding notes in DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     import mixture_experts_ffn_scatter_amd as pkg
@@ -160,7 +211,7 @@ def main():
     ach = bytes_[dom] / (dur_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": "grouped_mx_gemm_kernel (moe_grouped_gemm1)",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
                 "alg_bytes_per_launch": int(bytes_[dom]), "avg_launch_us": round(dur_us[dom], 3)}
 
     result = {
