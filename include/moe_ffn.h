@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 enum moe_status {
     MOE_OK = 0,
@@ -150,21 +150,31 @@ int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_star
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * moe_pack_weight_scales - one-time, load-time relayout of MXFP4 weight
- * scales into the packed MN-major words the grouped GEMMs consume.
+ * moe_pack_mx_weights - one-time, load-time relayout of MXFP4 expert weights
+ * (codes and E8M0 scales) into the fragment-ordered form the grouped GEMMs
+ * stream.
  * [SGL] section 2.1 (weight preparation runs once at load time so that the
- * run-time GEMM never touches the weight layout) and 2.1.2 (weight scales
- * become UE8M0 packed four per int32, MN-major).
+ * run-time GEMM never touches the checkpoint layout) and 2.1.2 (weights and
+ * scales are rewritten into the layout the GEMM kernel consumes).
  *
- *   w_scale         u8 [E, N, K/32]: E8M0 byte of columns [32j, 32j+32) of
- *                   row n at w_scale[(e*N + n)*(K/32) + j]
- *   w_scale_packed  int32 [E, K/128, N] out: word (e, c, n) holds the bytes
- *                   of groups 4c..4c+3 of row n in byte 0..3 (little endian)
- * Pure data movement (bit-exact). Requires K % 128 == 0, E <= 65535,
- * K/128 <= 65535. The caller owns both buffers.
+ *   w               u8 [E, N, K/2]: two E2M1 codes per byte, low nibble =
+ *                   even column (checkpoint layout)
+ *   w_scale         u8 [E, N, K/32]: E8M0 byte of columns [32j, 32j+32)
+ *   w_packed        u8, E*N*K/2 bytes, out: for column block cb = n/16 and
+ *                   k-step ks = k/128 a 1 KB chunk at ((e*N/16 + cb)*K/128 + ks)*1024
+ *                   whose 16 bytes at lane*16 are bytes [64ks + 16(lane/16), +16)
+ *                   of row 16cb + lane%16
+ *   w_scale_packed  u8, E*(N/16)*ceil(K/1024)*512 bytes, out: for column block
+ *                   cb and 8-step group q a 512 B unit at
+ *                   ((e*N/16 + cb)*ceil(K/1024) + q)*512 whose byte lane*8 + j is
+ *                   the E8M0 byte of group 4(8q + j) + lane/16 of row
+ *                   16cb + lane%16 (0 past the last k-step)
+ * Pure data movement (bit-exact). Requires K % 128 == 0, N % 16 == 0,
+ * E <= 65535. The caller owns all four buffers; the packed buffers are what
+ * moe_grouped_gemm1 / moe_grouped_gemm2 take.
  * ------------------------------------------------------------------------ */
-int moe_pack_weight_scales(const uint8_t* w_scale, int E, int N, int K,
-                           int32_t* w_scale_packed, void* stream);
+int moe_pack_mx_weights(const uint8_t* w, const uint8_t* w_scale, int E, int N, int K,
+                        uint8_t* w_packed, uint8_t* w_scale_packed, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_grouped_gemm1 - gate/up projection of every live row with its expert's
@@ -176,10 +186,10 @@ int moe_pack_weight_scales(const uint8_t* w_scale, int E, int N, int K,
  *
  *   xq, xs       as produced by moe_scatter_endpoints (K = H)
  *   expert_ends  int32 [E_local]
- *   w13          u8 [E_local, 2I, H/2]: two E2M1 codes per byte, low nibble =
- *                even column; rows 0..I-1 gate, I..2I-1 up
- *   w13_scale_packed  int32 [E_local, H/128, 2I]: E8M0 byte per 32 columns
- *                of each w13 row, packed by moe_pack_weight_scales
+ *   w13_packed, w13_scale_packed
+ *                moe_pack_mx_weights of w13 u8 [E_local, 2I, H/2] (two E2M1
+ *                codes per byte, low nibble = even column; rows 0..I-1 gate,
+ *                I..2I-1 up) and its E8M0 scales u8 [E_local, 2I, H/32]
  *   gateup       bf16 [M_cap, 2I] out: live rows only,
  *                gateup[r, n] = bf16_rne(sum_k xq*2^(xs-127) * w13*2^(s-127))
  *                accumulated in fp32
@@ -187,8 +197,8 @@ int moe_pack_weight_scales(const uint8_t* w_scale, int E, int N, int K,
  * ------------------------------------------------------------------------ */
 int moe_grouped_gemm1(const uint8_t* xq, const int32_t* xs, const int32_t* expert_ends,
                       int E_local, int A, int M_cap, int H, int I,
-                      const uint8_t* w13, const int32_t* w13_scale_packed, uint16_t* gateup,
-                      void* stream);
+                      const uint8_t* w13_packed, const uint8_t* w13_scale_packed,
+                      uint16_t* gateup, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_act_quant_liverows - SiLU(gate)*up + FP8/UE8M0 quantisation of live
@@ -219,16 +229,16 @@ int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends, i
  * recipe follows K = I); [LIVE] section 2 (FC2 consumes the endpoints).
  *
  *   hq, hs       as produced by moe_act_quant_liverows (K = I)
- *   w2           u8 [E_local, H, I/2]
- *   w2_scale_packed  int32 [E_local, I/128, H]: moe_pack_weight_scales of the
- *                E8M0 scales u8 [E_local, H, I/32]
+ *   w2_packed, w2_scale_packed
+ *                moe_pack_mx_weights of w2 u8 [E_local, H, I/2] and its E8M0
+ *                scales u8 [E_local, H, I/32]
  *   down         bf16 [M_cap, H] out: live rows only
  * Requires I % 128 == 0, H % 128 == 0, E_local <= 1024.
  * ------------------------------------------------------------------------ */
 int moe_grouped_gemm2(const uint8_t* hq, const int32_t* hs, const int32_t* expert_ends,
                       int E_local, int A, int M_cap, int I, int H,
-                      const uint8_t* w2, const int32_t* w2_scale_packed, uint16_t* down,
-                      void* stream);
+                      const uint8_t* w2_packed, const uint8_t* w2_scale_packed,
+                      uint16_t* down, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine - unpermute and weighted top-k sum.

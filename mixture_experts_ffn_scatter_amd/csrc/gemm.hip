@@ -1,16 +1,16 @@
 // moe_grouped_gemm1 / moe_grouped_gemm2: grouped MX GEMMs over the live rows
-// of the aligned expert layout, on gfx950 scaled MFMA.
+// of the aligned expert layout, on gfx950 scaled MFMA; and
+// moe_pack_mx_weights, the load-time weight preparation they consume.
 //
 //   out[m, n] = sum_k X[m, k] * W_e[n, k]      for m in [start_e, end_e)
 //
 // X is E4M3 with one UE8M0 byte per 32 columns (packed MN-major, four per
-// int32), W_e is packed E2M1 (two per byte, low nibble = even column) with
-// one E8M0 byte per 32 columns ("Blackwell DeepGEMM FusedMoE (sglang)",
-// sections 2.3 / 2.5 / 3.3 and 3.8: contiguous grouped FP8 x FP4 GEMM with
-// (1,32) weight scales; here the activation recipe is (1,32) as well).
-// "Blackwell FP4 MoE: live-row boundary", section 2: both GEMMs take the
-// int32 expert ends; rows outside [start_e, end_e) are neither read nor
-// written.
+// int32), W_e is E2M1 with one E8M0 byte per 32 columns ("Blackwell DeepGEMM
+// FusedMoE (sglang)", sections 2.3 / 2.5 / 3.3 and 3.8: contiguous grouped
+// FP8 x FP4 GEMM with (1,32) weight scales; here the activation recipe is
+// (1,32) as well). "Blackwell FP4 MoE: live-row boundary", section 2: both
+// GEMMs take the int32 expert ends; rows outside [start_e, end_e) are
+// neither read nor written.
 //
 // Mapping onto V_MFMA_SCALE_F32_16X16X128_F8F6F4 (lane layout measured on
 // gfx950 with a one-instruction probe): the weight tile is the A operand
@@ -23,79 +23,81 @@
 // 16x16 fp32 result gives lane l four consecutive output columns of row
 // l%16, stored as one 8-byte bf16 write.
 //
-// Scheduling: the tile list (expert, n-tile, m-tile) is rebuilt inside every
-// block from expert_ends (a block-wide scan of ceil(count_e/128) * N/512),
-// so the grid depends only on host-known sizes and the call needs no
-// device-to-host read. A persistent grid walks the list; m-tiles of one
-// (expert, n-tile) are adjacent so concurrent blocks share weight tiles in
-// cache. Empty experts produce no tiles and read no weights. Inside a tile,
-// 16-row blocks past the expert's end issue neither loads nor MFMAs.
+// Weight preparation (once, at load time; "Blackwell DeepGEMM FusedMoE
+// (sglang)", section 2.1: weights are rearranged into the layout the GEMM
+// consumes, so that the run-time GEMM never touches the checkpoint layout):
+// codes are stored in MFMA fragment order, one contiguous 1 KB chunk per
+// (16-column block, 128-wide k-step), and scales as one 8-byte word per lane
+// per (16-column block, 8 k-steps). A wave then streams its weights with
+// fully coalesced 16-byte loads straight into registers.
+//
+// Work decomposition. An item is (n-tile of 256 columns, expert, m-chunk of
+// up to 128 live rows). Items are listed n-tile-major and the list is cut
+// into 8 equal contiguous ranges, one per XCD (block b runs on XCD b % 8);
+// the blocks of an XCD take its items round-robin, so the m-chunks of one
+// (expert, n-tile) run side by side on one XCD and share its weight slice
+// in that L2, and every XCD streams about 1/8 of the weights. The list is
+// rebuilt inside every block from expert_ends (a block-wide scan), so the
+// grid depends only on host-known sizes and no count is read back.
+//
+// Inside an item, the 8 waves form 2 row groups x 4 column groups: wave
+// (rg, cg) computes rows [64rg, 64rg+64) x columns [64cg, 64cg+64) of the
+// tile, so an activation fragment read from LDS feeds 4 MFMAs. Its weight
+// fragments go global -> registers 4 k-steps ahead (both row groups read
+// the same fragments, the second from cache; a row group with no live rows
+// reads nothing). The activation chunk (shared by all waves) is loaded
+// 3 k-steps ahead into registers, one 16-row block per wave, and written
+// to a two-slot LDS ring one step ahead; one barrier per k-step. Loads use buffer resources whose
+// range ends at the last live row (or column): lanes past it read zeros
+// without touching memory, so padding rows are never read and every wave
+// issues the same instruction stream.
 #include "common.h"
+
+#ifndef GEMM_CB
+#define GEMM_CB 2
+#endif
+#ifndef GEMM_WD
+#define GEMM_WD 4
+#endif
+#ifndef GEMM_XD
+#define GEMM_XD 2
+#endif
 
 namespace moe {
 
-constexpr int kGemmThreads = 512;  // 8 waves: 2 (rows) x 4 (columns)
-constexpr int kGemmBM = 128;       // rows (tokens) per tile
-constexpr int kGemmBN = 512;       // output columns per tile
-constexpr int kGemmBK = 128;       // k per pipeline stage (one MFMA k-step)
-constexpr int kGemmStages = 3;
+constexpr int kGemmThreads = 512;  // 8 waves
+constexpr int kGemmBM = 128;       // rows per item (8 blocks of 16)
+constexpr int kGemmBN = 256;       // columns per item (16 blocks of 16)
+constexpr int kGemmCB = GEMM_CB;                        // column blocks per wave
+constexpr int kGemmNCG = kGemmBN / 16 / kGemmCB;            // column groups
+constexpr int kGemmMB = (kGemmBM / 16) / (kGemmThreads / 64 / kGemmNCG);  // row blocks per wave
+static_assert(kGemmNCG * (kGemmBM / 16 / kGemmMB) == kGemmThreads / 64, "wave grid");
+constexpr int kGemmU = 8;          // k-loop unroll (one weight-scale word group)
+constexpr int kGemmWD = GEMM_WD;   // weight prefetch distance in k-steps
+constexpr int kGemmXD = GEMM_XD;   // activation register prefetch depth
 constexpr int kGemmMaxE = 1024;
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: reads zero, no traffic
 
-// One pipeline stage in LDS, in MFMA fragment order so that every fragment
-// read is one contiguous 1 KB ds_read_b128 per wave:
-//   w[nb][lane]      16 B: weight row 16nb + lane%16, bytes [16*(lane/16), +16) of the k-step
-//   x[mb][h][lane]   16 B: activation row 16mb + lane%16, k [64h + 16*(lane/16), +16)
-//   ws[n], xs[m]     the packed E8M0 word (four 32-groups) of the k-step
-struct __attribute__((aligned(16))) GemmStage {
-  uint8_t w[kGemmBN / 16][64 * 16];
+// One LDS slot: the activation chunk of one k-step in MFMA fragment order
+// (x[mb][h][lane] = 16 bytes of row 16mb + lane%16, k [64h + 16(lane/16), +16))
+// and its 128 packed scale words.
+struct __attribute__((aligned(16))) GemmXSlot {
   uint8_t x[kGemmBM / 16][2][64 * 16];
-  uint32_t ws[kGemmBN];
   uint32_t xs[kGemmBM];
 };
 
-// Direct global -> LDS copies (16 or 4 bytes per lane; lane i's bytes land
-// at the wave-uniform LDS base in M0 plus i * size). Issued through inline
-// assembly so that the compiler does not track them: its conservative
-// tracking would drain the whole ring before every LDS read. Completion is
-// awaited explicitly with wait_vmcnt() before the ring barrier.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-// base: wave-uniform global address (SGPR pair); off: per-lane byte offset
-__device__ __forceinline__ void lds_load16(const void* base, uint32_t off, const void* l) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_load4(const void* base, uint32_t off, const void* l) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(off), "s"(base), "s"(lds_addr(l)) : "memory", "m0");
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // raw buffer (stride 0); word 3 as for every gfx9 raw buffer
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-// Workgroup barrier for the LDS ring. __syncthreads() adds a release fence
-// that drains every outstanding load of the wave, which would empty the
-// pipeline; here each wave has already waited for its own copies of the
-// stage it is about to read, so a bare s_barrier (plus completion of this
-// wave's LDS reads) is enough. The memory clobber keeps the compiler from
-// moving LDS accesses across it.
+// Workgroup barrier without the release fence of __syncthreads() (which
+// would wait for every outstanding global load and empty the prefetch):
+// this wave's LDS writes are completed first, which is all the ring needs.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// wait until at most N vector-memory operations of this wave are in flight
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-// the same with a wave-uniform runtime count (0..16); the immediate comes from a switch
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-  switch (n) {
-#define MOE_W(N) case N: wait_vmcnt<N>(); break;
-    MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7) MOE_W(8)
-    MOE_W(9) MOE_W(10) MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14) MOE_W(15) MOE_W(16)
-#undef MOE_W
-    default: wait_vmcnt<0>(); break;
-  }
 }
 
 __device__ int block_exclusive_scan(int v, int* tmp) {
@@ -115,20 +117,43 @@ __device__ int block_exclusive_scan(int v, int* tmp) {
   return off + incl - v;
 }
 
+// One work item's load parameters. Buffer ranges end at the item's last
+// live column block (weights) and last live row (activations); an absent
+// item has empty ranges, so every load from it reads zero without touching
+// memory.
+struct GemmItem {
+  __amdgpu_buffer_rsrc_t wr, sr, xr, xsr;
+  uint32_t wo[kGemmCB], so[kGemmCB];   // per-lane weight / scale offsets
+  uint32_t xso;                        // per-lane scale-word offset (row part)
+  int r0, rows, nblk, mlive, cb0, ncb, valid;
+};
+
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
     const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
     const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int K, int N,
-    const uint8_t* __restrict__ W, const int32_t* __restrict__ Wsp, uint16_t* __restrict__ out) {
-  __shared__ GemmStage st[kGemmStages];
+    const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out) {
+  __shared__ GemmXSlot xl[2];
   __shared__ int s_prefix[kGemmMaxE + 1];
   __shared__ int s_tmp[kGemmThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int rg = wid / kGemmNCG;         // row group: row blocks [MB*rg, MB*rg+MB)
+  const int cg = wid % kGemmNCG;         // column group: column blocks [CB*cg, CB*cg+CB)
+  const int KS = K / 128;                // k-steps
+  const int KS8 = (KS + 7) / 8;          // 8-step scale groups
+  const int NB = N / 16;                 // column blocks
   const int NT = (N + kGemmBN - 1) / kGemmBN;
+  // With KS a multiple of the weight prefetch distance (K % 512 == 0) the
+  // register rings line up across items, and the loads of the next item's
+  // first steps are issued during the current item's last ones. Otherwise
+  // each item starts with its own prologue.
+  const bool chain = KS % kGemmWD == 0;
 
-  // per-expert tile counts and their exclusive scan (2 experts per thread)
+  // m-chunks per expert and their exclusive scan (2 experts per thread)
   int cnt[2];
   int local_sum = 0;
 #pragma unroll
@@ -138,7 +163,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
     if (e < E_local) {
       int s, en;
       expert_range(expert_ends, e, A, M_cap, s, en);
-      cnt[j] = ((en - s + kGemmBM - 1) / kGemmBM) * NT;
+      cnt[j] = (en - s + kGemmBM - 1) / kGemmBM;
     }
     local_sum += cnt[j];
   }
@@ -151,218 +176,309 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
   }
   if (tid == kGemmThreads - 1) s_prefix[E_local] = run;
   __syncthreads();
-  const int total = s_prefix[E_local];
+  const int MT = s_prefix[E_local];      // m-chunks over all experts
+  const int L = MT * NT;                 // items
 
-  const int wm = wid & 1;    // wave's 64-row half of the tile
-  const int wn = wid >> 1;   // wave's 128-column quarter of the tile
-  const int l16 = lane & 15;
-  const int kq = lane >> 4;
-  const size_t wrow = (size_t)K / 2;
-  const int nk = K / kGemmBK;
+  // this block's XCD range of the item list and its slot in it
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int nslot = gridDim.x >> 3;      // the grid is a multiple of 8
+  const int i_end = (int)(((long long)L * (xcd + 1)) / 8);
+  const int first = (int)(((long long)L * xcd) / 8) + slot;
 
-  // XCD-aware order: blocks are dealt round-robin over the 8 XCDs, so
-  // block b runs on XCD b % 8. Renumber so that each XCD walks a contiguous
-  // run of the tile list: the n-tiles of one expert (which share its
-  // activation rows) and the m-tiles of one n-tile (which share its weight
-  // slice) then meet in the same L2.
-  const int G = gridDim.x;
-  const int vb = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  for (int tile = vb; tile < total; tile += G) {
+  const uint32_t xo = (uint32_t)(16 * wid + l16) * (uint32_t)K + 16 * g;   // staged row block wid
+
+  auto make_item = [&](int item) {
+    GemmItem it;
+    it.valid = item < i_end;
+    if (!it.valid) {
+      it.wr = it.sr = it.xr = it.xsr = make_rsrc(Wp, 0u);
+#pragma unroll
+      for (int c = 0; c < kGemmCB; ++c) it.wo[c] = it.so[c] = kOob;
+      it.xso = kOob;
+      it.r0 = it.rows = it.nblk = it.mlive = it.cb0 = it.ncb = 0;
+      return it;
+    }
+    const int nt = item / MT;
+    const int j = item - nt * MT;
     int lo = 0, hi = E_local - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+      if (s_prefix[mid] <= j) lo = mid; else hi = mid - 1;
     }
     const int e = lo;
     int start, end;
     expert_range(expert_ends, e, A, M_cap, start, end);
-    const int mt = (end - start + kGemmBM - 1) / kGemmBM;
-    const int local = tile - s_prefix[e];
-    const int n_tile = local / mt;
-    const int m_tile = local - n_tile * mt;
-    const int tr0 = start + m_tile * kGemmBM;   // first row of the tile
-    const int tn0 = n_tile * kGemmBN;           // first column of the tile
-    const uint8_t* We = W + (size_t)e * N * wrow;
-    const int32_t* Wse = Wsp + (size_t)e * nk * N;   // [K/128][N] words of expert e
-
-    // this wave's share of each stage's copies; only live data is fetched:
-    //   weights: columns [tn0 + 64*wid, +64) (4 x 1 KB + 256 B of scales)
-    //   activations: rows [tr0 + 16*wid, +16) (2 x 1 KB) when any is live;
-    //   activation scales: waves 0,1 fetch rows [tr0 + 64*wid, +64)
-    const bool w_live = tn0 + 64 * wid < N;
-    const bool x_live = tr0 + 16 * wid < end;
-    const bool xs_live = wid < 2 && tr0 + 64 * wid < end;
-    const int loads = (w_live ? 5 : 0) + (x_live ? 2 : 0) + (xs_live ? 1 : 0);
-    // per-lane byte offsets (loop-invariant); the k-step advances the
-    // wave-uniform bases instead. Offsets stay below 4 GiB: a weight matrix
-    // is N*K/2 bytes and an activation buffer M_cap*K bytes.
-    const uint32_t ow = (uint32_t)((size_t)(tn0 + 64 * wid + l16) * wrow + kq * 16);
-    const uint32_t ow_step = (uint32_t)(16 * wrow);
-    const uint32_t osw = (uint32_t)(4 * (tn0 + 64 * wid + lane));
-    const int mx = min(tr0 + 16 * wid + l16, end - 1);   // never a padding row
-    const uint32_t ox = (uint32_t)((size_t)mx * K + kq * 16);
-    const uint32_t osx = (uint32_t)(4 * min(tr0 + 64 * wid + lane, end - 1));
-
-    auto issue = [&](int ks, GemmStage& S) {
-      const int k0 = ks * kGemmBK;
-      if (w_live) {
-        const uint8_t* bw = We + (k0 >> 1);
+    it.r0 = start + (j - s_prefix[e]) * kGemmBM;
+    it.rows = min(kGemmBM, end - it.r0);                  // >= 1
+    it.nblk = (it.rows + 15) >> 4;
+    it.mlive = min(max(it.nblk - kGemmMB * rg, 0), kGemmMB);
+    it.cb0 = nt * (kGemmBN / 16);
+    it.ncb = min(kGemmBN / 16, NB - it.cb0);
+    it.wr = make_rsrc(Wp + ((size_t)e * NB + it.cb0) * KS * 1024, (uint32_t)(it.ncb * KS) * 1024u);
+    it.sr = make_rsrc(Sp + ((size_t)e * NB + it.cb0) * KS8 * 512, (uint32_t)(it.ncb * KS8) * 512u);
+    it.xr = make_rsrc(X + (size_t)it.r0 * K, (uint32_t)it.rows * (uint32_t)K);
+    it.xsr = make_rsrc(Xs + it.r0, (uint32_t)((KS - 1) * M_cap + it.rows) * 4u);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lds_load16(bw, ow + j * ow_step, &S.w[4 * wid + j][0]);
-        lds_load4(Wse + (size_t)ks * N, osw, &S.ws[64 * wid]);
+    for (int c = 0; c < kGemmCB; ++c) {
+      const int cb = kGemmCB * cg + c;
+      const bool live = cb < it.ncb && it.mlive > 0;
+      it.wo[c] = live ? (uint32_t)(cb * KS) * 1024u + lane * 16 : kOob;
+      it.so[c] = live ? (uint32_t)(cb * KS8) * 512u + lane * 8 : kOob;
+    }
+    it.xso = (lane < 16 && 16 * wid + l16 < it.rows) ? (uint32_t)(16 * wid + l16) * 4u : kOob;
+    return it;
+  };
+
+  // loads of step ks of item p (ks < KS)
+  auto load_w = [&](const GemmItem& p, int ks, v4i* dst) {
+#pragma unroll
+    for (int c = 0; c < kGemmCB; ++c)
+      dst[c] = __builtin_amdgcn_raw_buffer_load_b128(p.wr, p.wo[c] + ks * 1024, 0, 0);
+  };
+  auto load_s = [&](const GemmItem& p, int q, v2i* dst) {
+#pragma unroll
+    for (int c = 0; c < kGemmCB; ++c)
+      dst[c] = __builtin_amdgcn_raw_buffer_load_b64(p.sr, p.so[c] + q * 512, 0, 0);
+  };
+  auto load_x = [&](const GemmItem& p, int ks, v4i* dst, uint32_t& ws) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b128(p.xr, xo + ks * 128, 0, 0);
+    dst[1] = __builtin_amdgcn_raw_buffer_load_b128(p.xr, xo + ks * 128 + 64, 0, 0);
+    ws = __builtin_amdgcn_raw_buffer_load_b32(
+        p.xsr, p.xso == kOob ? kOob : p.xso + (uint32_t)(ks * M_cap) * 4u, 0, 0);
+  };
+  auto store_x = [&](int sl, const v4i* src, uint32_t ws) {
+    *reinterpret_cast<v4i*>(&xl[sl].x[wid][0][lane * 16]) = src[0];
+    *reinterpret_cast<v4i*>(&xl[sl].x[wid][1][lane * 16]) = src[1];
+    if (lane < 16) xl[sl].xs[16 * wid + lane] = ws;
+  };
+
+  v4i wbuf[kGemmWD][kGemmCB];
+  v2i s_cur[kGemmCB], s_nxt[kGemmCB];
+  v4i xbuf[kGemmXD][2];
+  uint32_t xsb[kGemmXD];
+  const GemmItem none = make_item(i_end);
+
+  // prologue of an item: weights of steps 0..WD-1, scale groups 0 and 1,
+  // activations of steps 0..XD-1 (step 0 goes to LDS slot 0 and its
+  // registers take step XD); loads past the item read nothing
+  auto prologue = [&](const GemmItem& p) {
+#pragma unroll
+    for (int s = 0; s < kGemmWD; ++s) load_w(s < KS ? p : none, s < KS ? s : 0, wbuf[s]);
+    load_s(p, 0, s_cur);
+    load_s(KS8 > 1 ? p : none, 1, s_nxt);
+#pragma unroll
+    for (int s = 0; s < kGemmXD; ++s) load_x(s < KS ? p : none, s < KS ? s : 0, xbuf[s], xsb[s]);
+    store_x(0, xbuf[0], xsb[0]);
+    load_x(kGemmXD < KS ? p : none, kGemmXD < KS ? kGemmXD : 0, xbuf[0], xsb[0]);
+    ring_barrier();
+  };
+
+  int item = first;
+  GemmItem cur = make_item(item);
+  if (cur.valid) prologue(cur);
+  while (cur.valid) {
+    const GemmItem nxt = make_item(item + nslot);
+    // loads for steps past the end of this item come from the next one
+    const GemmItem& pf = chain ? nxt : none;
+
+    v4f acc[kGemmCB][kGemmMB];
+#pragma unroll
+    for (int c = 0; c < kGemmCB; ++c)
+#pragma unroll
+      for (int i = 0; i < kGemmMB; ++i) acc[c][i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = 0; kb < KS; kb += kGemmU) {
+      if (kb > 0) {
+#pragma unroll
+        for (int c = 0; c < kGemmCB; ++c) s_cur[c] = s_nxt[c];
       }
-      if (x_live) {
-        lds_load16(X + k0, ox, &S.x[wid][0][0]);
-        lds_load16(X + k0 + 64, ox, &S.x[wid][1][0]);
+      // the scale group after the current one: this item's, else the next
+      // item's group 0 (groups 0 and 1 of the first item come from the prologue)
+      if (kb > 0) {
+        const int q = kb / kGemmU + 1;
+        load_s(q < KS8 ? cur : pf, q < KS8 ? q : 0, s_nxt);
       }
-      if (xs_live) lds_load4(Xs + (size_t)(k0 >> 7) * M_cap, osx, &S.xs[64 * wid]);
-    };
+#pragma unroll
+      for (int jj = 0; jj < kGemmU; ++jj) {
+        const int ks = kb + jj;
+        if (ks >= KS) break;
+        // stage step ks+1 (of this item, else step 0 of the next) into the
+        // other slot, then refill its registers (xbuf[i % XD] holds step i)
+        const int xi = (jj + 1) % kGemmXD;
+        if (ks + 1 < KS || chain) store_x((jj + 1) & 1, xbuf[xi], xsb[xi]);
+        {
+          const int t = ks + 1 + kGemmXD;
+          load_x(t < KS ? cur : pf, t < KS ? t : t - KS, xbuf[xi], xsb[xi]);
+        }
 
-    const int row0 = tr0 + wm * 64;     // this wave's first output row
-    const int rows_left = end - row0;
-    int nblk = rows_left <= 0 ? 0 : (rows_left + 15) / 16;
-    nblk = nblk > 4 ? 4 : nblk;
-    const bool c_live = tn0 + 128 * wn < N;   // N % 128 == 0: whole quarter live or dead
-    if (!c_live) nblk = 0;
-
-    v4f acc[8][4];
+        // compute step ks from slot ks % 2 (kb and KS are even)
+        const GemmXSlot& S = xl[jj & 1];
+        v8i a8[kGemmCB];
+        int sa[kGemmCB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // the wave's 8 column blocks in two halves of 4, so that only 4 weight
-    // fragments are live next to the 128 accumulators; activation fragments
-    // are read once per half
-    auto compute = [&](const GemmStage& S) {
-      if (nblk == 0) return;
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        v4i a[4];
-        int sa[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int nb = 8 * wn + 4 * hb + j;
-          a[j] = *reinterpret_cast<const v4i*>(&S.w[nb][lane * 16]);
-          sa[j] = (int)(S.ws[nb * 16 + l16] >> (8 * kq));
+        for (int c = 0; c < kGemmCB; ++c) {
+          const v4i wv = wbuf[jj % kGemmWD][c];
+          a8[c] = v8i{wv.x, wv.y, wv.z, wv.w, 0, 0, 0, 0};
+          // weight scale byte of this step moved to byte 0 (opsel 0)
+          sa[c] = (int)((uint32_t)s_cur[c][jj >> 2] >> (8 * (jj & 3)));
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          if (mb < nblk) {
-            const v4i lo4 = *reinterpret_cast<const v4i*>(&S.x[4 * wm + mb][0][lane * 16]);
-            const v4i hi4 = *reinterpret_cast<const v4i*>(&S.x[4 * wm + mb][1][lane * 16]);
+        for (int i = 0; i < kGemmMB; ++i) {
+          if (i < cur.mlive) {
+            const int mb = kGemmMB * rg + i;
+            const v4i lo4 = *reinterpret_cast<const v4i*>(&S.x[mb][0][lane * 16]);
+            const v4i hi4 = *reinterpret_cast<const v4i*>(&S.x[mb][1][lane * 16]);
             const v8i b = v8i{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-            const int sb = (int)(S.xs[(4 * wm + mb) * 16 + l16] >> (8 * kq));
+            const int sb = (int)(S.xs[mb * 16 + l16] >> (8 * g));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const v8i a8 = v8i{a[j].x, a[j].y, a[j].z, a[j].w, 0, 0, 0, 0};
-              acc[4 * hb + j][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  a8, b, acc[4 * hb + j][mb], 4, 0, 0, sa[j], 0, sb);
-            }
+            for (int c = 0; c < kGemmCB; ++c)
+              acc[c][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  a8[c], b, acc[c][i], 4, 0, 0, sa[c], 0, sb);
           }
         }
-      }
-    };
-
-    // the ring: keep kGemmStages-1 stages in flight; at step ks refill the
-    // slot consumed at step ks-1, wait for stage ks, compute, and fence
-    // before that slot is refilled again
-#pragma unroll
-    for (int s = 0; s < kGemmStages - 1; ++s)
-      if (s < nk) issue(s, st[s]);
-    for (int ks = 0; ks < nk; ++ks) {
-      const int nxt = ks + kGemmStages - 1;
-      if (nxt < nk) {
-        issue(nxt, st[nxt % kGemmStages]);
-        wait_vmcnt_dyn((kGemmStages - 1) * loads);
-      } else {
-        wait_vmcnt_dyn((nk - 1 - ks) * loads);
-      }
-      ring_barrier();
-      compute(st[ks % kGemmStages]);
-      ring_barrier();
-    }
-
-    // epilogue: lane holds columns n0+16nb+4kq .. +3 of row row0+16mb+l16
-    const int n0 = tn0 + wn * 128;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = row0 + mb * 16 + l16;
-      if (mb >= nblk || m >= end) continue;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int n = n0 + nb * 16 + kq * 4;
-        const v4f c = acc[nb][mb];
-        const uint2 o = make_uint2(pack_bf16x2(c.x, c.y), pack_bf16x2(c.z, c.w));
-        *reinterpret_cast<uint2*>(out + (size_t)m * N + n) = o;
+        // refill this step's weight registers with step ks + WD (of this
+        // item, else of the next)
+        {
+          const int t = ks + kGemmWD;
+          load_w(t < KS ? cur : pf, t < KS ? t : t - KS, wbuf[jj % kGemmWD]);
+        }
+        ring_barrier();
       }
     }
+    // the next item's scale groups 0 and 1 (group 0 is already in s_nxt
+    // when this item had more than one group, else in flight below)
+    if (chain) {
+#pragma unroll
+      for (int c = 0; c < kGemmCB; ++c) s_cur[c] = s_nxt[c];
+      if (KS8 == 1) load_s(nxt, 0, s_cur);
+      load_s(KS8 > 1 ? nxt : none, 1, s_nxt);
+    }
+
+    // epilogue: lane holds columns 16cb + 4g .. +3 of row r0 + 16mb + l16
+#pragma unroll
+    for (int c = 0; c < kGemmCB; ++c) {
+      const int cb = kGemmCB * cg + c;
+      if (cb >= cur.ncb) continue;
+      const int n = (cur.cb0 + cb) * 16 + 4 * g;
+#pragma unroll
+      for (int i = 0; i < kGemmMB; ++i) {
+        const int mr = 16 * (kGemmMB * rg + i) + l16;
+        if (i >= cur.mlive || mr >= cur.rows) continue;
+        const v4f v = acc[c][i];
+        const uint2 o = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        *reinterpret_cast<uint2*>(out + (size_t)(cur.r0 + mr) * N + n) = o;
+      }
+    }
+    item += nslot;
+    cur = nxt;
+    if (!chain && cur.valid) prologue(cur);
   }
 }
 
+// Load-time weight preparation (bit-exact data movement):
+//   codes  w [E][N][K/2] -> wp [E][N/16][K/128][64 lanes][16 B]
+//          lane l of chunk (e, cb, ks) = bytes [64ks + 16(l/16), +16) of row 16cb + l%16
+//   scales s [E][N][K/32] -> sp [E][N/16][ceil(K/1024)][64 lanes][8 B]
+//          byte j of lane l of (e, cb, q) = group 4(8q + j) + l/16 of row 16cb + l%16,
+//          zero past the last k-step
+// One wave per 1 KB chunk (codes) or 512 B unit (scales).
+__global__ __launch_bounds__(256) void pack_mx_codes_kernel(const uint8_t* __restrict__ w, int N,
+                                                            int K, uint8_t* __restrict__ wp) {
+  const int KS = K / 128;
+  const size_t per_e = (size_t)(N / 16) * KS;
+  const size_t chunk = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (chunk >= per_e) return;
+  const int e = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int cb = (int)(chunk / KS);
+  const int ks = (int)(chunk - (size_t)cb * KS);
+  const size_t row = (size_t)e * N + 16 * cb + (lane & 15);
+  const uint4 v =
+      *reinterpret_cast<const uint4*>(w + row * (size_t)(K / 2) + 64 * ks + 16 * (lane >> 4));
+  *reinterpret_cast<uint4*>(wp + ((size_t)e * per_e + chunk) * 1024 + lane * 16) = v;
+}
+
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ s, int N,
+                                                             int K, uint8_t* __restrict__ sp) {
+  const int KS = K / 128;
+  const int KS8 = (KS + 7) / 8;
+  const size_t per_e = (size_t)(N / 16) * KS8;
+  const size_t unit = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= per_e) return;
+  const int e = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int cb = (int)(unit / KS8);
+  const int q = (int)(unit - (size_t)cb * KS8);
+  const uint8_t* src = s + ((size_t)e * N + 16 * cb + (lane & 15)) * (size_t)(K / 32);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int ks = 8 * q + jj;
+    const uint32_t b = ks < KS ? src[4 * ks + (lane >> 4)] : 0u;
+    if (jj < 4) lo |= b << (8 * jj); else hi |= b << (8 * (jj - 4));
+  }
+  *reinterpret_cast<uint2*>(sp + ((size_t)e * per_e + unit) * 512 + lane * 8) = make_uint2(lo, hi);
+}
+
 static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_t* ends,
-                               int E_local, int A, int M_cap, int K, int N, const uint8_t* W,
-                               const int32_t* Ws, uint16_t* out, void* stream) {
+                               int E_local, int A, int M_cap, int K, int N, const uint8_t* Wp,
+                               const uint8_t* Sp, uint16_t* out, void* stream) {
   if (E_local < 0 || E_local > kGemmMaxE || A < 1 || M_cap < 0 || K <= 0 || N <= 0)
     return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
-  // per-lane copy offsets are 32-bit: one expert's weights and the whole
-  // activation buffer must each stay below 4 GiB
-  if ((long long)N * K / 2 >= (1LL << 32) || (long long)M_cap * K >= (1LL << 32))
+  // buffer ranges are 32-bit: one expert's packed weights and one 128-row
+  // activation chunk must stay below 2 GiB
+  if ((long long)N * K / 2 >= (1LL << 31) || (long long)kGemmBM * K >= (1LL << 31) ||
+      (long long)(K / 128) * M_cap * 4 >= (1LL << 31))
     return MOE_ERR_SHAPE;
   if (E_local == 0 || M_cap == 0) return MOE_OK;
-  if (!X || !Xs || !ends || !W || !Ws || !out) return MOE_ERR_NULL;
-  // one resident block per CU (LDS-limited); each walks the device-built tile list
-  const int max_tiles = ((M_cap + kGemmBM - 1) / kGemmBM + E_local) * ((N + kGemmBN - 1) / kGemmBN);
-  const int grid = max_tiles < 256 ? max_tiles : 256;
+  if (!X || !Xs || !ends || !Wp || !Sp || !out) return MOE_ERR_NULL;
+  // one resident block per CU; each walks its XCD's share of the item list
+  const int NT = (N + kGemmBN - 1) / kGemmBN;
+  const long long max_items = (long long)((M_cap + kGemmBM - 1) / kGemmBM + E_local) * NT;
+  int grid = max_items < 256 ? (int)max_items : 256;
+  grid = (grid + 7) & ~7;
   hipLaunchKernelGGL(grouped_mx_gemm_kernel, dim3(grid), dim3(kGemmThreads), 0,
-                     (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, W, Ws, out);
+                     (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, Wp, Sp, out);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
 
-// E8M0 weight scales, row-major bytes [E][N][K/32] -> packed words laid out
-// MN-major [E][K/128][N] (word c of row n holds groups 4c..4c+3, byte j =
-// group 4c+j). One word per thread; consecutive threads write consecutive n.
-__global__ __launch_bounds__(256) void pack_weight_scales_kernel(const uint8_t* __restrict__ s,
-                                                                 int N, int K,
-                                                                 int32_t* __restrict__ out) {
-  const int e = blockIdx.z;
-  const int c = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(s + ((size_t)e * N + n) * (K / 32) + 4 * c);
-  out[((size_t)e * (K / 128) + c) * N + n] = (int32_t)w;
-}
-
 }  // namespace moe
 
-extern "C" int moe_pack_weight_scales(const uint8_t* w_scale, int E, int N, int K,
-                                      int32_t* w_scale_packed, void* stream) {
-  if (E < 0 || N < 0 || K <= 0) return MOE_ERR_SHAPE;
-  if (K % 128 != 0) return MOE_ERR_ALIGN;
+extern "C" int moe_pack_mx_weights(const uint8_t* w, const uint8_t* w_scale, int E, int N, int K,
+                                   uint8_t* w_packed, uint8_t* w_scale_packed, void* stream) {
+  if (E < 0 || N < 0 || K <= 0 || E > 65535) return MOE_ERR_SHAPE;
+  if (K % 128 != 0 || N % 16 != 0) return MOE_ERR_ALIGN;
   if (E == 0 || N == 0) return MOE_OK;
-  if (!w_scale || !w_scale_packed) return MOE_ERR_NULL;
-  if (K / 128 > 65535 || E > 65535) return MOE_ERR_SHAPE;
-  dim3 grid((N + 255) / 256, K / 128, E);
-  hipLaunchKernelGGL(moe::pack_weight_scales_kernel, grid, dim3(256), 0, (hipStream_t)stream,
-                     w_scale, N, K, w_scale_packed);
+  if (!w || !w_scale || !w_packed || !w_scale_packed) return MOE_ERR_NULL;
+  const size_t chunks = (size_t)(N / 16) * (K / 128);
+  const size_t units = (size_t)(N / 16) * ((K / 128 + 7) / 8);
+  if ((chunks + 3) / 4 > 0x7fffffffu) return MOE_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(moe::pack_mx_codes_kernel, dim3((unsigned)((chunks + 3) / 4), (unsigned)E),
+                     dim3(256), 0, st, w, N, K, w_packed);
+  MOE_CHECK_LAUNCH();
+  hipLaunchKernelGGL(moe::pack_mx_scales_kernel, dim3((unsigned)((units + 3) / 4), (unsigned)E),
+                     dim3(256), 0, st, w_scale, N, K, w_scale_packed);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
 
 extern "C" int moe_grouped_gemm1(const uint8_t* xq, const int32_t* xs, const int32_t* expert_ends,
-                                 int E_local, int A, int M_cap, int H, int I, const uint8_t* w13,
-                                 const int32_t* w13_scale_packed, uint16_t* gateup, void* stream) {
-  if (I <= 0 || H <= 0) return MOE_ERR_SHAPE;
-  return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I, w13,
+                                 int E_local, int A, int M_cap, int H, int I,
+                                 const uint8_t* w13_packed, const uint8_t* w13_scale_packed,
+                                 uint16_t* gateup, void* stream) {
+  if (I <= 0 || I % 64 != 0) return MOE_ERR_ALIGN;
+  return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I, w13_packed,
                                   w13_scale_packed, gateup, stream);
 }
 
 extern "C" int moe_grouped_gemm2(const uint8_t* hq, const int32_t* hs, const int32_t* expert_ends,
-                                 int E_local, int A, int M_cap, int I, int H, const uint8_t* w2,
-                                 const int32_t* w2_scale_packed, uint16_t* down, void* stream) {
-  if (I <= 0 || H <= 0) return MOE_ERR_SHAPE;
-  return moe::launch_grouped_gemm(hq, hs, expert_ends, E_local, A, M_cap, I, H, w2,
+                                 int E_local, int A, int M_cap, int I, int H,
+                                 const uint8_t* w2_packed, const uint8_t* w2_scale_packed,
+                                 uint16_t* down, void* stream) {
+  return moe::launch_grouped_gemm(hq, hs, expert_ends, E_local, A, M_cap, I, H, w2_packed,
                                   w2_scale_packed, down, stream);
 }

@@ -142,32 +142,37 @@ def moe_scatter_endpoints(topk_ids, expert_start: int, E_local: int, A: int, x,
 
 # ------------------------------------------------------------------ GEMMs
 
-def moe_pack_weight_scales(w_scale, out=None):
-    """E8M0 weight scales u8 [E, N, K/32] -> packed MN-major int32 [E, K/128, N]
-    (load-time, once per weight)."""
-    _req(w_scale, "w_scale", (torch.uint8,))
-    E, N, G = w_scale.shape
-    K = 32 * G
-    if out is None:
-        out = torch.empty((E, K // 128, N), dtype=torch.int32, device=w_scale.device)
-    _req(out, "w_scale_packed", (torch.int32,), (E, K // 128, N))
-    st = lib().moe_pack_weight_scales(_ptr(w_scale), E, N, K, _ptr(out), _stream())
-    check(st, "moe_pack_weight_scales")
-    return out
+def packed_scale_shape(E: int, N: int, K: int):
+    return (E, N // 16, (K // 128 + 7) // 8, 512)
 
 
-def moe_grouped_gemm1(xq, xs, expert_ends, A: int, w13, w13_scale_packed, gateup):
+def moe_pack_mx_weights(w, w_scale):
+    """Load-time weight preparation: MXFP4 codes u8 [E, N, K/2] and E8M0
+    scales u8 [E, N, K/32] -> (codes in fragment order, same shape [E, N, K/2];
+    scales u8 [E, N/16, ceil(K/1024), 512]), the operands of the grouped GEMMs."""
+    _req(w, "w", (torch.uint8,))
+    E, N, K2 = w.shape
+    K = 2 * K2
+    _req(w_scale, "w_scale", (torch.uint8,), (E, N, K // 32))
+    wp = torch.empty_like(w)
+    sp = torch.empty(packed_scale_shape(E, N, K), dtype=torch.uint8, device=w.device)
+    st = lib().moe_pack_mx_weights(_ptr(w), _ptr(w_scale), E, N, K, _ptr(wp), _ptr(sp), _stream())
+    check(st, "moe_pack_mx_weights")
+    return wp, sp
+
+
+def moe_grouped_gemm1(xq, xs, expert_ends, A: int, w13_packed, w13_scale_packed, gateup):
     M_cap, H = xq.shape
-    E_local, twoI, _ = w13.shape
+    E_local, twoI, _ = w13_packed.shape
     I = twoI // 2
     _req(xq, "xq", (torch.uint8,))
     _req(xs, "xs", (torch.int32,), (H // 128, M_cap))
     _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
-    _req(w13, "w13", (torch.uint8,), (E_local, 2 * I, H // 2))
-    _req(w13_scale_packed, "w13_scale_packed", (torch.int32,), (E_local, H // 128, 2 * I))
+    _req(w13_packed, "w13_packed", (torch.uint8,), (E_local, 2 * I, H // 2))
+    _req(w13_scale_packed, "w13_scale_packed", (torch.uint8,), packed_scale_shape(E_local, 2 * I, H))
     _req(gateup, "gateup", _BF16, (M_cap, 2 * I))
     st = lib().moe_grouped_gemm1(_ptr(xq), _ptr(xs), _ptr(expert_ends), E_local, A, M_cap, H, I,
-                                 _ptr(w13), _ptr(w13_scale_packed), _ptr(gateup), _stream())
+                                 _ptr(w13_packed), _ptr(w13_scale_packed), _ptr(gateup), _stream())
     check(st, "moe_grouped_gemm1")
 
 
@@ -184,17 +189,17 @@ def moe_act_quant_liverows(gateup, expert_ends, A: int, clamp_limit: float, hq, 
     check(st, "moe_act_quant_liverows")
 
 
-def moe_grouped_gemm2(hq, hs, expert_ends, A: int, w2, w2_scale_packed, down):
+def moe_grouped_gemm2(hq, hs, expert_ends, A: int, w2_packed, w2_scale_packed, down):
     M_cap, I = hq.shape
-    E_local, H, _ = w2.shape
+    E_local, H, _ = w2_packed.shape
     _req(hq, "hq", (torch.uint8,))
     _req(hs, "hs", (torch.int32,), (I // 128, M_cap))
     _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
-    _req(w2, "w2", (torch.uint8,), (E_local, H, I // 2))
-    _req(w2_scale_packed, "w2_scale_packed", (torch.int32,), (E_local, I // 128, H))
+    _req(w2_packed, "w2_packed", (torch.uint8,), (E_local, H, I // 2))
+    _req(w2_scale_packed, "w2_scale_packed", (torch.uint8,), packed_scale_shape(E_local, H, I))
     _req(down, "down", _BF16, (M_cap, H))
     st = lib().moe_grouped_gemm2(_ptr(hq), _ptr(hs), _ptr(expert_ends), E_local, A, M_cap, I, H,
-                                 _ptr(w2), _ptr(w2_scale_packed), _ptr(down), _stream())
+                                 _ptr(w2_packed), _ptr(w2_scale_packed), _ptr(down), _stream())
     check(st, "moe_grouped_gemm2")
 
 
@@ -244,18 +249,19 @@ def moe_sparse_gemv(act, act_per_slot: bool, topk_ids, expert_start: int, E_loca
 
 # ------------------------------------------------------------------ chains
 
-def moe_ffn_prefill(x, topk_ids, topk_weights, expert_start: int, A: int, w13,
-                    w13_scale_packed, w2, w2_scale_packed, buf: GroupedBuffers,
+def moe_ffn_prefill(x, topk_ids, topk_weights, expert_start: int, A: int, w13_packed,
+                    w13_scale_packed, w2_packed, w2_scale_packed, buf: GroupedBuffers,
                     clamp_limit: float = 0.0, routed_scale: float = 1.0):
     """scatter -> GEMM1 -> live-row act-quant -> GEMM2 -> combine, all on the
-    current stream, no host synchronisation. Weight scales are the packed
-    words of moe_pack_weight_scales."""
-    E_local = w13.shape[0]
+    current stream, no host synchronisation. Weights are the outputs of
+    moe_pack_mx_weights."""
+    E_local = w13_packed.shape[0]
     moe_scatter_endpoints(topk_ids, expert_start, E_local, A, x, buf.expert_ends, buf.route_row,
                           buf.xq, buf.xs, buf.workspace)
-    moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, A, w13, w13_scale_packed, buf.gateup)
+    moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, A, w13_packed, w13_scale_packed,
+                      buf.gateup)
     moe_act_quant_liverows(buf.gateup, buf.expert_ends, A, clamp_limit, buf.hq, buf.hs)
-    moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, A, w2, w2_scale_packed, buf.down)
+    moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, A, w2_packed, w2_scale_packed, buf.down)
     moe_combine(buf.down, buf.route_row, topk_weights, routed_scale, buf.out)
     return buf.out
 

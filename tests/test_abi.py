@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     for s in range(0, -8, -1):
         assert lib.moe_status_string(s).decode()
     assert lib.moe_status_string(5).decode() == "unknown status"
@@ -83,10 +83,11 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
                                  NULL) == -3
     assert lib.moe_grouped_gemm2(NULL, NULL, NULL, 8, 128, 1152, 100, 256, NULL, NULL, NULL,
                                  NULL) == -3
-    # weight-scale packing: K not a multiple of 128; empty is a no-op
-    assert lib.moe_pack_weight_scales(NULL, 4, 256, 96, NULL, NULL) == -3
-    assert lib.moe_pack_weight_scales(NULL, 0, 256, 128, NULL, NULL) == 0
-    assert lib.moe_pack_weight_scales(NULL, 4, 256, 128, NULL, NULL) == -1
+    # weight packing: K not a multiple of 128, N not of 16; empty is a no-op
+    assert lib.moe_pack_mx_weights(NULL, NULL, 4, 256, 96, NULL, NULL, NULL) == -3
+    assert lib.moe_pack_mx_weights(NULL, NULL, 4, 200, 128, NULL, NULL, NULL) == -3
+    assert lib.moe_pack_mx_weights(NULL, NULL, 0, 256, 128, NULL, NULL, NULL) == 0
+    assert lib.moe_pack_mx_weights(NULL, NULL, 4, 256, 128, NULL, NULL, NULL) == -1
     # combine: H not a multiple of 8
     assert lib.moe_combine(NULL, 0, NULL, NULL, 4, 2, 12, ctypes.c_float(1.0), NULL, NULL) == -3
     # sparse GEMV: too many slots, unsupported format

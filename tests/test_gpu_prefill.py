@@ -214,8 +214,9 @@ def _tiny_state(ops, c, clamp=0.0):
     ids, wts = M.route_softmax(c.logits, c.k)
     buf = ops.alloc_grouped(c.T, c.k, c.E, c.M_cap, c.H, c.I, fill=True)
     w = c.weights
-    dw = dict(w13=dev(w.w13), s13=ops.moe_pack_weight_scales(dev(w.s13)), w2=dev(w.w2),
-              s2=ops.moe_pack_weight_scales(dev(w.s2)))
+    w13p, s13p = ops.moe_pack_mx_weights(dev(w.w13), dev(w.s13))
+    w2p, s2p = ops.moe_pack_mx_weights(dev(w.w2), dev(w.s2))
+    dw = dict(w13=w13p, s13=s13p, w2=w2p, s2=s2p)
     ops.moe_scatter_endpoints(dev(ids), 0, c.E, c.A, dev_bf16(c.x), buf.expert_ends, buf.route_row,
                               buf.xq, buf.xs, buf.workspace)
     return ids, wts, buf, dw
@@ -287,9 +288,9 @@ def test_prefill_chain_tiny_end_to_end_and_deterministic(ops):
     outs = []
     for _ in range(2):
         buf = ops.alloc_grouped(c.T, c.k, c.E, c.M_cap, c.H, c.I, fill=True)
-        y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A, dev(w.w13),
-                                ops.moe_pack_weight_scales(dev(w.s13)), dev(w.w2),
-                                ops.moe_pack_weight_scales(dev(w.s2)), buf)
+        y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A,
+                                *ops.moe_pack_mx_weights(dev(w.w13), dev(w.s13)),
+                                *ops.moe_pack_mx_weights(dev(w.w2), dev(w.s2)), buf)
         outs.append(host(y))
     assert np.array_equal(outs[0], outs[1])
     ok, mx, mean = end_to_end_ok(outs[0], ref.out)
@@ -310,9 +311,9 @@ def test_prefill_chain_window_clamp_scale(ops):
     ref = M.prefill_expert_major(c.x, ids, wts, es, E_local, A, c.I, w.w13[sl], w.s13[sl],
                                  w.w2[sl], w.s2[sl], clamp=6.0, routed_scale=0.5)
     buf = ops.alloc_grouped(c.T, c.k, E_local, M_cap, c.H, c.I, fill=True)
-    y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), es, A, dev(w.w13[sl]),
-                            ops.moe_pack_weight_scales(dev(w.s13[sl])), dev(w.w2[sl]),
-                            ops.moe_pack_weight_scales(dev(w.s2[sl])), buf, clamp_limit=6.0,
+    y = ops.moe_ffn_prefill(dev_bf16(c.x), dev(ids), dev(wts), es, A,
+                            *ops.moe_pack_mx_weights(dev(w.w13[sl]), dev(w.s13[sl])),
+                            *ops.moe_pack_mx_weights(dev(w.w2[sl]), dev(w.s2[sl])), buf, clamp_limit=6.0,
                             routed_scale=0.5)
     ok, mx, mean = end_to_end_ok(host(y), ref.out)
     assert ok, (mx, mean)
@@ -322,18 +323,36 @@ def test_prefill_chain_window_clamp_scale(ops):
 
 # ------------------------------------------------- weight prep + full size
 
-def test_pack_weight_scales_bitexact(ops):
-    """Load-time relayout: byte j of word (e, c, n) is group 4c+j of row n."""
+def _expected_packing(w, s):
+    """The documented packed layouts, built by plain indexing."""
+    E, N, K2 = w.shape
+    K = 2 * K2
+    KS, KS8 = K // 128, (K // 128 + 7) // 8
+    lane = np.arange(64)
+    wp = np.empty((E, N // 16, KS, 64, 16), np.uint8)
+    sp = np.zeros((E, N // 16, KS8, 64, 8), np.uint8)
+    for cb in range(N // 16):
+        rows = 16 * cb + lane % 16
+        for ks in range(KS):
+            cols = 64 * ks + 16 * (lane // 16)
+            wp[:, cb, ks] = w[:, rows[:, None], cols[:, None] + np.arange(16)[None, :]]
+            q, j = divmod(ks, 8)
+            sp[:, cb, q, :, j] = s[:, rows, 4 * ks + lane // 16]
+    return wp.reshape(E, N, K2), sp.reshape(E, N // 16, KS8, 512)
+
+
+def test_pack_mx_weights_bitexact(ops):
+    """Load-time weight preparation is pure data movement into the documented
+    fragment order (codes) and 8-step lane words (scales, zero-padded)."""
     rng = np.random.default_rng(2024)
-    for E, N, K in ((3, 300, 512), (1, 128, 128), (2, 4096, 4096)):
-        say(f"pack weight scales E={E} N={N} K={K}")
+    for E, N, K in ((3, 48, 384), (1, 128, 128), (2, 256, 2048), (1, 64, 1152)):
+        say(f"pack mx weights E={E} N={N} K={K}")
+        w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
         s = rng.integers(0, 256, size=(E, N, K // 32), dtype=np.uint8)
-        got = host(ops.moe_pack_weight_scales(dev(s)))
-        want = np.empty((E, K // 128, N), np.int64)
-        for c in range(K // 128):
-            b = s[:, :, 4 * c: 4 * c + 4].astype(np.int64)
-            want[:, c, :] = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
-        assert np.array_equal(got.view(np.uint32).astype(np.int64), want)
+        wp, sp = ops.moe_pack_mx_weights(dev(w), dev(s))
+        ew, es = _expected_packing(w, s)
+        assert np.array_equal(host(wp), ew)
+        assert np.array_equal(host(sp), es)
 
 
 def test_prefill_group_full_size_gemms_sampled(ops):
@@ -348,11 +367,11 @@ def test_prefill_group_full_size_gemms_sampled(ops):
     ops.moe_scatter_endpoints(dev(ids), 0, c.E_local, c.A, dev_bf16(c.x), buf.expert_ends,
                               buf.route_row, buf.xq, buf.xs, buf.workspace)
     say("full-size prefill GEMMs: gemm1 / act-quant / gemm2")
-    s13 = ops.moe_pack_weight_scales(dev(w.s13))
-    s2 = ops.moe_pack_weight_scales(dev(w.s2))
-    ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, dev(w.w13), s13, buf.gateup)
+    w13p, s13p = ops.moe_pack_mx_weights(dev(w.w13), dev(w.s13))
+    w2p, s2p = ops.moe_pack_mx_weights(dev(w.w2), dev(w.s2))
+    ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, w13p, s13p, buf.gateup)
     ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, 0.0, buf.hq, buf.hs)
-    ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, dev(w.w2), s2, buf.down)
+    ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, w2p, s2p, buf.down)
     ends = host(buf.expert_ends)
     segs = _expert_rows(ends, c.A)
     counts = np.array([r.size for r in segs])
