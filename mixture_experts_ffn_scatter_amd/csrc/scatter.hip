@@ -8,39 +8,84 @@
 // t*k+s, so the permutation is unique.
 //
 // Three launches, none of which depends on a host-visible count:
-//   1. count  - one block per 256-token block: LDS histogram of its local
-//               routes, written to workspace[w][e].
+//   1. rank   - one block per 64-token block: walks the block's routes in
+//               flattened order, 256 at a time; inside a wave, routes with
+//               the same expert are found with ballots (one round per
+//               distinct expert) and ranked by lane order; per-wave counts
+//               in LDS give the order across waves, and a running count per
+//               expert carries it across rounds. Writes each local route's
+//               rank inside the token block and the block's expert counts.
 //   2. scan   - one block: per-expert totals, the aligned exclusive scan
 //               over experts (the endpoint recurrence), expert_ends, and the
 //               per-token-block row offsets (in place over the counts).
-//   3. rows   - one block per token: the rank of each of its routes among
-//               earlier routes of the same expert in its token block, the
-//               route row, and the quantised copy of x[t] into every
-//               destination row (codes coalesced 8 bytes per lane, packed
-//               scales assembled across 16 lanes and stored MN-major).
+//   3. rows   - one block per token: route row = block offset + rank, and
+//               the quantised copy of x[t] into every destination row (codes
+//               coalesced 8 bytes per lane, packed scales assembled across
+//               16 lanes and stored MN-major).
 #include "common.h"
 
 namespace moe {
 
-constexpr int kTokBlock = 256;     // tokens per histogram block
+constexpr int kTokBlock = 64;      // tokens per rank block
 constexpr int kScatterMaxE = 1024;
 constexpr int kScatterMaxK = 32;
 
-__global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t* __restrict__ ids, int T,
-                                                            int k, int expert_start, int E_local,
-                                                            int32_t* __restrict__ counts) {
-  __shared__ int hist[kScatterMaxE];
+__global__ __launch_bounds__(256) void scatter_rank_kernel(const int32_t* __restrict__ ids, int T,
+                                                           int k, int expert_start, int E_local,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ route_rank) {
+  __shared__ int base[kScatterMaxE];        // routes of each expert in earlier rounds
+  __shared__ int wcnt[4][kScatterMaxE];     // this round's routes per wave and expert
   const int w = blockIdx.x;
-  for (int e = threadIdx.x; e < E_local; e += blockDim.x) hist[e] = 0;
-  __syncthreads();
-  const int r0 = w * kTokBlock * k;
-  const int r1 = min(T, (w + 1) * kTokBlock) * k;
-  for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
-    const int e = ids[r] - expert_start;
-    if (e >= 0 && e < E_local) atomicAdd(&hist[e], 1);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  for (int e = tid; e < E_local; e += 256) {
+    base[e] = 0;
+    wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E_local; e += blockDim.x) counts[(size_t)w * E_local + e] = hist[e];
+  const int rb = w * kTokBlock * k;
+  const int re = min(T, (w + 1) * kTokBlock) * k;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r0 = rb; r0 < re; r0 += 256) {             // block-uniform rounds
+    const int r = r0 + tid;
+    int e = -1;
+    if (r < re) {
+      const int v = ids[r] - expert_start;
+      e = (v >= 0 && v < E_local) ? v : -1;
+    }
+    // in-wave rank: one ballot round per distinct expert present
+    uint64_t todo = __ballot(e >= 0);
+    int inwave = 0, lead = -1;
+    while (todo) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const int key = __shfl(e, leader, 64);
+      const uint64_t m = __ballot(e == key);
+      if (e == key) inwave = __popcll(m & below);
+      if (lane == leader) {
+        wcnt[wid][key] = __popcll(m);
+        lead = key;
+      }
+      todo &= ~m;
+    }
+    __syncthreads();
+    if (r < re) {
+      int rank = -1;
+      if (e >= 0) {
+        rank = base[e] + inwave;
+        for (int v = 0; v < wid; ++v) rank += wcnt[v][e];
+      }
+      route_rank[r] = rank;
+    }
+    __syncthreads();
+    if (lead >= 0) {
+      atomicAdd(&base[lead], wcnt[wid][lead]);
+      wcnt[wid][lead] = 0;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < E_local; e += 256) counts[(size_t)w * E_local + e] = base[e];
 }
 
 // Block-wide exclusive scan of one int per thread (1024 threads).
@@ -69,20 +114,46 @@ __device__ int block_exclusive_scan_1024(int v, int* wave_tot) {
   return wave_tot[16 + wid] + incl - v;
 }
 
+constexpr int kScanLds = 8192;    // counts staged in LDS when W * E_local fits
+
 __global__ __launch_bounds__(1024) void scatter_scan_kernel(int W, int E_local, int A,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ expert_ends) {
   __shared__ int wave_tot[32];
+  __shared__ int s_cnt[kScanLds];
   const int e = threadIdx.x;
+  const int n = W * E_local;
+  const bool staged = n <= kScanLds;          // block-uniform
+  if (staged) {
+    for (int i = threadIdx.x; i < n; i += 1024) s_cnt[i] = counts[i];
+    __syncthreads();
+  }
   int total = 0;
   if (e < E_local) {
+    if (staged) {
 #pragma unroll 8
-    for (int w = 0; w < W; ++w) total += counts[(size_t)w * E_local + e];
+      for (int w = 0; w < W; ++w) total += s_cnt[w * E_local + e];
+    } else {
+#pragma unroll 8
+      for (int w = 0; w < W; ++w) total += counts[(size_t)w * E_local + e];
+    }
   }
   const int aligned = e < E_local ? align_up_dev(total, A) : 0;
   const int start = block_exclusive_scan_1024(aligned, wave_tot);
-  if (e < E_local) {
-    expert_ends[e] = start + total;
+  if (e < E_local) expert_ends[e] = start + total;
+  // counts -> per-block row offsets (exclusive over token blocks, plus start_e)
+  if (staged) {
+    if (e < E_local) {
+      int run = start;
+      for (int w = 0; w < W; ++w) {
+        const int c = s_cnt[w * E_local + e];
+        s_cnt[w * E_local + e] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 1024) counts[i] = s_cnt[i];
+  } else if (e < E_local) {
     int run = start;
     for (int w = 0; w < W; ++w) {
       int32_t* p = counts + (size_t)w * E_local + e;
@@ -93,51 +164,33 @@ __global__ __launch_bounds__(1024) void scatter_scan_kernel(int W, int E_local, 
   }
 }
 
-__global__ __launch_bounds__(256) void scatter_rows_kernel(
+// One block per token. Lanes < k turn their route's rank into its row; the
+// block then quantises x[t]: each thread owns 8 consecutive columns per
+// 2048-column chunk, a 32-column group spans 4 lanes and a packed scale word
+// (128 columns) 16 lanes; codes go to every destination row (8 bytes per
+// lane, coalesced) and scale words MN-major.
+constexpr int kRowsThreads = 256;
+
+__global__ __launch_bounds__(kRowsThreads) void scatter_rows_kernel(
     const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int M_cap,
     const uint16_t* __restrict__ x, int H, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ route_row, uint8_t* __restrict__ xq, int32_t* __restrict__ xs) {
-  __shared__ int s_e[kScatterMaxK];
-  __shared__ int s_cnt[kScatterMaxK];
   __shared__ int s_row[kScatterMaxK];
   __shared__ int s_any;
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int w = t / kTokBlock;
-  if (tid < k) {
-    const int e = ids[(size_t)t * k + tid] - expert_start;
-    s_e[tid] = (e >= 0 && e < E_local) ? e : -1;
-    s_cnt[tid] = 0;
-  }
   if (tid == 0) s_any = 0;
   __syncthreads();
-  // rank of route (t, s) among earlier routes of the same expert in the
-  // token block: count matches over [block start, t*k + s)
-  // counted in registers per slot, then reduced per wave: one LDS atomic
-  // per wave and slot instead of one per matching route
-  const int rb = w * kTokBlock * k;
-  const int rt = t * k;
-  int cnt[kScatterMaxK];
-#pragma unroll
-  for (int s = 0; s < kScatterMaxK; ++s) cnt[s] = 0;
-  for (int r = rb + tid; r < rt + k; r += blockDim.x) {
-    const int e = ids[r] - expert_start;
-#pragma unroll
-    for (int s = 0; s < kScatterMaxK; ++s)
-      if (s < k) cnt[s] += (r < rt + s && e == s_e[s] && e >= 0) ? 1 : 0;
-  }
-#pragma unroll
-  for (int s = 0; s < kScatterMaxK; ++s) {
-    if (s >= k) break;  // block-uniform
-    int c = cnt[s];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
-    if ((tid & 63) == 0 && c) atomicAdd(&s_cnt[s], c);
-  }
-  __syncthreads();
   if (tid < k) {
-    const int e = s_e[tid];
-    const int row = e >= 0 ? offsets[(size_t)w * E_local + e] + s_cnt[tid] : -1;
+    // route_row holds the rank from the rank pass (or -1); turn it into the row
+    const int rank = route_row[(size_t)t * k + tid];
+    int row = -1;
+    if (rank >= 0) {
+      const int e = ids[(size_t)t * k + tid] - expert_start;
+      row = offsets[(size_t)w * E_local + e] + rank;
+      if (row >= M_cap) row = -1;           // corrupt metadata: never write past the buffer
+    }
     s_row[tid] = row;
     route_row[(size_t)t * k + tid] = row;
     if (row >= 0) atomicOr(&s_any, 1);
@@ -145,13 +198,11 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
   __syncthreads();
   if (!s_any) return;  // block-uniform: no local route for this token
 
-  // quantised copy: each lane owns 8 consecutive columns per 2048-wide chunk;
-  // a 32-column group spans 4 lanes, a packed word (128 columns) 16 lanes
   const uint16_t* xr = x + (size_t)t * H;
-  const int nchunks = (H + 2047) / 2048;
+  const int nchunks = (H + 8 * kRowsThreads - 1) / (8 * kRowsThreads);
   for (int i = 0; i < nchunks; ++i) {
-    const int base = tid * 8 + i * 2048;
-    const bool act = base < H;
+    const int base = tid * 8 + i * 8 * kRowsThreads;
+    const bool act = base < H;              // whole 16-lane groups (H % 128 == 0)
     uint4 raw = make_uint4(0, 0, 0, 0);
     if (act) raw = *reinterpret_cast<const uint4*>(xr + base);
     float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
@@ -175,7 +226,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(
       const int c = base >> 7;
       for (int s = 0; s < k; ++s) {
         const int row = s_row[s];
-        if (row < 0 || row >= M_cap) continue;
+        if (row < 0) continue;
         *reinterpret_cast<uint2*>(xq + (size_t)row * H + base) = make_uint2(lo, hi);
         if ((tid & 15) == 0) xs[(size_t)c * M_cap + row] = (int32_t)word;
       }
@@ -230,14 +281,14 @@ extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int 
   hipStream_t st = (hipStream_t)stream;
   const int W = (T + kTokBlock - 1) / kTokBlock;
   int32_t* counts = (int32_t*)workspace;
-  hipLaunchKernelGGL(scatter_count_kernel, dim3(W), dim3(256), 0, st, topk_ids, T, k, expert_start,
-                     E_local, counts);
+  hipLaunchKernelGGL(scatter_rank_kernel, dim3(W), dim3(256), 0, st, topk_ids, T, k, expert_start,
+                     E_local, counts, route_row);
   MOE_CHECK_LAUNCH();
   hipLaunchKernelGGL(scatter_scan_kernel, dim3(1), dim3(1024), 0, st, W, E_local, A, counts,
                      expert_ends);
   MOE_CHECK_LAUNCH();
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3(T), dim3(256), 0, st, topk_ids, T, k, expert_start,
-                     E_local, M_cap, x, H, counts, route_row, xq, xs);
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3(T), dim3(kRowsThreads), 0, st, topk_ids, T, k,
+                     expert_start, E_local, M_cap, x, H, counts, route_row, xq, xs);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -51,7 +51,7 @@ def test_abi_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.moe_scatter_workspace_bytes(4096, 6, 32) == 16 * 32 * 4   # 256-token blocks
+    assert lib.moe_scatter_workspace_bytes(4096, 6, 32) == 64 * 32 * 4   # 64-token blocks
     assert lib.moe_scatter_workspace_bytes(0, 6, 32) == 0
 
 
