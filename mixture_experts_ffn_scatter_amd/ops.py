@@ -296,3 +296,23 @@ def moe_ffn_decode(x, topk_ids, topk_weights, expert_start: int, E_local: int, w
                     buf.down, None, glu=False)
     moe_combine(buf.down, buf.slot_row, topk_weights, 1.0, buf.out)
     return buf.out
+
+
+# ------------------------------------------------------------ graph capture
+
+def capture_graph(launch) -> "torch.cuda.CUDAGraph":
+    """Capture ``launch()`` (a sequence of the calls above on fixed buffers)
+    into a HIP graph. Every entry point sizes its grid from host-known
+    arguments and never reads device data back, so the captured chain stays
+    valid when the routing, and with it every count and endpoint, changes
+    between replays; the caller rewrites the input buffers in place and
+    calls ``replay()``. One eager run on a side stream precedes the capture."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch()
+    return graph
