@@ -7,18 +7,16 @@
 // (sglang)", section 2.4: activation and quantisation are fused so gate/up
 // is read once and FP8 + packed scales are written once; SiLU stays fp32.
 //
-// Work decomposition: one persistent block of 8 waves per CU walks units of
-// [0, end of the last expert). A unit is up to 32 (row, 512-column chunk)
-// items (rows per unit = 32 / chunks per row, at most 16); a row is
-// processed only if it lies inside some [start_e, end_e). A lane owns 8
-// consecutive columns of a chunk (16-byte loads of gate and up, 8-byte
-// stores of codes), a 32-column group spans 4 lanes (amax by two shuffles),
-// a packed scale word spans 16 lanes. The unit's scale words are staged in
-// LDS and stored MN-major as one contiguous run per scale row. The next
-// unit's loads are issued before the current unit is computed (registers
-// double-buffered); loads go through a buffer resource that ends at the
-// unit's last row, and items that are dead or past the row read nothing, so
-// every wave issues the same load stream and padding is never read.
+// Work decomposition: the live rows are numbered 0..R-1 in layout order
+// (expert by expert, from the endpoints) and split evenly over one block of
+// 8 waves per CU, so padding rows are never visited. A block's rows are cut
+// into (row, 512-column chunk) items, taken 64 at a time (8 per wave); the
+// next batch's loads are issued before the current batch is computed
+// (registers double-buffered), and the sigmoid table's loads go out before
+// any of them. A lane owns 8 consecutive columns of a chunk (16-byte loads
+// of gate and up, 8-byte stores of codes), a 32-column group spans 4 lanes
+// (amax by two shuffles), a packed scale word spans 16 lanes and is stored
+// by its first lane (MN-major).
 //
 // Arithmetic per element, all IEEE fp32 with no contraction:
 //   g = bf16 gate, u = bf16 up; optional clamp g = min(g, L), u = med3(u, -L, L)
@@ -38,9 +36,7 @@ namespace moe {
 
 constexpr int kActThreads = 512;   // 8 waves
 constexpr int kActWaves = kActThreads / 64;
-constexpr int kActItems = 32;      // (row, 512-column chunk) items per unit
-constexpr int kActBatch = kActItems / kActWaves;
-constexpr int kActMaxRows = 16;
+constexpr int kActBatch = 8;       // items per wave per batch
 constexpr int kActMaxE = 1024;
 constexpr int kActMaxWordsPerRow = 64;  // I <= 8192
 constexpr uint32_t kActOob = 0x80000000u;
@@ -54,15 +50,21 @@ __device__ __forceinline__ float sigmoid_lookup(const float* tab, float g) {
   return tab[idx];
 }
 
-// largest e with start_e <= r (starts are non-decreasing; an expert sharing
-// its start with a later one is empty)
-__device__ __forceinline__ int expert_of_row(const int* s_start, int E, int r) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_start[mid] <= r) lo = mid; else hi = mid - 1;
+__device__ int act_block_scan(int v, int* tmp) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
   }
-  return lo;
+  if (lane == 63) tmp[wid] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wid; ++w) off += tmp[w];
+  __syncthreads();
+  return off + incl - v;
 }
 
 template <bool CLAMP>
@@ -70,10 +72,10 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     const uint16_t* __restrict__ gateup, const int32_t* __restrict__ expert_ends, int E_local,
     int A, int M_cap, int I, float L, uint8_t* __restrict__ hq, int32_t* __restrict__ hs) {
   __shared__ __attribute__((aligned(16))) float s_tab[MOE_SIGMOID_TABLE_SIZE];
-  __shared__ int s_start[kActMaxE];
-  __shared__ int s_end[kActMaxE];
-  __shared__ uint32_t s_words[2][kActMaxWordsPerRow * kActMaxRows];
-  __shared__ int s_live[2][kActMaxRows];
+  __shared__ int s_start[kActMaxE];   // first row of expert e
+  __shared__ int s_pref[kActMaxE];    // live rows of the experts before e
+  __shared__ int s_tmp[kActWaves];
+  __shared__ int s_total;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -88,69 +90,83 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     const int i = tid + j * kActThreads;
     tv[j] = i < kVec ? reinterpret_cast<const v4i*>(g_sigmoid_table)[i] : v4i{0, 0, 0, 0};
   }
-  for (int e = tid; e < E_local; e += kActThreads) {
-    int s, en;
-    expert_range(expert_ends, e, A, M_cap, s, en);
-    s_start[e] = s;
-    s_end[e] = en;
+  // expert ranges and the exclusive scan of their live-row counts (2 per thread)
+  int cnt[2], st[2];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = 2 * tid + j;
+    cnt[j] = 0;
+    st[j] = 0;
+    if (e < E_local) {
+      int s, en;
+      expert_range(expert_ends, e, A, M_cap, s, en);
+      st[j] = s;
+      cnt[j] = en - s;
+    }
+    sum += cnt[j];
   }
+  int run = act_block_scan(sum, s_tmp);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = 2 * tid + j;
+    if (e < E_local) {
+      s_start[e] = st[j];
+      s_pref[e] = run;
+    }
+    run += cnt[j];
+  }
+  if (tid == kActThreads - 1) s_total = run;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = tid + j * kActThreads;
     if (i < kVec) reinterpret_cast<v4i*>(s_tab)[i] = tv[j];
   }
   __syncthreads();
-  // ends are monotone in a valid layout; the running max keeps the walk
-  // bounded by the farthest end even for inconsistent metadata
-  int last = 0;
-  for (int e = 0; e < E_local; ++e) last = max(last, s_end[e]);
-  const int words = I >> 7;
-  const int nchunks = (I + 511) >> 9;
-  const int R = min(kActMaxRows, max(1, kActItems / nchunks));   // rows per unit
-  const int items = R * nchunks;
-  const int n_units = (last + R - 1) / R;
 
-  auto live_of = [&](int unit, int buf) {
-    if (tid < R) {
-      const int r = unit * R + tid;
-      bool live = false;
-      if (r < last) {
-        const int e = expert_of_row(s_start, E_local, r);
-        live = r >= s_start[e] && r < s_end[e];
+  const int R = s_total;
+  const int i0 = (int)(((long long)R * blockIdx.x) / gridDim.x);
+  const int i1 = (int)(((long long)R * (blockIdx.x + 1)) / gridDim.x);
+  const int nchunks = (I + 511) >> 9;
+  const int items = (i1 - i0) * nchunks;
+  const int nbatch = (items + kActWaves * kActBatch - 1) / (kActWaves * kActBatch);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(gateup), (short)0, (int)((uint32_t)M_cap * (uint32_t)(4 * I)), 0x00020000);
+
+  // row of live row number i (wave-uniform): the expert holding it, then its offset
+  auto row_of = [&](int i) {
+    int lo = 0, hi = E_local - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return s_start[lo] + (i - s_pref[lo]);
+  };
+  // item it of this block: live row i0 + it / nchunks, chunk it % nchunks
+  auto load_batch = [&](int b, v4i* G, v4i* U) {
+#pragma unroll
+    for (int j = 0; j < kActBatch; ++j) {
+      const int it = (b * kActBatch + j) * kActWaves + wid;
+      uint32_t off = kActOob;
+      if (it < items) {
+        const int i = i0 + it / nchunks;
+        const int col = (it % nchunks) * 512 + lane * 8;
+        if (col < I) off = (uint32_t)row_of(i) * (uint32_t)(4 * I) + (uint32_t)col * 2u;
       }
-      s_live[buf][tid] = live ? 1 : 0;
+      G[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      U[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off == kActOob ? kActOob : off + (uint32_t)I * 2u, 0, 0);
     }
   };
-  // gate/up of this wave's items of a unit; dead items read nothing
-  auto load_unit = [&](int unit, int buf, v4i* G, v4i* U) {
-    const int r0 = unit * R;
-    const int nrows = min(R, last - r0);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(gateup + (size_t)r0 * (2 * I)), (short)0,
-        (int)((uint32_t)max(nrows, 0) * (uint32_t)(4 * I)), 0x00020000);
+  auto compute_batch = [&](int b, const v4i* G, const v4i* U) {
 #pragma unroll
-    for (int b = 0; b < kActBatch; ++b) {
-      const int it = wid + b * kActWaves;
-      const int rl = it / nchunks;
-      const int col = (it - rl * nchunks) * 512 + lane * 8;
-      const bool ok = it < items && col < I && s_live[buf][rl < R ? rl : 0];
-      const uint32_t off = (uint32_t)rl * (uint32_t)(4 * I) + (uint32_t)col * 2u;
-      G[b] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off : kActOob, 0, 0);
-      U[b] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off + (uint32_t)I * 2u : kActOob, 0, 0);
-    }
-  };
-  auto compute_unit = [&](int unit, int buf, const v4i* G, const v4i* U) {
-    const int r0 = unit * R;
-#pragma unroll
-    for (int b = 0; b < kActBatch; ++b) {
-      const int it = wid + b * kActWaves;
+    for (int j = 0; j < kActBatch; ++j) {
+      const int it = (b * kActBatch + j) * kActWaves + wid;
       if (it >= items) break;  // wave-uniform
-      const int rl = it / nchunks;
-      if (!s_live[buf][rl]) continue;  // wave-uniform
-      const int col = (it - rl * nchunks) * 512 + lane * 8;
+      const int row = row_of(i0 + it / nchunks);
+      const int col = (it % nchunks) * 512 + lane * 8;
       const bool act = col < I;
-      const uint32_t gw[4] = {(uint32_t)G[b].x, (uint32_t)G[b].y, (uint32_t)G[b].z, (uint32_t)G[b].w};
-      const uint32_t uw[4] = {(uint32_t)U[b].x, (uint32_t)U[b].y, (uint32_t)U[b].z, (uint32_t)U[b].w};
+      const uint32_t gw[4] = {(uint32_t)G[j].x, (uint32_t)G[j].y, (uint32_t)G[j].z, (uint32_t)G[j].w};
+      const uint32_t uw[4] = {(uint32_t)U[j].x, (uint32_t)U[j].y, (uint32_t)U[j].z, (uint32_t)U[j].w};
       float h[8];
       float amax = 0.f;
 #pragma unroll
@@ -179,41 +195,20 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
       word |= __shfl_xor(word, 4, 64);
       word |= __shfl_xor(word, 8, 64);
       if (act) {
-        *reinterpret_cast<uint2*>(hq + (size_t)(r0 + rl) * I + col) = make_uint2(lo, hi);
-        if ((lane & 15) == 0) s_words[buf][(col >> 7) * kActMaxRows + rl] = word;
+        *reinterpret_cast<uint2*>(hq + (size_t)row * I + col) = make_uint2(lo, hi);
+        if ((lane & 15) == 0) hs[(size_t)(col >> 7) * M_cap + row] = (int32_t)word;
       }
     }
   };
-  auto store_words = [&](int unit, int buf) {
-    const int r0 = unit * R;
-    for (int i = tid; i < words * R; i += kActThreads) {
-      const int c = i / R;
-      const int rl = i - c * R;
-      if (s_live[buf][rl]) hs[(size_t)c * M_cap + r0 + rl] = (int32_t)s_words[buf][c * kActMaxRows + rl];
-    }
-  };
-  // one unit: prefetch the next one, compute this one, store its words
-  auto step = [&](int unit, int buf, const v4i* Gc, const v4i* Uc, v4i* Gn, v4i* Un) {
-    const int un = unit + gridDim.x;
-    __syncthreads();   // the previous unit's word stores are done with the other buffer
-    if (un < n_units) live_of(un, buf ^ 1);
-    __syncthreads();
-    if (un < n_units) load_unit(un, buf ^ 1, Gn, Un);
-    compute_unit(unit, buf, Gc, Uc);
-    __syncthreads();
-    store_words(unit, buf);
-    return un;
-  };
 
   v4i GA[kActBatch], UA[kActBatch], GB[kActBatch], UB[kActBatch];
-  int unit = blockIdx.x;
-  if (unit < n_units) live_of(unit, 0);
-  __syncthreads();
-  if (unit < n_units) load_unit(unit, 0, GA, UA);
-  while (unit < n_units) {
-    unit = step(unit, 0, GA, UA, GB, UB);
-    if (unit >= n_units) break;
-    unit = step(unit, 1, GB, UB, GA, UA);
+  if (nbatch > 0) load_batch(0, GA, UA);
+  for (int b = 0; b < nbatch; b += 2) {
+    if (b + 1 < nbatch) load_batch(b + 1, GB, UB);
+    compute_batch(b, GA, UA);
+    if (b + 1 >= nbatch) break;
+    if (b + 2 < nbatch) load_batch(b + 2, GA, UA);
+    compute_batch(b + 1, GB, UB);
   }
 }
 
@@ -226,6 +221,8 @@ extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* exp
   if (E_local < 0 || E_local > kActMaxE || A < 1 || M_cap < 0 || I <= 0) return MOE_ERR_SHAPE;
   if (I % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
   if (I / 128 > kActMaxWordsPerRow) return MOE_ERR_SHAPE;
+  // one buffer range covers gate/up: M_cap rows of 4*I bytes below 2 GiB
+  if ((long long)M_cap * I * 4 >= (1LL << 31)) return MOE_ERR_SHAPE;
   bool clamp = false;
   if (clamp_limit > 0.f && clamp_limit < __builtin_inff()) {
     uint32_t bits;
@@ -238,10 +235,8 @@ extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* exp
   if (E_local == 0 || M_cap == 0) return MOE_OK;
   if (!gateup || !expert_ends || !hq || !hs) return MOE_ERR_NULL;
   hipStream_t st = (hipStream_t)stream;
-  // one persistent block per CU (the sigmoid table takes 33 KB of LDS per
-  // block, loaded once and reused for every unit the block walks)
-  const int max_units = M_cap;   // at least one row per unit
-  const int grid = max_units < 256 ? max_units : 256;
+  // one block per CU (the sigmoid table takes 33 KB of LDS per block)
+  const int grid = 256;         // one block per CU; each takes 1/256 of the live rows
   if (clamp)
     hipLaunchKernelGGL(act_quant_kernel<true>, dim3(grid), dim3(kActThreads), 0, st, gateup,
                        expert_ends, E_local, A, M_cap, I, clamp_limit, hq, hs);
