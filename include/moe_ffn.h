@@ -216,7 +216,8 @@ int moe_grouped_gemm1(const uint8_t* xq, const int32_t* xs, const int32_t* exper
  *   hs           int32 [I/128][M_cap] out: packed UE8M0 scales, live rows only
  * Per element: s = sigmoid(g) rounded to fp32; h = fl32(fl32(g*s) * u); then
  * the per-32 quantisation of moe_scatter_endpoints on h.
- * Requires I % 128 == 0, M_cap % 4 == 0, E_local <= 1024.
+ * Requires I % 128 == 0, M_cap % 4 == 0, E_local <= 1024, M_cap <= 524288,
+ * M_cap * I * 4 < 2^31 (else MOE_ERR_SHAPE).
  * ------------------------------------------------------------------------ */
 int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends, int E_local,
                            int A, int M_cap, int I, float clamp_limit,

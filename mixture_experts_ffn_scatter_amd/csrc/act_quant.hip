@@ -39,6 +39,7 @@ constexpr int kActWaves = kActThreads / 64;
 constexpr int kActBatch = 8;       // items per wave per batch
 constexpr int kActMaxE = 1024;
 constexpr int kActMaxWordsPerRow = 64;  // I <= 8192
+constexpr int kActMaxRowsPerBlock = 2048;  // live rows per block (M_cap <= 256 * 2048)
 constexpr uint32_t kActOob = 0x80000000u;
 
 __device__ __forceinline__ float sigmoid_lookup(const float* tab, float g) {
@@ -76,6 +77,7 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
   __shared__ int s_pref[kActMaxE];    // live rows of the experts before e
   __shared__ int s_tmp[kActWaves];
   __shared__ int s_total;
+  __shared__ int s_rows[kActMaxRowsPerBlock];   // row of each of this block's live rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,41 +119,50 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     run += cnt[j];
   }
   if (tid == kActThreads - 1) s_total = run;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = tid + j * kActThreads;
-    if (i < kVec) reinterpret_cast<v4i*>(s_tab)[i] = tv[j];
-  }
   __syncthreads();
 
   const int R = s_total;
   const int i0 = (int)(((long long)R * blockIdx.x) / gridDim.x);
   const int i1 = (int)(((long long)R * (blockIdx.x + 1)) / gridDim.x);
-  const int nchunks = (I + 511) >> 9;
-  const int items = (i1 - i0) * nchunks;
-  const int nbatch = (items + kActWaves * kActBatch - 1) / (kActWaves * kActBatch);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(gateup), (short)0, (int)((uint32_t)M_cap * (uint32_t)(4 * I)), 0x00020000);
-
-  // row of live row number i (wave-uniform): the expert holding it, then its offset
-  auto row_of = [&](int i) {
+  const int nrows = min(i1 - i0, kActMaxRowsPerBlock);   // the host guarantees <=
+  // row of each of the block's live rows: the expert holding live row i, then its offset
+  for (int t = tid; t < nrows; t += kActThreads) {
+    const int i = i0 + t;
     int lo = 0, hi = E_local - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pref[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    return s_start[lo] + (i - s_pref[lo]);
+    s_rows[t] = s_start[lo] + (i - s_pref[lo]);
+  }
+  __syncthreads();
+  const int nchunks = (I + 511) >> 9;
+  const float inv_nchunks = 1.0f / (float)nchunks;
+  const int items = nrows * nchunks;
+  // item -> (local row, chunk) without an integer division (items < 2^24)
+  auto split = [&](int it, int& rl, int& ch) {
+    int q = (int)((float)it * inv_nchunks);
+    int r = it - q * nchunks;
+    if (r >= nchunks) { ++q; r -= nchunks; }
+    if (r < 0) { --q; r += nchunks; }
+    rl = q;
+    ch = r;
   };
-  // item it of this block: live row i0 + it / nchunks, chunk it % nchunks
+  const int nbatch = (items + kActWaves * kActBatch - 1) / (kActWaves * kActBatch);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(gateup), (short)0, (int)((uint32_t)M_cap * (uint32_t)(4 * I)), 0x00020000);
+
+  // item it of this block: local live row it / nchunks, chunk it % nchunks
   auto load_batch = [&](int b, v4i* G, v4i* U) {
 #pragma unroll
     for (int j = 0; j < kActBatch; ++j) {
       const int it = (b * kActBatch + j) * kActWaves + wid;
       uint32_t off = kActOob;
       if (it < items) {
-        const int i = i0 + it / nchunks;
-        const int col = (it % nchunks) * 512 + lane * 8;
-        if (col < I) off = (uint32_t)row_of(i) * (uint32_t)(4 * I) + (uint32_t)col * 2u;
+        int rl, ch;
+        split(it, rl, ch);
+        const int col = ch * 512 + lane * 8;
+        if (col < I) off = (uint32_t)s_rows[rl] * (uint32_t)(4 * I) + (uint32_t)col * 2u;
       }
       G[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
       U[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off == kActOob ? kActOob : off + (uint32_t)I * 2u, 0, 0);
@@ -162,8 +173,10 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     for (int j = 0; j < kActBatch; ++j) {
       const int it = (b * kActBatch + j) * kActWaves + wid;
       if (it >= items) break;  // wave-uniform
-      const int row = row_of(i0 + it / nchunks);
-      const int col = (it % nchunks) * 512 + lane * 8;
+      int rl, ch;
+      split(it, rl, ch);
+      const int row = s_rows[rl];
+      const int col = ch * 512 + lane * 8;
       const bool act = col < I;
       const uint32_t gw[4] = {(uint32_t)G[j].x, (uint32_t)G[j].y, (uint32_t)G[j].z, (uint32_t)G[j].w};
       const uint32_t uw[4] = {(uint32_t)U[j].x, (uint32_t)U[j].y, (uint32_t)U[j].z, (uint32_t)U[j].w};
@@ -203,6 +216,14 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
 
   v4i GA[kActBatch], UA[kActBatch], GB[kActBatch], UB[kActBatch];
   if (nbatch > 0) load_batch(0, GA, UA);
+  // the table goes to LDS while the first batch is in flight (it waits only
+  // for the table's own loads, which were issued first)
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + j * kActThreads;
+    if (i < kVec) reinterpret_cast<v4i*>(s_tab)[i] = tv[j];
+  }
+  __syncthreads();
   for (int b = 0; b < nbatch; b += 2) {
     if (b + 1 < nbatch) load_batch(b + 1, GB, UB);
     compute_batch(b, GA, UA);
@@ -221,8 +242,10 @@ extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* exp
   if (E_local < 0 || E_local > kActMaxE || A < 1 || M_cap < 0 || I <= 0) return MOE_ERR_SHAPE;
   if (I % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
   if (I / 128 > kActMaxWordsPerRow) return MOE_ERR_SHAPE;
-  // one buffer range covers gate/up: M_cap rows of 4*I bytes below 2 GiB
+  // one buffer range covers gate/up: M_cap rows of 4*I bytes below 2 GiB;
+  // at most kActMaxRowsPerBlock live rows per block
   if ((long long)M_cap * I * 4 >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (M_cap > 256 * kActMaxRowsPerBlock) return MOE_ERR_SHAPE;
   bool clamp = false;
   if (clamp_limit > 0.f && clamp_limit < __builtin_inff()) {
     uint32_t bits;
