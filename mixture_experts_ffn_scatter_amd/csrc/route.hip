@@ -18,14 +18,36 @@ constexpr int kRouteTokensPerBlock = 4;
 constexpr int kRouteMaxE = 1024;
 constexpr int kRouteMaxK = 32;
 
-struct Cand {
-  float key;
-  int idx;     // expert id; INT32_MAX marks "no candidate"
-  float aux;   // sigmoid value (sigmoid mode) or logit (softmax mode)
-};
+// A candidate packed into one integer that orders like (key descending,
+// expert index ascending): the key's bits mapped to an unsigned order in the
+// high word, the complement of the index in the low word. 0 is below every
+// candidate and marks "taken / none".
+__device__ __forceinline__ uint64_t pack_cand(float key, int idx) {
+  uint32_t b = __float_as_uint(key);
+  if (b == 0x80000000u) b = 0;  // -0 ties with +0
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
 
-__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-  return a.key > b.key || (a.key == b.key && a.idx < b.idx);
+// wave-wide maximum with DPP row shifts and row broadcasts (a few cycles per
+// step, no LDS traffic); the result of lane 63 is returned to every lane
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, ROWMASK, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, ROWMASK, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0x111, 0xF>(v); v = v > o ? v : o;   // row_shr:1
+  o = dpp_u64<0x112, 0xF>(v); v = v > o ? v : o;   // row_shr:2
+  o = dpp_u64<0x114, 0xF>(v); v = v > o ? v : o;   // row_shr:4
+  o = dpp_u64<0x118, 0xF>(v); v = v > o ? v : o;   // row_shr:8
+  o = dpp_u64<0x142, 0xA>(v); v = v > o ? v : o;   // row_bcast:15
+  o = dpp_u64<0x143, 0xC>(v); v = v > o ? v : o;   // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 template <int PER_LANE, bool SIGMOID>
@@ -37,65 +59,65 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int t = blockIdx.x * kRouteTokensPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;  // wave-uniform
   const float* row = logits + (size_t)t * E;
-
-  float key[PER_LANE];
+  uint64_t cand[PER_LANE];
   float aux[PER_LANE];
 #pragma unroll
   for (int j = 0; j < PER_LANE; ++j) {
     const int e = lane + 64 * j;
+    cand[j] = 0;
+    aux[j] = 0.f;
     if (e < E) {
       const float v = row[e];
+      float key = v;
       if (SIGMOID) {
         const double s64 = 1.0 / (1.0 + exp(-(double)v));
-        const float s = (float)s64;
-        aux[j] = s;
-        key[j] = __fadd_rn(s, bias[e]);
+        aux[j] = (float)s64;
+        key = __fadd_rn(aux[j], bias[e]);
       } else {
         aux[j] = v;
-        key[j] = v;
       }
-    } else {
-      key[j] = -__builtin_inff();
-      aux[j] = 0.f;
+      cand[j] = pack_cand(key, e);
     }
   }
-
-  uint32_t taken = 0;
+  // k rounds: the best remaining candidate of the wave; lane s keeps round s
   int my_id = -1;
   float my_aux = 0.f;
   for (int s = 0; s < k; ++s) {
-    Cand best{-__builtin_inff(), INT32_MAX, 0.f};
+    uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-      const int e = lane + 64 * j;
-      Cand c{key[j], e, aux[j]};
-      if (e < E && !((taken >> j) & 1u) && better(c, best)) best = c;
-    }
+    for (int j = 0; j < PER_LANE; ++j) best = cand[j] > best ? cand[j] : best;
+    best = wave_max_u64(best);
+    const int idx = (int)(0xFFFFFFFFu - (uint32_t)best);   // wave-uniform
+    const int owner = idx & 63, slot = idx >> 6;
+    float a = 0.f;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      Cand o{__shfl_xor(best.key, m, 64), __shfl_xor(best.idx, m, 64),
-             __shfl_xor(best.aux, m, 64)};
-      if (better(o, best)) best = o;
-    }
-    if (best.idx < E && (best.idx & 63) == lane) taken |= 1u << (best.idx >> 6);
+    for (int j = 0; j < PER_LANE; ++j)
+      if (j == slot) {
+        a = aux[j];
+        if (lane == owner) cand[j] = 0;                  // taken
+      }
+    a = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(a), owner));
     if (lane == s) {
-      my_id = best.idx;
-      my_aux = best.aux;
+      my_id = idx;
+      my_aux = a;
     }
   }
-
-  // weights over the k selected slots, evaluated in fp64 and rounded once
+  // weights over the k selected slots, evaluated in fp64 and rounded once;
+  // the sum runs in slot order
   double num;
   if (SIGMOID) {
     num = (double)my_aux;
   } else {
-    const float top = __shfl(my_aux, 0, 64);
+    const float top = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_aux), 0));
     num = exp((double)my_aux - (double)top);
   }
-  double v = lane < k ? num : 0.0;
-  double sum = v;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+  double sum = 0.0;
+  for (int s = 0; s < k; ++s) {
+    const uint64_t bits = (uint64_t)__double_as_longlong(num);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)bits, s);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(bits >> 32), s);
+    sum += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  }
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     weights[(size_t)t * k + lane] = (float)(num / sum);

@@ -27,12 +27,20 @@ def ops():
 
 # ------------------------------------------------------------------ routing
 
-@pytest.mark.parametrize("case", ["tiny", "prefill-own", "prefill-group", "decode", "large"])
+@pytest.mark.parametrize("case", ["tiny", "ties", "prefill-own", "prefill-group", "decode", "large"])
 def test_route_ids_bitexact(ops, case):
     say(f"route {case}")
     bias = None
     if case == "tiny":
         c = W.tiny(); logits, k = c.logits, c.k
+    elif case == "ties":
+        # few distinct values, signed zeros and -inf: the order falls to the index
+        rng = np.random.default_rng(11)
+        vals = np.array([0.0, -0.0, 1.0, -1.0, 0.5], dtype=np.float32)
+        logits, k = vals[rng.integers(0, len(vals), size=(300, 160))], 8
+        logits[::7, :3] = -np.inf
+        logits[1::7, :] = -0.0
+        logits[1::7, 5::9] = 0.0
     elif case == "prefill-own":
         c = W.prefill(with_weights=False); logits, k = c.logits[:512], c.k
     elif case == "prefill-group":
