@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum moe_status {
     MOE_OK = 0,
@@ -164,11 +164,10 @@ int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_star
  *                   k-step ks = k/128 a 1 KB chunk at ((e*N/16 + cb)*K/128 + ks)*1024
  *                   whose 16 bytes at lane*16 are bytes [64ks + 16(lane/16), +16)
  *                   of row 16cb + lane%16
- *   w_scale_packed  u8, E*(N/16)*ceil(K/1024)*512 bytes, out: for column block
- *                   cb and 8-step group q a 512 B unit at
- *                   ((e*N/16 + cb)*ceil(K/1024) + q)*512 whose byte lane*8 + j is
- *                   the E8M0 byte of group 4(8q + j) + lane/16 of row
- *                   16cb + lane%16 (0 past the last k-step)
+ *   w_scale_packed  u8, E*(K/128)*(N/16)*64 bytes (= E*N*K/32), out: for k-step
+ *                   ks and column block cb a 64-byte line at
+ *                   ((e*K/128 + ks)*N/16 + cb)*64 whose byte lane is the E8M0
+ *                   byte of group 4ks + lane/16 of row 16cb + lane%16
  * Pure data movement (bit-exact). Requires K % 128 == 0, N % 16 == 0,
  * E <= 65535. The caller owns all four buffers; the packed buffers are what
  * moe_grouped_gemm1 / moe_grouped_gemm2 take.

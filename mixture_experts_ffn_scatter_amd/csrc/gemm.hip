@@ -27,9 +27,9 @@
 // (sglang)", section 2.1: weights are rearranged into the layout the GEMM
 // consumes, so that the run-time GEMM never touches the checkpoint layout):
 // codes are stored in MFMA fragment order, one contiguous 1 KB chunk per
-// (16-column block, 128-wide k-step), and scales as one 8-byte word per lane
-// per (16-column block, 8 k-steps). A wave then streams its weights with
-// fully coalesced 16-byte loads straight into registers.
+// (16-column block, 128-wide k-step), and scales as one 64-byte line per
+// (k-step, 16-column block) holding each lane's byte, so that one k-step of
+// a 256-column tile's scales is a single contiguous 1 KB run.
 //
 // Work decomposition. An item is (n-tile of 256 columns, expert, m-chunk of
 // up to 128 live rows). Items are listed n-tile-major and the list is cut
@@ -40,51 +40,60 @@
 // rebuilt inside every block from expert_ends (a block-wide scan), so the
 // grid depends only on host-known sizes and no count is read back.
 //
-// Inside an item, the 8 waves form 2 row groups x 4 column groups: wave
-// (rg, cg) computes rows [64rg, 64rg+64) x columns [64cg, 64cg+64) of the
-// tile, so an activation fragment read from LDS feeds 4 MFMAs. Its weight
-// fragments go global -> registers 4 k-steps ahead (both row groups read
-// the same fragments, the second from cache; a row group with no live rows
-// reads nothing). The activation chunk (shared by all waves) is loaded
-// 3 k-steps ahead into registers, one 16-row block per wave, and written
-// to a two-slot LDS ring one step ahead; one barrier per k-step. Loads use buffer resources whose
-// range ends at the last live row (or column): lanes past it read zeros
-// without touching memory, so padding rows are never read and every wave
-// issues the same instruction stream.
+// Data path. Every operand travels global -> LDS by the buffer-to-LDS
+// transfer of gfx950 (no register staging) into a ring of 4 stages of one
+// k-step each (activations, weights and both scale sets: 33.5 KB a stage).
+// A step issues the transfers of the step 3 ahead (continuing into the next
+// item of the block), so 3 steps of loads are always in flight; each wave
+// waits for its own transfers of the current stage with an exact count and
+// one barrier publishes the stage. The 8 waves form 2 row groups x 4
+// column groups; wave (rg, cg) owns rows [64 rg, +64) x columns [64 cg, +64)
+// of the tile, so per step it reads 4 weight and 4 activation fragments
+// (12 KB of LDS for 16 MFMAs) and issues up to 16 MFMAs, reading the
+// activation fragments two row blocks ahead of the MFMAs that consume them.
+// Loads use buffer resources whose range ends at the last live row (or
+// column): lanes past it read zeros without touching memory, so
+// padding rows are never read.
 #include "common.h"
 
-#ifndef GEMM_CB
-#define GEMM_CB 2
-#endif
-#ifndef GEMM_WD
-#define GEMM_WD 4
-#endif
-#ifndef GEMM_XD
-#define GEMM_XD 2
-#endif
+#include <type_traits>
 
 namespace moe {
 
 constexpr int kGemmThreads = 512;  // 8 waves
 constexpr int kGemmBM = 128;       // rows per item (8 blocks of 16)
 constexpr int kGemmBN = 256;       // columns per item (16 blocks of 16)
-constexpr int kGemmCB = GEMM_CB;                        // column blocks per wave
-constexpr int kGemmNCG = kGemmBN / 16 / kGemmCB;            // column groups
-constexpr int kGemmMB = (kGemmBM / 16) / (kGemmThreads / 64 / kGemmNCG);  // row blocks per wave
-static_assert(kGemmNCG * (kGemmBM / 16 / kGemmMB) == kGemmThreads / 64, "wave grid");
-constexpr int kGemmU = 8;          // k-loop unroll (one weight-scale word group)
-constexpr int kGemmWD = GEMM_WD;   // weight prefetch distance in k-steps
-constexpr int kGemmXD = GEMM_XD;   // activation register prefetch depth
+constexpr int kGemmCB = 4;         // column blocks per wave (MFMA)
+constexpr int kGemmMB = 4;         // row blocks per wave (MFMA)
+constexpr int kGemmRG = kGemmBM / 16 / kGemmMB;         // row groups of waves
+constexpr int kGemmCG = kGemmBN / 16 / kGemmCB;         // column groups of waves
+constexpr int kDmaCB = 2;          // weight chunks each wave transfers per step
+constexpr int kGemmStages = 4;     // LDS ring depth (k-steps)
+#ifndef GEMM_RD
+#define GEMM_RD 3
+#endif
+constexpr int kGemmRD = GEMM_RD;   // activation fragments in registers (read-ahead + 1)
 constexpr int kGemmMaxE = 1024;
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: reads zero, no traffic
+static_assert(kGemmRG * kGemmCG == kGemmThreads / 64, "wave grid");
+static_assert(kDmaCB * (kGemmThreads / 64) == kGemmBN / 16, "each wave transfers 2 weight chunks");
 
-// One LDS slot: the activation chunk of one k-step in MFMA fragment order
-// (x[mb][h][lane] = 16 bytes of row 16mb + lane%16, k [64h + 16(lane/16), +16))
-// and its 128 packed scale words.
-struct __attribute__((aligned(16))) GemmXSlot {
-  uint8_t x[kGemmBM / 16][2][64 * 16];
+// One LDS stage: everything one k-step of a 128 x 256 tile reads.
+//   x[mb][h]: activations of rows 16mb.. in B-fragment order (lane l: 16 bytes
+//             of row 16mb + l%16 at k 64h + 16(l/16))
+//   w[cb]:    weight codes of column block cb in A-fragment order
+//   xs[row]:  the row's 4 UE8M0 bytes (k-blocks 0..3 of the step)
+//   ws[cb]:   lane l's E8M0 byte of column block cb
+struct __attribute__((aligned(16))) GemmStage {
+  uint8_t x[kGemmBM / 16][2][1024];
+  uint8_t w[kGemmBN / 16][1024];
   uint32_t xs[kGemmBM];
+  uint8_t ws[kGemmBN / 16][64];
 };
+constexpr int kOffW = kGemmBM / 16 * 2 * 1024;
+constexpr int kOffXs = kOffW + kGemmBN / 16 * 1024;
+constexpr int kOffWs = kOffXs + kGemmBM * 4;
+static_assert(sizeof(GemmStage) == kOffWs + kGemmBN / 16 * 64, "stage layout");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   // raw buffer (stride 0); word 3 as for every gfx9 raw buffer
@@ -92,12 +101,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            0x00020000);
 }
 
-// Workgroup barrier without the release fence of __syncthreads() (which
-// would wait for every outstanding global load and empty the prefetch):
-// this wave's LDS writes are completed first, which is all the ring needs.
-// The memory clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Buffer-to-LDS transfers: lane l's 16 (or 4) bytes at buffer offset voff
+// land at LDS byte address m0 + 16 l (or m0 + 4 l). Lanes past the buffer's
+// range write zeros and read no memory. The transfers are invisible to the
+// compiler's wait counting; the kernel waits for them explicitly.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r) : "memory");
 }
 
 __device__ int block_exclusive_scan(int v, int* tmp) {
@@ -117,41 +131,40 @@ __device__ int block_exclusive_scan(int v, int* tmp) {
   return off + incl - v;
 }
 
-// One work item's load parameters. Buffer ranges end at the item's last
-// live column block (weights) and last live row (activations); an absent
-// item has empty ranges, so every load from it reads zero without touching
-// memory.
-struct GemmItem {
+// Where one work item sits: rows [r0, r0 + rows) of expert e, column
+// blocks [cb0, cb0 + ncb).
+struct GemmTile {
+  int e, r0, rows, nblk, cb0, ncb;
+};
+
+// One work item's transfer sources. With live false every offset is kOob,
+// which is how an absent item (or a step past the last) is "loaded".
+struct GemmSrc {
   __amdgpu_buffer_rsrc_t wr, sr, xr, xsr;
-  uint32_t wo[kGemmCB], so[kGemmCB];   // per-lane weight / scale offsets
-  uint32_t xso;                        // per-lane scale-word offset (row part)
-  int r0, rows, nblk, mlive, cb0, ncb, valid;
+  uint32_t wo[kDmaCB];   // per-lane weight-code offsets of the wave's transferred blocks
+  uint32_t xo;           // per-lane activation offset of this wave's row block
+  uint32_t xso;          // per-lane scale-word offset (waves 0, 1: rows 64 w + lane)
+  uint32_t so;           // per-lane weight-scale offset (wave 2: the tile's 1 KB line)
 };
 
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
     const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
     const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int K, int N,
     const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out) {
-  __shared__ GemmXSlot xl[2];
+  __shared__ GemmStage stage[kGemmStages];
   __shared__ int s_prefix[kGemmMaxE + 1];
   __shared__ int s_tmp[kGemmThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int rg = wid / kGemmCG;          // MFMA rows: row blocks [MB rg, MB rg + MB)
+  const int cg = wid % kGemmCG;          // MFMA columns: column blocks [CB cg, CB cg + CB)
   const int l16 = lane & 15;
   const int g = lane >> 4;
-  const int rg = wid / kGemmNCG;         // row group: row blocks [MB*rg, MB*rg+MB)
-  const int cg = wid % kGemmNCG;         // column group: column blocks [CB*cg, CB*cg+CB)
   const int KS = K / 128;                // k-steps
-  const int KS8 = (KS + 7) / 8;          // 8-step scale groups
   const int NB = N / 16;                 // column blocks
   const int NT = (N + kGemmBN - 1) / kGemmBN;
-  // With KS a multiple of the weight prefetch distance (K % 512 == 0) the
-  // register rings line up across items, and the loads of the next item's
-  // first steps are issued during the current item's last ones. Otherwise
-  // each item starts with its own prologue.
-  const bool chain = KS % kGemmWD == 0;
 
   // m-chunks per expert and their exclusive scan (2 experts per thread)
   int cnt[2];
@@ -161,9 +174,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
     const int e = tid * 2 + j;
     cnt[j] = 0;
     if (e < E_local) {
-      int s, en;
-      expert_range(expert_ends, e, A, M_cap, s, en);
-      cnt[j] = (en - s + kGemmBM - 1) / kGemmBM;
+      int st, en;
+      expert_range(expert_ends, e, A, M_cap, st, en);
+      cnt[j] = (en - st + kGemmBM - 1) / kGemmBM;
     }
     local_sum += cnt[j];
   }
@@ -186,19 +199,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
   const int i_end = (int)(((long long)L * (xcd + 1)) / 8);
   const int first = (int)(((long long)L * xcd) / 8) + slot;
 
-  const uint32_t xo = (uint32_t)(16 * wid + l16) * (uint32_t)K + 16 * g;   // staged row block wid
-
-  auto make_item = [&](int item) {
-    GemmItem it;
-    it.valid = item < i_end;
-    if (!it.valid) {
-      it.wr = it.sr = it.xr = it.xsr = make_rsrc(Wp, 0u);
-#pragma unroll
-      for (int c = 0; c < kGemmCB; ++c) it.wo[c] = it.so[c] = kOob;
-      it.xso = kOob;
-      it.r0 = it.rows = it.nblk = it.mlive = it.cb0 = it.ncb = 0;
-      return it;
-    }
+  auto locate = [&](int item, GemmTile& T) {
     const int nt = item / MT;
     const int j = item - nt * MT;
     int lo = 0, hi = E_local - 1;
@@ -206,81 +207,86 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
       const int mid = (lo + hi + 1) >> 1;
       if (s_prefix[mid] <= j) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
     int start, end;
-    expert_range(expert_ends, e, A, M_cap, start, end);
-    it.r0 = start + (j - s_prefix[e]) * kGemmBM;
-    it.rows = min(kGemmBM, end - it.r0);                  // >= 1
-    it.nblk = (it.rows + 15) >> 4;
-    it.mlive = min(max(it.nblk - kGemmMB * rg, 0), kGemmMB);
-    it.cb0 = nt * (kGemmBN / 16);
-    it.ncb = min(kGemmBN / 16, NB - it.cb0);
-    it.wr = make_rsrc(Wp + ((size_t)e * NB + it.cb0) * KS * 1024, (uint32_t)(it.ncb * KS) * 1024u);
-    it.sr = make_rsrc(Sp + ((size_t)e * NB + it.cb0) * KS8 * 512, (uint32_t)(it.ncb * KS8) * 512u);
-    it.xr = make_rsrc(X + (size_t)it.r0 * K, (uint32_t)it.rows * (uint32_t)K);
-    it.xsr = make_rsrc(Xs + it.r0, (uint32_t)((KS - 1) * M_cap + it.rows) * 4u);
+    expert_range(expert_ends, lo, A, M_cap, start, end);
+    T.e = lo;
+    T.r0 = start + (j - s_prefix[lo]) * kGemmBM;
+    T.rows = min(kGemmBM, end - T.r0);                   // >= 1
+    T.nblk = (T.rows + 15) >> 4;
+    T.cb0 = nt * (kGemmBN / 16);
+    T.ncb = min(kGemmBN / 16, NB - T.cb0);
+  };
+  auto sources = [&](const GemmTile& T, bool live) {
+    GemmSrc q;
+    q.wr = make_rsrc(Wp + ((size_t)T.e * NB + T.cb0) * KS * 1024, (uint32_t)(T.ncb * KS) * 1024u);
+    q.sr = make_rsrc(Sp + (size_t)T.e * KS * NB * 64, (uint32_t)(KS * NB) * 64u);
+    q.xr = make_rsrc(X + (size_t)T.r0 * K, (uint32_t)T.rows * (uint32_t)K);
+    q.xsr = make_rsrc(Xs + T.r0, (uint32_t)((KS - 1) * M_cap + T.rows) * 4u);
 #pragma unroll
-    for (int c = 0; c < kGemmCB; ++c) {
-      const int cb = kGemmCB * cg + c;
-      const bool live = cb < it.ncb && it.mlive > 0;
-      it.wo[c] = live ? (uint32_t)(cb * KS) * 1024u + lane * 16 : kOob;
-      it.so[c] = live ? (uint32_t)(cb * KS8) * 512u + lane * 8 : kOob;
+    for (int c = 0; c < kDmaCB; ++c) {
+      const int cb = kDmaCB * wid + c;
+      q.wo[c] = (live && cb < T.ncb) ? (uint32_t)(cb * KS) * 1024u + lane * 16 : kOob;
     }
-    it.xso = (lane < 16 && 16 * wid + l16 < it.rows) ? (uint32_t)(16 * wid + l16) * 4u : kOob;
-    return it;
+    q.xo = (live && 16 * wid < T.rows) ? (uint32_t)(16 * wid + l16) * (uint32_t)K + 16 * g : kOob;
+    q.xso = (live && 64 * wid < T.rows) ? (uint32_t)(64 * wid + lane) * 4u : kOob;
+    q.so = live ? (uint32_t)T.cb0 * 64u + lane * 16 : kOob;
+    return q;
   };
 
-  // loads of step ks of item p (ks < KS)
-  auto load_w = [&](const GemmItem& p, int ks, v4i* dst) {
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&stage[0];
+  // transfers of k-step st of a source into ring stage sg: per wave its 2
+  // weight blocks and the 2 halves of its activation row block; waves 0, 1
+  // the scale words of rows 64 w .. 64 w + 63, wave 2 the weight-scale line
+  auto issue = [&](const GemmSrc& q, int st, int sg) {
+    const uint32_t base = lds0 + (uint32_t)sg * (uint32_t)sizeof(GemmStage);
 #pragma unroll
-    for (int c = 0; c < kGemmCB; ++c)
-      dst[c] = __builtin_amdgcn_raw_buffer_load_b128(p.wr, p.wo[c] + ks * 1024, 0, 0);
-  };
-  auto load_s = [&](const GemmItem& p, int q, v2i* dst) {
+    for (int c = 0; c < kDmaCB; ++c)
+      dma16(q.wr, q.wo[c] + (uint32_t)st * 1024u, base + kOffW + (kDmaCB * wid + c) * 1024);
 #pragma unroll
-    for (int c = 0; c < kGemmCB; ++c)
-      dst[c] = __builtin_amdgcn_raw_buffer_load_b64(p.sr, p.so[c] + q * 512, 0, 0);
+    for (int h = 0; h < 2; ++h)
+      dma16(q.xr, q.xo + (uint32_t)st * 128u + 64 * h, base + wid * 2048 + h * 1024);
+    if (wid < 2) dma4(q.xsr, q.xso + (uint32_t)(st * M_cap) * 4u, base + kOffXs + wid * 256);
+    else if (wid == 2) dma16(q.sr, q.so + (uint32_t)(st * NB) * 64u, base + kOffWs);
   };
-  auto load_x = [&](const GemmItem& p, int ks, v4i* dst, uint32_t& ws) {
-    dst[0] = __builtin_amdgcn_raw_buffer_load_b128(p.xr, xo + ks * 128, 0, 0);
-    dst[1] = __builtin_amdgcn_raw_buffer_load_b128(p.xr, xo + ks * 128 + 64, 0, 0);
-    ws = __builtin_amdgcn_raw_buffer_load_b32(
-        p.xsr, p.xso == kOob ? kOob : p.xso + (uint32_t)(ks * M_cap) * 4u, 0, 0);
-  };
-  auto store_x = [&](int sl, const v4i* src, uint32_t ws) {
-    *reinterpret_cast<v4i*>(&xl[sl].x[wid][0][lane * 16]) = src[0];
-    *reinterpret_cast<v4i*>(&xl[sl].x[wid][1][lane * 16]) = src[1];
-    if (lane < 16) xl[sl].xs[16 * wid + lane] = ws;
-  };
-
-  v4i wbuf[kGemmWD][kGemmCB];
-  v2i s_cur[kGemmCB], s_nxt[kGemmCB];
-  v4i xbuf[kGemmXD][2];
-  uint32_t xsb[kGemmXD];
-  const GemmItem none = make_item(i_end);
-
-  // prologue of an item: weights of steps 0..WD-1, scale groups 0 and 1,
-  // activations of steps 0..XD-1 (step 0 goes to LDS slot 0 and its
-  // registers take step XD); loads past the item read nothing
-  auto prologue = [&](const GemmItem& p) {
-#pragma unroll
-    for (int s = 0; s < kGemmWD; ++s) load_w(s < KS ? p : none, s < KS ? s : 0, wbuf[s]);
-    load_s(p, 0, s_cur);
-    load_s(KS8 > 1 ? p : none, 1, s_nxt);
-#pragma unroll
-    for (int s = 0; s < kGemmXD; ++s) load_x(s < KS ? p : none, s < KS ? s : 0, xbuf[s], xsb[s]);
-    store_x(0, xbuf[0], xsb[0]);
-    load_x(kGemmXD < KS ? p : none, kGemmXD < KS ? kGemmXD : 0, xbuf[0], xsb[0]);
-    ring_barrier();
+  // waits until this wave's transfers of the oldest stage in flight have
+  // landed: two stages (5 transfers per step on waves 0-2, 4 on the others)
+  // were issued after it, unless stores intervened (drain: wait for all)
+  static_assert(kGemmStages == 4, "wait counts assume two stages issued after the awaited one");
+  auto wait_stage = [&](bool drain) {
+    if (drain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (wid < 3) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   };
 
   int item = first;
-  GemmItem cur = make_item(item);
-  if (cur.valid) prologue(cur);
-  while (cur.valid) {
-    const GemmItem nxt = make_item(item + nslot);
-    // loads for steps past the end of this item come from the next one
-    const GemmItem& pf = chain ? nxt : none;
+  bool valid = item < i_end;
+  GemmTile T{0, 0, 1, 1, 0, 0};
+  if (valid) locate(item, T);
+  // the transfer walker: item pit, step pst, its sources; it runs 3 steps
+  // ahead of the compute and steps into the block's next item (or past the
+  // last, into sources that read nothing) at an item's end
+  int pit = item, pst = 0;
+  GemmSrc ps = sources(T, valid);
+  auto advance = [&]() {
+    if (++pst == KS) {
+      pst = 0;
+      pit += nslot;
+      GemmTile U = T;
+      if (pit < i_end) locate(pit, U);
+      ps = sources(U, pit < i_end);
+    }
+  };
+  int gs = 0;                            // running k-step count; ring stage gs % 4
+  if (valid) {
+    for (int s = 0; s < kGemmStages - 1; ++s) {
+      issue(ps, pst, s);
+      advance();
+    }
+  }
+  bool drain = false;
+  while (valid) {
+    // this wave's live row blocks among its kGemmMB
+    const int mlive = min(max(T.nblk - kGemmMB * rg, 0), kGemmMB);
 
     v4f acc[kGemmCB][kGemmMB];
 #pragma unroll
@@ -288,101 +294,99 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < kGemmMB; ++i) acc[c][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb = 0; kb < KS; kb += kGemmU) {
-      if (kb > 0) {
+    // one k-step; FULL (all of the wave's row blocks live) runs without
+    // per-row-block branches
+    auto step = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      // stage gs complete for this wave, then (barrier) for the block; the
+      // barrier also retires every read of the stage refilled below
+      wait_stage(drain);
+      drain = false;
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const GemmStage& S = stage[gs % kGemmStages];
+      // this wave's weight fragments and scale bytes
+      v4i af[kGemmCB];
+      int sa[kGemmCB];
 #pragma unroll
-        for (int c = 0; c < kGemmCB; ++c) s_cur[c] = s_nxt[c];
+      for (int c = 0; c < kGemmCB; ++c) {
+        af[c] = *reinterpret_cast<const v4i*>(&S.w[kGemmCB * cg + c][lane * 16]);
+        sa[c] = S.ws[kGemmCB * cg + c][lane];
       }
-      // the scale group after the current one: this item's, else the next
-      // item's group 0 (groups 0 and 1 of the first item come from the prologue)
-      if (kb > 0) {
-        const int q = kb / kGemmU + 1;
-        load_s(q < KS8 ? cur : pf, q < KS8 ? q : 0, s_nxt);
+      // the scale words of the lane's row in every row block (two per LDS
+      // read); k-block g is byte g, moved to byte 0 for the MFMA
+      uint32_t xw[kGemmMB];
+#pragma unroll
+      for (int i = 0; i < kGemmMB; ++i) xw[i] = S.xs[16 * (kGemmMB * rg + i) + l16];
+      // activation fragments, read kGemmRD - 1 row blocks ahead of their
+      // MFMAs (LDS latency under this load spans several MFMA pairs); a row
+      // block past the live ones is read as one broadcast word
+      v8i bf[kGemmRD];
+      auto read_b = [&](int i) {
+        const bool live = FULL || i < mlive;
+        const uint8_t* xb = &S.x[0][0][0];
+        const int o = live ? (kGemmMB * rg + i) * 2048 + lane * 16 : 0;
+        const v4i lo4 = *reinterpret_cast<const v4i*>(xb + o);
+        const v4i hi4 = *reinterpret_cast<const v4i*>(xb + o + (live ? 1024 : 0));
+        bf[i % kGemmRD] = v8i{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+      };
+#pragma unroll
+      for (int i = 0; i < kGemmRD - 1; ++i) read_b(i);
+      // transfers of the walker's step (3 ahead) into the stage the
+      // previous step used
+      issue(ps, pst, (gs + kGemmStages - 1) % kGemmStages);
+      advance();
+#pragma unroll
+      for (int i = 0; i < kGemmMB; ++i) {
+        if (i + kGemmRD - 1 < kGemmMB) read_b(i + kGemmRD - 1);
+        if (FULL || i < mlive) {
+          const int sb = (int)(xw[i] >> (8 * g));
+#pragma unroll
+          for (int c = 0; c < kGemmCB; ++c)
+            acc[c][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[c].xyzwxyzw, bf[i % kGemmRD], acc[c][i], 4, 0, 0, sa[c], 0, sb);
+        }
       }
-#pragma unroll
-      for (int jj = 0; jj < kGemmU; ++jj) {
-        const int ks = kb + jj;
-        if (ks >= KS) break;
-        // stage step ks+1 (of this item, else step 0 of the next) into the
-        // other slot, then refill its registers (xbuf[i % XD] holds step i)
-        const int xi = (jj + 1) % kGemmXD;
-        if (ks + 1 < KS || chain) store_x((jj + 1) & 1, xbuf[xi], xsb[xi]);
-        {
-          const int t = ks + 1 + kGemmXD;
-          load_x(t < KS ? cur : pf, t < KS ? t : t - KS, xbuf[xi], xsb[xi]);
-        }
-
-        // compute step ks from slot ks % 2 (kb and KS are even)
-        const GemmXSlot& S = xl[jj & 1];
-        v8i a8[kGemmCB];
-        int sa[kGemmCB];
-#pragma unroll
-        for (int c = 0; c < kGemmCB; ++c) {
-          const v4i wv = wbuf[jj % kGemmWD][c];
-          a8[c] = v8i{wv.x, wv.y, wv.z, wv.w, 0, 0, 0, 0};
-          // weight scale byte of this step moved to byte 0 (opsel 0)
-          sa[c] = (int)((uint32_t)s_cur[c][jj >> 2] >> (8 * (jj & 3)));
-        }
-#pragma unroll
-        for (int i = 0; i < kGemmMB; ++i) {
-          if (i < cur.mlive) {
-            const int mb = kGemmMB * rg + i;
-            const v4i lo4 = *reinterpret_cast<const v4i*>(&S.x[mb][0][lane * 16]);
-            const v4i hi4 = *reinterpret_cast<const v4i*>(&S.x[mb][1][lane * 16]);
-            const v8i b = v8i{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-            const int sb = (int)(S.xs[mb * 16 + l16] >> (8 * g));
-#pragma unroll
-            for (int c = 0; c < kGemmCB; ++c)
-              acc[c][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  a8[c], b, acc[c][i], 4, 0, 0, sa[c], 0, sb);
-          }
-        }
-        // refill this step's weight registers with step ks + WD (of this
-        // item, else of the next)
-        {
-          const int t = ks + kGemmWD;
-          load_w(t < KS ? cur : pf, t < KS ? t : t - KS, wbuf[jj % kGemmWD]);
-        }
-        ring_barrier();
-      }
-    }
-    // the next item's scale groups 0 and 1 (group 0 is already in s_nxt
-    // when this item had more than one group, else in flight below)
-    if (chain) {
-#pragma unroll
-      for (int c = 0; c < kGemmCB; ++c) s_cur[c] = s_nxt[c];
-      if (KS8 == 1) load_s(nxt, 0, s_cur);
-      load_s(KS8 > 1 ? nxt : none, 1, s_nxt);
+      ++gs;
+    };
+    if (mlive == kGemmMB) {
+      for (int ks = 0; ks < KS; ++ks) step(std::true_type{});
+    } else {
+      for (int ks = 0; ks < KS; ++ks) step(std::false_type{});
     }
 
     // epilogue: lane holds columns 16cb + 4g .. +3 of row r0 + 16mb + l16
 #pragma unroll
     for (int c = 0; c < kGemmCB; ++c) {
       const int cb = kGemmCB * cg + c;
-      if (cb >= cur.ncb) continue;
-      const int n = (cur.cb0 + cb) * 16 + 4 * g;
+      if (cb >= T.ncb) continue;
+      const int n = (T.cb0 + cb) * 16 + 4 * g;
 #pragma unroll
       for (int i = 0; i < kGemmMB; ++i) {
         const int mr = 16 * (kGemmMB * rg + i) + l16;
-        if (i >= cur.mlive || mr >= cur.rows) continue;
+        if (i >= mlive || mr >= T.rows) continue;
         const v4f v = acc[c][i];
         const uint2 o = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-        *reinterpret_cast<uint2*>(out + (size_t)(cur.r0 + mr) * N + n) = o;
+        *reinterpret_cast<uint2*>(out + (size_t)(T.r0 + mr) * N + n) = o;
       }
     }
+    // stores and transfers share one counter and need not complete in
+    // order: the next wait takes everything
+    drain = true;
     item += nslot;
-    cur = nxt;
-    if (!chain && cur.valid) prologue(cur);
+    valid = item < i_end;
+    if (valid) locate(item, T);
   }
+  // every transfer this block issued has landed before its LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Load-time weight preparation (bit-exact data movement):
 //   codes  w [E][N][K/2] -> wp [E][N/16][K/128][64 lanes][16 B]
 //          lane l of chunk (e, cb, ks) = bytes [64ks + 16(l/16), +16) of row 16cb + l%16
-//   scales s [E][N][K/32] -> sp [E][N/16][ceil(K/1024)][64 lanes][8 B]
-//          byte j of lane l of (e, cb, q) = group 4(8q + j) + l/16 of row 16cb + l%16,
-//          zero past the last k-step
-// One wave per 1 KB chunk (codes) or 512 B unit (scales).
+//   scales s [E][N][K/32] -> sp [E][K/128][N/16][64 lanes]
+//          byte l of line (e, ks, cb) = group 4ks + l/16 of row 16cb + l%16
+// One wave per 1 KB code chunk; one thread per scale byte.
 __global__ __launch_bounds__(256) void pack_mx_codes_kernel(const uint8_t* __restrict__ w, int N,
                                                             int K, uint8_t* __restrict__ wp) {
   const int KS = K / 128;
@@ -401,24 +405,17 @@ __global__ __launch_bounds__(256) void pack_mx_codes_kernel(const uint8_t* __res
 
 __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ s, int N,
                                                              int K, uint8_t* __restrict__ sp) {
-  const int KS = K / 128;
-  const int KS8 = (KS + 7) / 8;
-  const size_t per_e = (size_t)(N / 16) * KS8;
-  const size_t unit = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= per_e) return;
+  const int NB = N / 16;
+  const size_t per_e = (size_t)(K / 128) * NB * 64;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= per_e) return;
   const int e = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int cb = (int)(unit / KS8);
-  const int q = (int)(unit - (size_t)cb * KS8);
-  const uint8_t* src = s + ((size_t)e * N + 16 * cb + (lane & 15)) * (size_t)(K / 32);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int ks = 8 * q + jj;
-    const uint32_t b = ks < KS ? src[4 * ks + (lane >> 4)] : 0u;
-    if (jj < 4) lo |= b << (8 * jj); else hi |= b << (8 * (jj - 4));
-  }
-  *reinterpret_cast<uint2*>(sp + ((size_t)e * per_e + unit) * 512 + lane * 8) = make_uint2(lo, hi);
+  const int l = (int)(idx & 63);
+  const size_t line = idx >> 6;                  // ks * NB + cb
+  const int ks = (int)(line / NB);
+  const int cb = (int)(line - (size_t)ks * NB);
+  sp[(size_t)e * per_e + idx] =
+      s[((size_t)e * N + 16 * cb + (l & 15)) * (size_t)(K / 32) + 4 * ks + (l >> 4)];
 }
 
 static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_t* ends,
@@ -454,13 +451,13 @@ extern "C" int moe_pack_mx_weights(const uint8_t* w, const uint8_t* w_scale, int
   if (E == 0 || N == 0) return MOE_OK;
   if (!w || !w_scale || !w_packed || !w_scale_packed) return MOE_ERR_NULL;
   const size_t chunks = (size_t)(N / 16) * (K / 128);
-  const size_t units = (size_t)(N / 16) * ((K / 128 + 7) / 8);
-  if ((chunks + 3) / 4 > 0x7fffffffu) return MOE_ERR_SHAPE;
+  const size_t scale_bytes = (size_t)N * (K / 32);
+  if ((chunks + 3) / 4 > 0x7fffffffu || (scale_bytes + 255) / 256 > 0x7fffffffu) return MOE_ERR_SHAPE;
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(moe::pack_mx_codes_kernel, dim3((unsigned)((chunks + 3) / 4), (unsigned)E),
                      dim3(256), 0, st, w, N, K, w_packed);
   MOE_CHECK_LAUNCH();
-  hipLaunchKernelGGL(moe::pack_mx_scales_kernel, dim3((unsigned)((units + 3) / 4), (unsigned)E),
+  hipLaunchKernelGGL(moe::pack_mx_scales_kernel, dim3((unsigned)((scale_bytes + 255) / 256), (unsigned)E),
                      dim3(256), 0, st, w_scale, N, K, w_scale_packed);
   MOE_CHECK_LAUNCH();
   return MOE_OK;

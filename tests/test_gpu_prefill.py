@@ -335,23 +335,22 @@ def _expected_packing(w, s):
     """The documented packed layouts, built by plain indexing."""
     E, N, K2 = w.shape
     K = 2 * K2
-    KS, KS8 = K // 128, (K // 128 + 7) // 8
+    KS = K // 128
     lane = np.arange(64)
     wp = np.empty((E, N // 16, KS, 64, 16), np.uint8)
-    sp = np.zeros((E, N // 16, KS8, 64, 8), np.uint8)
+    sp = np.empty((E, KS, N // 16, 64), np.uint8)
     for cb in range(N // 16):
         rows = 16 * cb + lane % 16
         for ks in range(KS):
             cols = 64 * ks + 16 * (lane // 16)
             wp[:, cb, ks] = w[:, rows[:, None], cols[:, None] + np.arange(16)[None, :]]
-            q, j = divmod(ks, 8)
-            sp[:, cb, q, :, j] = s[:, rows, 4 * ks + lane // 16]
-    return wp.reshape(E, N, K2), sp.reshape(E, N // 16, KS8, 512)
+            sp[:, ks, cb, :] = s[:, rows, 4 * ks + lane // 16]
+    return wp.reshape(E, N, K2), sp
 
 
 def test_pack_mx_weights_bitexact(ops):
     """Load-time weight preparation is pure data movement into the documented
-    fragment order (codes) and 8-step lane words (scales, zero-padded)."""
+    fragment order (codes) and per-step lane lines (scales)."""
     rng = np.random.default_rng(2024)
     for E, N, K in ((3, 48, 384), (1, 128, 128), (2, 256, 2048), (1, 64, 1152)):
         say(f"pack mx weights E={E} N={N} K={K}")
