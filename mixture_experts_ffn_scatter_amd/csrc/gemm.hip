@@ -152,7 +152,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
     const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int K, int N,
     const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out) {
   __shared__ GemmStage stage[kGemmStages];
-  __shared__ int s_prefix[kGemmMaxE + 1];
+  __shared__ int s_fpre[kGemmMaxE + 1];
+  __shared__ int s_ppre[kGemmMaxE + 1];
   __shared__ int s_tmp[kGemmThreads / 64];
 
   const int tid = threadIdx.x;
@@ -166,51 +167,85 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
   const int NB = N / 16;                 // column blocks
   const int NT = (N + kGemmBN - 1) / kGemmBN;
 
-  // m-chunks per expert and their exclusive scan (2 experts per thread)
-  int cnt[2];
-  int local_sum = 0;
+  // chunks per expert: full 128-row chunks and at most one partial one, and
+  // the exclusive scans of both (2 experts per thread)
+  int nf[2], np_[2];
+  int fsum = 0, psum = 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int e = tid * 2 + j;
-    cnt[j] = 0;
+    nf[j] = np_[j] = 0;
     if (e < E_local) {
       int st, en;
       expert_range(expert_ends, e, A, M_cap, st, en);
-      cnt[j] = (en - st + kGemmBM - 1) / kGemmBM;
+      nf[j] = (en - st) / kGemmBM;
+      np_[j] = (en - st) % kGemmBM != 0;
     }
-    local_sum += cnt[j];
+    fsum += nf[j];
+    psum += np_[j];
   }
-  int run = block_exclusive_scan(local_sum, s_tmp);
+  // both scans in one pass: fulls in the low 16 bits, partials in the high
+  // (at most 1024 experts x (M_cap / 128) chunks; the host caps M_cap)
+  int run = block_exclusive_scan(fsum | (psum << 16), s_tmp);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int e = tid * 2 + j;
-    if (e < E_local) s_prefix[e] = run;
-    run += cnt[j];
+    if (e < E_local) {
+      s_fpre[e] = run & 0xFFFF;
+      s_ppre[e] = run >> 16;
+    }
+    run += nf[j] | (np_[j] << 16);
   }
-  if (tid == kGemmThreads - 1) s_prefix[E_local] = run;
+  if (tid == kGemmThreads - 1) {
+    s_fpre[E_local] = run & 0xFFFF;
+    s_ppre[E_local] = run >> 16;
+  }
   __syncthreads();
-  const int MT = s_prefix[E_local];      // m-chunks over all experts
-  const int L = MT * NT;                 // items
+  // LDS and global values the whole block agrees on are made scalar
+  // (readfirstlane), so the buffer resources built from them stay in SGPRs
+  const int F = __builtin_amdgcn_readfirstlane(s_fpre[E_local]);   // full chunks
+  const int P = __builtin_amdgcn_readfirstlane(s_ppre[E_local]);   // partial chunks
+  const int MT = F + P;                  // chunks of one n-tile
+  const int L = MT * NT;                 // items: u = nt * MT + j
+  if (MT == 0) return;                   // no live rows (uniform over the block)
 
-  // this block's XCD range of the item list and its slot in it
+  // this block's XCD range [i0, i1) of the item list (block b runs on XCD
+  // b % 8); the XCD's blocks take its items round-robin. Within an n-tile
+  // the chunks are listed expert by expert (the fulls of an expert, then its
+  // partial), so the m-chunks of one (expert, n-tile) run side by side on
+  // neighbouring blocks and share the weight slice in that XCD's L2, and
+  // heavy and light items run at the same time (MFMA-bound next to
+  // weight-streaming).
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslot = gridDim.x >> 3;      // the grid is a multiple of 8
-  const int i_end = (int)(((long long)L * (xcd + 1)) / 8);
-  const int first = (int)(((long long)L * xcd) / 8) + slot;
+  const int i0 = (int)(((long long)L * xcd) / 8);
+  const int i1 = (int)(((long long)L * (xcd + 1)) / 8);
+  // the block's k-th item, or -1 past its last
+  auto item_at = [&](int k) {
+    const int u = i0 + slot + k * nslot;
+    return u < i1 ? u : -1;
+  };
 
   auto locate = [&](int item, GemmTile& T) {
     const int nt = item / MT;
     const int j = item - nt * MT;
+    // chunks before expert e: s_fpre[e] + s_ppre[e]; the owner of chunk j is
+    // the largest e with that sum <= j
     int lo = 0, hi = E_local - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= j) lo = mid; else hi = mid - 1;
+      const int before = __builtin_amdgcn_readfirstlane(s_fpre[mid] + s_ppre[mid]);
+      if (before <= j) lo = mid; else hi = mid - 1;
     }
+    const int e = lo;
+    const int c = j - __builtin_amdgcn_readfirstlane(s_fpre[e] + s_ppre[e]);   // chunk of e
     int start, end;
-    expert_range(expert_ends, lo, A, M_cap, start, end);
-    T.e = lo;
-    T.r0 = start + (j - s_prefix[lo]) * kGemmBM;
+    expert_range(expert_ends, e, A, M_cap, start, end);
+    start = __builtin_amdgcn_readfirstlane(start);
+    end = __builtin_amdgcn_readfirstlane(end);
+    T.e = e;
+    T.r0 = start + c * kGemmBM;
     T.rows = min(kGemmBM, end - T.r0);                   // >= 1
     T.nblk = (T.rows + 15) >> 4;
     T.cb0 = nt * (kGemmBN / 16);
@@ -258,22 +293,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
     else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   };
 
-  int item = first;
-  bool valid = item < i_end;
+  int kc = 0;                            // the block's current item (k-th)
+  int item = item_at(0);
+  bool valid = item >= 0;
   GemmTile T{0, 0, 1, 1, 0, 0};
   if (valid) locate(item, T);
-  // the transfer walker: item pit, step pst, its sources; it runs 3 steps
+  // the transfer walker: item kp, step pst, its sources; it runs 3 steps
   // ahead of the compute and steps into the block's next item (or past the
   // last, into sources that read nothing) at an item's end
-  int pit = item, pst = 0;
+  int kp = 0, pst = 0;
   GemmSrc ps = sources(T, valid);
   auto advance = [&]() {
     if (++pst == KS) {
       pst = 0;
-      pit += nslot;
+      const int u = item_at(++kp);
       GemmTile U = T;
-      if (pit < i_end) locate(pit, U);
-      ps = sources(U, pit < i_end);
+      if (u >= 0) locate(u, U);
+      ps = sources(U, u >= 0);
     }
   };
   int gs = 0;                            // running k-step count; ring stage gs % 4
@@ -373,8 +409,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
     // stores and transfers share one counter and need not complete in
     // order: the next wait takes everything
     drain = true;
-    item += nslot;
-    valid = item < i_end;
+    item = item_at(++kc);
+    valid = item >= 0;
     if (valid) locate(item, T);
   }
   // every transfer this block issued has landed before its LDS is released
@@ -429,6 +465,8 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
   if ((long long)N * K / 2 >= (1LL << 31) || (long long)kGemmBM * K >= (1LL << 31) ||
       (long long)(K / 128) * M_cap * 4 >= (1LL << 31))
     return MOE_ERR_SHAPE;
+  // the in-kernel chunk scan packs full-chunk counts into 16 bits
+  if (M_cap / kGemmBM >= (1 << 16)) return MOE_ERR_SHAPE;
   if (E_local == 0 || M_cap == 0) return MOE_OK;
   if (!X || !Xs || !ends || !Wp || !Sp || !out) return MOE_ERR_NULL;
   // one resident block per CU; each walks its XCD's share of the item list

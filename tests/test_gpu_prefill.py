@@ -408,3 +408,54 @@ def test_prefill_group_full_size_gemms_sampled(ops):
         bm = M.block_max_bound(hq[rows], hb, w.w2[e], w.s2[e])
         ok, _, _ = gemm_within_bound(dn[rows], exact, tsum, c.I, bm)
         assert ok.all(), f"gemm2 expert {e}: {np.count_nonzero(~ok)} outside bound"
+
+
+# ------------------------------------------------- GEMM edge layouts
+
+def _gemm_edge_case(ops, counts, A, K, N, seed):
+    """Grouped GEMM on hand-made activations: experts with no rows, exactly one
+    full 128-row chunk, a full chunk plus one row, single rows, several chunks;
+    K of 1..3 k-steps (items shorter than the transfer ring), N with a partial
+    256-column tile. Every live row against the oracle, padding untouched."""
+    rng = np.random.default_rng(seed)
+    E = len(counts)
+    ends, prev = [], 0
+    for cnt in counts:
+        start = ((prev + A - 1) // A) * A
+        ends.append(start + cnt)
+        prev = start + cnt
+    M_cap = max(((prev + A - 1) // A) * A, A)
+    xq = rng.integers(0, 256, size=(M_cap, K), dtype=np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x3C                      # no E4M3 NaN codes
+    xsb = rng.integers(120, 131, size=(M_cap, K // 32), dtype=np.uint8)
+    xs = np.ascontiguousarray(F.pack_ue8m0_words(xsb).T)  # [K/128, M_cap]
+    w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ws = rng.integers(120, 131, size=(E, N, K // 32), dtype=np.uint8)
+    wp, sp = ops.moe_pack_mx_weights(dev(w), dev(ws))
+    out = torch.full((M_cap, N), BF16_SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ends_d = dev(np.asarray(ends, np.int32))
+    assert N % 2 == 0
+    ops.moe_grouped_gemm1(dev(xq), dev(xs), ends_d, A, wp, sp, out)
+    got = host(out)
+    live = np.zeros(M_cap, bool)
+    for e, rows in enumerate(_expert_rows(ends, A)):
+        if rows.size == 0:
+            continue
+        live[rows] = True
+        ab = xsb[rows]
+        _, exact, tsum = M.mx_gemm(xq[rows], ab, w[e], ws[e])
+        bm = M.block_max_bound(xq[rows], ab, w[e], ws[e])
+        ok, _, _ = gemm_within_bound(got[rows], exact, tsum, K, bm)
+        assert ok.all(), f"expert {e}: {np.count_nonzero(~ok)} of {ok.size} outside bound"
+    assert np.all(got[~live] == BF16_SENT)
+
+
+@pytest.mark.parametrize("K,N", [(128, 128), (256, 384), (384, 640), (1152, 256)])
+def test_gemm_edge_layouts(ops, K, N):
+    say(f"gemm edge layouts K={K} N={N}")
+    _gemm_edge_case(ops, [0, 128, 129, 1, 300, 0, 17], 128, K, N, seed=K + N)
+
+
+def test_gemm_all_empty_writes_nothing(ops):
+    say("gemm all-empty")
+    _gemm_edge_case(ops, [0, 0, 0], 128, 256, 256, seed=5)
