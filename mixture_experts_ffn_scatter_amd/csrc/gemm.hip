@@ -60,15 +60,32 @@
 
 namespace moe {
 
+#ifndef GEMM_DMA_SPREAD
+#define GEMM_DMA_SPREAD 1
+#endif
+#ifndef GEMM_HALF
+#define GEMM_HALF 0
+#endif
+#if GEMM_HALF
+// two independent 4-wave blocks per CU, each on its own 128-column item
+constexpr int kGemmThreads = 256;  // 4 waves
+constexpr int kGemmBN = 128;       // columns per item (8 blocks of 16)
+constexpr int kGemmStages = 3;     // LDS ring depth (k-steps)
+constexpr int kGemmBlocksPerCU = 2;
+#else
 constexpr int kGemmThreads = 512;  // 8 waves
-constexpr int kGemmBM = 128;       // rows per item (8 blocks of 16)
 constexpr int kGemmBN = 256;       // columns per item (16 blocks of 16)
+constexpr int kGemmStages = 4;     // LDS ring depth (k-steps)
+constexpr int kGemmBlocksPerCU = 1;
+#endif
+constexpr int kGemmWaves = kGemmThreads / 64;
+constexpr int kGemmBM = 128;       // rows per item (8 blocks of 16)
 constexpr int kGemmCB = 4;         // column blocks per wave (MFMA)
 constexpr int kGemmMB = 4;         // row blocks per wave (MFMA)
 constexpr int kGemmRG = kGemmBM / 16 / kGemmMB;         // row groups of waves
 constexpr int kGemmCG = kGemmBN / 16 / kGemmCB;         // column groups of waves
-constexpr int kDmaCB = 2;          // weight chunks each wave transfers per step
-constexpr int kGemmStages = 4;     // LDS ring depth (k-steps)
+constexpr int kDmaCB = kGemmBN / 16 / kGemmWaves;      // weight chunks a wave transfers per step
+constexpr int kDmaXR = kGemmBM / 16 / kGemmWaves;      // activation row blocks a wave transfers
 #ifndef GEMM_RD
 #define GEMM_RD 3
 #endif
@@ -76,7 +93,12 @@ constexpr int kGemmRD = GEMM_RD;   // activation fragments in registers (read-ah
 constexpr int kGemmMaxE = 1024;
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: reads zero, no traffic
 static_assert(kGemmRG * kGemmCG == kGemmThreads / 64, "wave grid");
-static_assert(kDmaCB * (kGemmThreads / 64) == kGemmBN / 16, "each wave transfers 2 weight chunks");
+static_assert(kDmaCB * kGemmWaves == kGemmBN / 16 && kDmaXR * kGemmWaves == kGemmBM / 16,
+              "transfers split evenly over the waves");
+static_assert(kGemmWaves >= 3, "waves 0, 1 move the scale words, wave 2 the weight scales");
+// transfers a wave issues per step: its weight chunks, 2 halves of each of
+// its row blocks, plus one scale transfer on waves 0-2
+constexpr int kDmaOps = kDmaCB + 2 * kDmaXR;
 
 // One LDS stage: everything one k-step of a 128 x 256 tile reads.
 //   x[mb][h]: activations of rows 16mb.. in B-fragment order (lane l: 16 bytes
@@ -142,19 +164,20 @@ struct GemmTile {
 struct GemmSrc {
   __amdgpu_buffer_rsrc_t wr, sr, xr, xsr;
   uint32_t wo[kDmaCB];   // per-lane weight-code offsets of the wave's transferred blocks
-  uint32_t xo;           // per-lane activation offset of this wave's row block
+  uint32_t xo;           // per-lane activation offset of this wave's first row block
   uint32_t xso;          // per-lane scale-word offset (waves 0, 1: rows 64 w + lane)
   uint32_t so;           // per-lane weight-scale offset (wave 2: the tile's 1 KB line)
 };
 
-__global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
+__global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gemm_kernel(
     const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
     const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int K, int N,
     const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out) {
   __shared__ GemmStage stage[kGemmStages];
-  __shared__ int s_fpre[kGemmMaxE + 1];
-  __shared__ int s_ppre[kGemmMaxE + 1];
-  __shared__ int s_tmp[kGemmThreads / 64];
+  // per expert: full chunks before it (low 16 bits), partial chunks before
+  // it (high 16 bits)
+  __shared__ int s_pre[kGemmMaxE + 1];
+  __shared__ int s_tmp[kGemmWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -168,54 +191,43 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
   const int NT = (N + kGemmBN - 1) / kGemmBN;
 
   // chunks per expert: full 128-row chunks and at most one partial one, and
-  // the exclusive scans of both (2 experts per thread)
-  int nf[2], np_[2];
-  int fsum = 0, psum = 0;
+  // the exclusive scan of both, packed: fulls in the low 16 bits, partials
+  // in the high (at most 1024 experts; the host caps M_cap / 128 < 2^16)
+  constexpr int kEPT = kGemmMaxE / kGemmThreads;   // experts per thread
+  int cnt[kEPT];
+  int local_sum = 0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = tid * 2 + j;
-    nf[j] = np_[j] = 0;
+  for (int j = 0; j < kEPT; ++j) {
+    const int e = tid * kEPT + j;
+    cnt[j] = 0;
     if (e < E_local) {
       int st, en;
       expert_range(expert_ends, e, A, M_cap, st, en);
-      nf[j] = (en - st) / kGemmBM;
-      np_[j] = (en - st) % kGemmBM != 0;
+      cnt[j] = (en - st) / kGemmBM | (((en - st) % kGemmBM != 0) << 16);
     }
-    fsum += nf[j];
-    psum += np_[j];
+    local_sum += cnt[j];
   }
-  // both scans in one pass: fulls in the low 16 bits, partials in the high
-  // (at most 1024 experts x (M_cap / 128) chunks; the host caps M_cap)
-  int run = block_exclusive_scan(fsum | (psum << 16), s_tmp);
+  int run = block_exclusive_scan(local_sum, s_tmp);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = tid * 2 + j;
-    if (e < E_local) {
-      s_fpre[e] = run & 0xFFFF;
-      s_ppre[e] = run >> 16;
-    }
-    run += nf[j] | (np_[j] << 16);
+  for (int j = 0; j < kEPT; ++j) {
+    const int e = tid * kEPT + j;
+    if (e < E_local) s_pre[e] = run;
+    run += cnt[j];
   }
-  if (tid == kGemmThreads - 1) {
-    s_fpre[E_local] = run & 0xFFFF;
-    s_ppre[E_local] = run >> 16;
-  }
+  if (tid == kGemmThreads - 1) s_pre[E_local] = run;
   __syncthreads();
   // LDS and global values the whole block agrees on are made scalar
   // (readfirstlane), so the buffer resources built from them stay in SGPRs
-  const int F = __builtin_amdgcn_readfirstlane(s_fpre[E_local]);   // full chunks
-  const int P = __builtin_amdgcn_readfirstlane(s_ppre[E_local]);   // partial chunks
+  const int tot = __builtin_amdgcn_readfirstlane(s_pre[E_local]);
+  const int F = tot & 0xFFFF;            // full chunks over all experts
+  const int P = tot >> 16;               // partial chunks
   const int MT = F + P;                  // chunks of one n-tile
-  const int L = MT * NT;                 // items: u = nt * MT + j
+  const int L = MT * NT;                 // items
   if (MT == 0) return;                   // no live rows (uniform over the block)
 
   // this block's XCD range [i0, i1) of the item list (block b runs on XCD
-  // b % 8); the XCD's blocks take its items round-robin. Within an n-tile
-  // the chunks are listed expert by expert (the fulls of an expert, then its
-  // partial), so the m-chunks of one (expert, n-tile) run side by side on
-  // neighbouring blocks and share the weight slice in that XCD's L2, and
-  // heavy and light items run at the same time (MFMA-bound next to
-  // weight-streaming).
+  // b % 8); the XCD's blocks take its items round-robin, so neighbouring
+  // items run side by side.
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslot = gridDim.x >> 3;      // the grid is a multiple of 8
@@ -227,19 +239,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
     return u < i1 ? u : -1;
   };
 
+  // items are listed expert-major: expert e owns items [NT cb(e), NT cb(e+1))
+  // (cb(e): chunks of the experts before e), n-tile-major inside, so the
+  // items running at once on an XCD share their activation chunks (one
+  // expert, several n-tiles) and their weight slices (one n-tile, several
+  // m-chunks) in its L2
   auto locate = [&](int item, GemmTile& T) {
-    const int nt = item / MT;
-    const int j = item - nt * MT;
-    // chunks before expert e: s_fpre[e] + s_ppre[e]; the owner of chunk j is
-    // the largest e with that sum <= j
+    const int jq = item / NT;
     int lo = 0, hi = E_local - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      const int before = __builtin_amdgcn_readfirstlane(s_fpre[mid] + s_ppre[mid]);
-      if (before <= j) lo = mid; else hi = mid - 1;
+      const int pm = __builtin_amdgcn_readfirstlane(s_pre[mid]);
+      if ((pm & 0xFFFF) + (pm >> 16) <= jq) lo = mid; else hi = mid - 1;
     }
     const int e = lo;
-    const int c = j - __builtin_amdgcn_readfirstlane(s_fpre[e] + s_ppre[e]);   // chunk of e
+    const int pe = __builtin_amdgcn_readfirstlane(s_pre[e]);
+    const int pn = __builtin_amdgcn_readfirstlane(s_pre[e + 1]);
+    const int cb_e = (pe & 0xFFFF) + (pe >> 16);           // chunks before e
+    const int nch = (pn & 0xFFFF) + (pn >> 16) - cb_e;     // chunks of e (>= 1)
+    const int local = item - NT * cb_e;
+    const int nt = local / nch;
+    const int c = local - nt * nch;
     int start, end;
     expert_range(expert_ends, e, A, M_cap, start, end);
     start = __builtin_amdgcn_readfirstlane(start);
@@ -262,7 +282,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
       const int cb = kDmaCB * wid + c;
       q.wo[c] = (live && cb < T.ncb) ? (uint32_t)(cb * KS) * 1024u + lane * 16 : kOob;
     }
-    q.xo = (live && 16 * wid < T.rows) ? (uint32_t)(16 * wid + l16) * (uint32_t)K + 16 * g : kOob;
+    q.xo = (live && 16 * kDmaXR * wid < T.rows)
+               ? (uint32_t)(16 * kDmaXR * wid + l16) * (uint32_t)K + 16 * g : kOob;
     q.xso = (live && 64 * wid < T.rows) ? (uint32_t)(64 * wid + lane) * 4u : kOob;
     q.so = live ? (uint32_t)T.cb0 * 64u + lane * 16 : kOob;
     return q;
@@ -272,25 +293,46 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
   // transfers of k-step st of a source into ring stage sg: per wave its 2
   // weight blocks and the 2 halves of its activation row block; waves 0, 1
   // the scale words of rows 64 w .. 64 w + 63, wave 2 the weight-scale line
-  auto issue = [&](const GemmSrc& q, int st, int sg) {
+  auto issue_op = [&](const GemmSrc& q, int st, int sg, auto kk) {
+    constexpr int k = decltype(kk)::value;
     const uint32_t base = lds0 + (uint32_t)sg * (uint32_t)sizeof(GemmStage);
-#pragma unroll
-    for (int c = 0; c < kDmaCB; ++c)
-      dma16(q.wr, q.wo[c] + (uint32_t)st * 1024u, base + kOffW + (kDmaCB * wid + c) * 1024);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      dma16(q.xr, q.xo + (uint32_t)st * 128u + 64 * h, base + wid * 2048 + h * 1024);
-    if (wid < 2) dma4(q.xsr, q.xso + (uint32_t)(st * M_cap) * 4u, base + kOffXs + wid * 256);
-    else if (wid == 2) dma16(q.sr, q.so + (uint32_t)(st * NB) * 64u, base + kOffWs);
+    if constexpr (k < kDmaCB) {
+      dma16(q.wr, q.wo[k] + (uint32_t)st * 1024u, base + kOffW + (kDmaCB * wid + k) * 1024);
+    } else if constexpr (k < kDmaOps) {
+      constexpr int r = (k - kDmaCB) / 2, h = (k - kDmaCB) % 2;
+      dma16(q.xr, q.xo + (uint32_t)(16 * r) * (uint32_t)K + (uint32_t)st * 128u + 64 * h,
+            base + (kDmaXR * wid + r) * 2048 + h * 1024);
+    } else {
+      if (wid < 2) {
+        dma4(q.xsr, q.xso + (uint32_t)(st * M_cap) * 4u, base + kOffXs + wid * 256);
+      } else if (wid == 2) {
+        // the tile's weight-scale line: 64 bytes per column block
+        if (kGemmBN / 16 * 4 >= 64 || lane < kGemmBN / 16 * 4)
+          dma16(q.sr, q.so + (uint32_t)(st * NB) * 64u, base + kOffWs);
+      }
+    }
+  };
+  auto issue = [&](const GemmSrc& q, int st, int sg) {
+    issue_op(q, st, sg, std::integral_constant<int, 0>{});
+    issue_op(q, st, sg, std::integral_constant<int, 1>{});
+    issue_op(q, st, sg, std::integral_constant<int, 2>{});
+    issue_op(q, st, sg, std::integral_constant<int, 3>{});
+    issue_op(q, st, sg, std::integral_constant<int, 4>{});
+    if constexpr (kDmaOps + 1 > 5) issue_op(q, st, sg, std::integral_constant<int, 5>{});
+    if constexpr (kDmaOps + 1 > 6) issue_op(q, st, sg, std::integral_constant<int, 6>{});
+    static_assert(kDmaOps + 1 <= 7, "issue covers up to 7 transfers");
   };
   // waits until this wave's transfers of the oldest stage in flight have
-  // landed: two stages (5 transfers per step on waves 0-2, 4 on the others)
-  // were issued after it, unless stores intervened (drain: wait for all)
-  static_assert(kGemmStages == 4, "wait counts assume two stages issued after the awaited one");
+  // landed: kGemmStages - 2 stages (kDmaOps + 1 transfers per step on waves
+  // 0-2, kDmaOps on the others) were issued after it, unless stores
+  // intervened (drain: wait for all)
+  constexpr int kWaitA = (kGemmStages - 2) * (kDmaOps + 1);
+  constexpr int kWaitB = (kGemmStages - 2) * kDmaOps;
+  static_assert(kWaitA < 64, "vmcnt field");
   auto wait_stage = [&](bool drain) {
     if (drain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (wid < 3) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (wid < 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitA) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitB) : "memory");
   };
 
   int kc = 0;                            // the block's current item (k-th)
@@ -370,8 +412,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
       for (int i = 0; i < kGemmRD - 1; ++i) read_b(i);
       // transfers of the walker's step (3 ahead) into the stage the
       // previous step used
-      issue(ps, pst, (gs + kGemmStages - 1) % kGemmStages);
-      advance();
+      const int sg = (gs + kGemmStages - 1) % kGemmStages;
+#if !GEMM_DMA_SPREAD
+      issue(ps, pst, sg);
+#endif
 #pragma unroll
       for (int i = 0; i < kGemmMB; ++i) {
         if (i + kGemmRD - 1 < kGemmMB) read_b(i + kGemmRD - 1);
@@ -382,7 +426,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_mx_gemm_kernel(
             acc[c][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 af[c].xyzwxyzw, bf[i % kGemmRD], acc[c][i], 4, 0, 0, sa[c], 0, sb);
         }
+#if GEMM_DMA_SPREAD
+        // two transfers after each row block's MFMAs, so the block's
+        // transfers spread over the step instead of queueing at its start
+        if (i == 0) {
+          issue_op(ps, pst, sg, std::integral_constant<int, 0>{});
+          issue_op(ps, pst, sg, std::integral_constant<int, 1>{});
+        } else if (i == 1) {
+          issue_op(ps, pst, sg, std::integral_constant<int, 2>{});
+          issue_op(ps, pst, sg, std::integral_constant<int, 3>{});
+        } else if (i == 2) {
+          issue_op(ps, pst, sg, std::integral_constant<int, 4>{});
+          if constexpr (kDmaOps + 1 > 5) issue_op(ps, pst, sg, std::integral_constant<int, 5>{});
+        } else if (i == 3) {
+          if constexpr (kDmaOps + 1 > 6) issue_op(ps, pst, sg, std::integral_constant<int, 6>{});
+        }
+#endif
       }
+      advance();
       ++gs;
     };
     if (mlive == kGemmMB) {
@@ -472,7 +533,8 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
   // one resident block per CU; each walks its XCD's share of the item list
   const int NT = (N + kGemmBN - 1) / kGemmBN;
   const long long max_items = (long long)((M_cap + kGemmBM - 1) / kGemmBM + E_local) * NT;
-  int grid = max_items < 256 ? (int)max_items : 256;
+  const int resident = 256 * kGemmBlocksPerCU;
+  int grid = max_items < resident ? (int)max_items : resident;
   grid = (grid + 7) & ~7;
   hipLaunchKernelGGL(grouped_mx_gemm_kernel, dim3(grid), dim3(kGemmThreads), 0,
                      (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, Wp, Sp, out);
