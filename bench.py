@@ -79,6 +79,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--unfused", action="store_true",
+                   help="time GEMM1 and the live-row act-quant as two launches")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run 4 plain 1 GiB device copies (the reference kernel that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -133,8 +135,11 @@ def main():
     x = up_bf16(c.x)
     logits_group = up(c.logits)
     logits_own = up(c.logits[: c.own_tokens])
-    # load-time weight preparation: codes and scales into the GEMMs' fragment order
-    w13, s13 = ops.moe_pack_mx_weights(up(w.w13), up(w.s13))
+    # load-time weight preparation: codes and scales into the GEMMs' fragment
+    # order (w13 with gate / up interleaved for the fused GEMM1 + act-quant)
+    fused = not args.unfused
+    pack13 = ops.moe_pack_mx_weights_gateup if fused else ops.moe_pack_mx_weights
+    w13, s13 = pack13(up(w.w13), up(w.s13))
     w2, s2 = ops.moe_pack_mx_weights(up(w.w2), up(w.s2))
     # the group's routes (every rank routes its own 512 tokens; the 4096
     # tokens' ids are what this GPU receives)
@@ -143,6 +148,9 @@ def main():
     own_w = torch.empty((c.own_tokens, c.k), dtype=torch.float32, device=dev)
     buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I)
     torch.cuda.synchronize()
+
+    names = (["route", "scatter", "gemm1_act", "gemm2", "combine"] if fused else
+             ["route", "scatter", "gemm1", "act_quant", "gemm2", "combine"])
 
     def step(ev=None):
         def mark(i):
@@ -154,20 +162,25 @@ def main():
         ops.moe_scatter_endpoints(ids, 0, c.E_local, c.A, x, buf.expert_ends, buf.route_row,
                                   buf.xq, buf.xs, buf.workspace)
         mark(2)
-        ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13, buf.gateup)
-        mark(3)
-        ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, 0.0, buf.hq, buf.hs)
-        mark(4)
+        if fused:
+            ops.moe_grouped_gemm1_act_quant(buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13, 0.0,
+                                            buf.hq, buf.hs)
+        else:
+            ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13, buf.gateup)
+            mark(3)
+            ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, 0.0, buf.hq, buf.hs)
+        mark(len(names) - 2)
         ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, w2, s2, buf.down)
-        mark(5)
+        mark(len(names) - 1)
         ops.moe_combine(buf.down, buf.route_row, wts, c.routed_scale, buf.out)
-        mark(6)
+        mark(len(names))
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -175,7 +188,6 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    names = ["route", "scatter", "gemm1", "act_quant", "gemm2", "combine"]
     dur_us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in
                                 range(args.steps)])) * 1e3 for j, n in enumerate(names)}
     log(f"eager ms/step {ms_per_step:.4f}", {k: round(v, 2) for k, v in dur_us.items()})
@@ -211,10 +223,11 @@ def main():
         "scatter": U_tok * H * 2 + R * (H + H // 32) + T * k * 8 + 4 * c.E_local,
         "gemm1": E_ne * (2 * I * H // 2 + 2 * I * H // 32) + R * (H + H // 32) + R * 2 * I * 2,
         "act_quant": R * (2 * I * 2 + I + I // 32) + 4 * c.E_local,
+        "gemm1_act": E_ne * (2 * I * H // 2 + 2 * I * H // 32) + R * (H + H // 32) + R * (I + I // 32),
         "gemm2": E_ne * (H * I // 2 + H * I // 32) + R * (I + I // 32) + R * H * 2,
         "combine": R * H * 2 + T * k * 8 + T * H * 2,
     }
-    flops = {"gemm1": 2.0 * R * 2 * I * H, "gemm2": 2.0 * R * H * I}
+    flops = {"gemm1": 2.0 * R * 2 * I * H, "gemm1_act": 2.0 * R * 2 * I * H, "gemm2": 2.0 * R * H * I}
     kernels = {}
     for n in names:
         t = dur_us[n] * 1e-6
@@ -226,9 +239,11 @@ def main():
             kernels[n].update({"flop": flops[n], "TFLOPs": round(tf, 1),
                                "mfma_frac_fp8_peak": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
                                "mfma_frac_fp4_peak": round(tf / FP4_MFMA_PEAK_TFLOPS, 4)})
-    dom = "gemm1"
+    dom = "gemm1_act" if fused else "gemm1"
     ach = bytes_[dom] / (dur_us[dom] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "grouped_mx_gemm_kernel (moe_grouped_gemm1)",
+    roofline = {"bound": "hbm",
+                "kernel": ("grouped_mx_gemm_kernel<true> (moe_grouped_gemm1_act_quant)" if fused
+                           else "grouped_mx_gemm_kernel<false> (moe_grouped_gemm1)"),
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
                 "alg_bytes_per_launch": int(bytes_[dom]), "avg_launch_us": round(dur_us[dom], 3)}

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 enum moe_status {
     MOE_OK = 0,
@@ -174,6 +174,48 @@ int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_star
  * ------------------------------------------------------------------------ */
 int moe_pack_mx_weights(const uint8_t* w, const uint8_t* w_scale, int E, int N, int K,
                         uint8_t* w_packed, uint8_t* w_scale_packed, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_pack_mx_weights_gateup - moe_pack_mx_weights for the fused GEMM1 +
+ * activation path: the same code and scale layouts, with the column blocks
+ * of w13 reordered so that each 256-column group holds the gate blocks of
+ * one 128-column slice of h and their up blocks, interleaved two by two.
+ * [SGL] section 2.1 (load-time weight preparation into the layout the
+ * kernel consumes) and 2.4 (activation and quantisation fused).
+ *
+ *   w13, w13_scale  as for moe_pack_mx_weights with N = 2I, K = H
+ *   w_packed, w_scale_packed  out, sizes as for moe_pack_mx_weights; packed
+ *                   column block p = 16t + 4c + k holds source block
+ *                   8t + 2c + k (gate) for k < 2 and I/16 + 8t + 2c + k - 2
+ *                   (up) for k >= 2
+ * Requires I % 128 == 0 and the conditions of moe_pack_mx_weights.
+ * ------------------------------------------------------------------------ */
+int moe_pack_mx_weights_gateup(const uint8_t* w13, const uint8_t* w13_scale, int E, int I,
+                               int H, uint8_t* w_packed, uint8_t* w_scale_packed, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_gemm1_act_quant - moe_grouped_gemm1 followed by
+ * moe_act_quant_liverows in one kernel: the gate/up products of each live
+ * row are rounded to bf16 (the gateup values moe_grouped_gemm1 would
+ * store), then SiLU(gate)*up is formed and quantised to E4M3 + UE8M0
+ * exactly as moe_act_quant_liverows does on those bf16 values, so hq and
+ * hs are byte-identical to the two-call path; gateup never reaches memory.
+ * [SGL] section 2.4 (act + quant fused, gate/up read once); [LIVE]
+ * sections 1-3 (live rows only, padding untouched).
+ *
+ *   xq, xs, expert_ends, E_local, A, M_cap, H, I  as for moe_grouped_gemm1
+ *   w13_gateup_packed, w13_gateup_scale_packed  moe_pack_mx_weights_gateup
+ *                of w13 and its scales
+ *   clamp_limit  as for moe_act_quant_liverows
+ *   hq, hs       as for moe_act_quant_liverows (out, live rows only)
+ * Requires I % 128 == 0, M_cap * I < 2^31 and the conditions of
+ * moe_grouped_gemm1.
+ * ------------------------------------------------------------------------ */
+int moe_grouped_gemm1_act_quant(const uint8_t* xq, const int32_t* xs, const int32_t* expert_ends,
+                                int E_local, int A, int M_cap, int H, int I,
+                                const uint8_t* w13_gateup_packed,
+                                const uint8_t* w13_gateup_scale_packed, float clamp_limit,
+                                uint8_t* hq, int32_t* hs, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_grouped_gemm1 - gate/up projection of every live row with its expert's

@@ -33,6 +33,9 @@ namespace moe {
 // sigma(g) for every bf16 g, generated at build time (gen_sigmoid_table.cpp)
 #define MOE_SIGMOID_TABLE_STORAGE __device__ const __attribute__((aligned(16)))
 #include "sigmoid_table.inc"
+}  // namespace moe
+#include "sigmoid_lookup.h"
+namespace moe {
 
 constexpr int kActThreads = 512;   // 8 waves
 constexpr int kActWaves = kActThreads / 64;
@@ -41,15 +44,6 @@ constexpr int kActMaxE = 1024;
 constexpr int kActMaxWordsPerRow = 64;  // I <= 8192
 constexpr int kActMaxRowsPerBlock = 2048;  // live rows per block (M_cap <= 256 * 2048)
 constexpr uint32_t kActOob = 0x80000000u;
-
-__device__ __forceinline__ float sigmoid_lookup(const float* tab, float g) {
-  const uint32_t bits = __float_as_uint(g) >> 16;  // g is an exact bf16 value
-  uint32_t a = bits & 0x7FFFu;
-  a = min(max(a, (uint32_t)(MOE_SIGMOID_EXP_LO << 7)), (uint32_t)((MOE_SIGMOID_EXP_HI << 7) | 127));
-  const uint32_t idx = a - (MOE_SIGMOID_EXP_LO << 7) +
-                       ((bits >> 15) ? (uint32_t)((MOE_SIGMOID_EXP_HI - MOE_SIGMOID_EXP_LO + 1) * 128) : 0u);
-  return tab[idx];
-}
 
 __device__ int act_block_scan(int v, int* tmp) {
   const int lane = threadIdx.x & 63;
@@ -190,7 +184,7 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
           gv = fminf(gv, L);
           uv = fminf(fmaxf(uv, -L), L);
         }
-        const float sig = sigmoid_lookup(s_tab, gv);
+        const float sig = sigmoid_lookup_table(s_tab, gv);
         const float sg = gv * sig;
         h[q] = sg * uv;
         amax = fmaxf(amax, fabsf(h[q]));

@@ -34,6 +34,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// both to bf16 with one hardware conversion (round to nearest even; NaN
+// handling is left to the caller): lo in the low half
+typedef __bf16 moe_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((moe_f32x2_t){lo, hi}, moe_bf16x2_t));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }

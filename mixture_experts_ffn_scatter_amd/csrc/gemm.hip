@@ -56,28 +56,29 @@
 // padding rows are never read.
 #include "common.h"
 
+#include <cstring>
 #include <type_traits>
+
+namespace moe {
+namespace gemm_act {
+// sigma(g) for every bf16 g (the activation kernel's table, generated at
+// build time; a private copy for the fused GEMM1 epilogue, read through L2)
+#define MOE_SIGMOID_TABLE_STORAGE static __device__ const __attribute__((aligned(16)))
+#include "sigmoid_table.inc"
+#undef MOE_SIGMOID_TABLE_STORAGE
+}  // namespace gemm_act
+}  // namespace moe
+#include "sigmoid_lookup.h"
 
 namespace moe {
 
 #ifndef GEMM_DMA_SPREAD
 #define GEMM_DMA_SPREAD 1
 #endif
-#ifndef GEMM_HALF
-#define GEMM_HALF 0
-#endif
-#if GEMM_HALF
-// two independent 4-wave blocks per CU, each on its own 128-column item
-constexpr int kGemmThreads = 256;  // 4 waves
-constexpr int kGemmBN = 128;       // columns per item (8 blocks of 16)
-constexpr int kGemmStages = 3;     // LDS ring depth (k-steps)
-constexpr int kGemmBlocksPerCU = 2;
-#else
 constexpr int kGemmThreads = 512;  // 8 waves
 constexpr int kGemmBN = 256;       // columns per item (16 blocks of 16)
 constexpr int kGemmStages = 4;     // LDS ring depth (k-steps)
 constexpr int kGemmBlocksPerCU = 1;
-#endif
 constexpr int kGemmWaves = kGemmThreads / 64;
 constexpr int kGemmBM = 128;       // rows per item (8 blocks of 16)
 constexpr int kGemmCB = 4;         // column blocks per wave (MFMA)
@@ -169,15 +170,35 @@ struct GemmSrc {
   uint32_t so;           // per-lane weight-scale offset (wave 2: the tile's 1 KB line)
 };
 
+// The fused GEMM1 epilogue (ACT): the weights are packed with the gate and
+// up column blocks of each 128-column slice of h interleaved (tile nt holds
+// gate blocks 8nt..8nt+7 and the matching up blocks), so the wave of
+// column group cg holds gate blocks 2cg, 2cg+1 in acc[0..1] and their up
+// blocks in acc[2..3]. It rounds both to bf16 (what GEMM1 would store),
+// forms h = SiLU(g) * u and quantises one 32-column group per row exactly as
+// moe_act_quant_liverows does with those bf16 inputs, and writes hq / hs.
+struct GemmActOut {
+  uint8_t* hq;       // [M_cap, I] E4M3
+  int32_t* hs;       // [I/128, M_cap] packed UE8M0 words
+  int I;
+  float L;           // clamp limit (> 0: clamp)
+};
+
+static_assert(kGemmBN == 256 && kGemmCB == 4, "the fused epilogue pairs 2 gate and 2 up blocks per wave");
+
+template <bool ACT>
 __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gemm_kernel(
     const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
     const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int K, int N,
-    const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out) {
+    const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out,
+    GemmActOut act) {
   __shared__ GemmStage stage[kGemmStages];
   // per expert: full chunks before it (low 16 bits), partial chunks before
   // it (high 16 bits)
   __shared__ int s_pre[kGemmMaxE + 1];
   __shared__ int s_tmp[kGemmWaves];
+  // the fused epilogue's sigmoid values (the compact subset of the table)
+  __shared__ __attribute__((aligned(16))) float s_sig[ACT ? kSigRows * 128 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -188,6 +209,11 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   const int g = lane >> 4;
   const int KS = K / 128;                // k-steps
   const int NB = N / 16;                 // column blocks
+  if constexpr (ACT) {
+    // published by the barriers of the chunk scan below
+    const float* tab = reinterpret_cast<const float*>(gemm_act::g_sigmoid_table);
+    for (int i = tid; i < kSigRows * 128; i += kGemmThreads) s_sig[i] = tab[sigmoid_compact_source(i)];
+  }
   const int NT = (N + kGemmBN - 1) / kGemmBN;
 
   // chunks per expert: full 128-row chunks and at most one partial one, and
@@ -324,14 +350,12 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   };
   // waits until this wave's transfers of the oldest stage in flight have
   // landed: kGemmStages - 2 stages (kDmaOps + 1 transfers per step on waves
-  // 0-2, kDmaOps on the others) were issued after it, unless stores
-  // intervened (drain: wait for all)
+  // 0-2, kDmaOps on the others) were issued after it
   constexpr int kWaitA = (kGemmStages - 2) * (kDmaOps + 1);
   constexpr int kWaitB = (kGemmStages - 2) * kDmaOps;
   static_assert(kWaitA < 64, "vmcnt field");
-  auto wait_stage = [&](bool drain) {
-    if (drain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (wid < 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitA) : "memory");
+  auto wait_stage = [&]() {
+    if (wid < 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitA) : "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitB) : "memory");
   };
 
@@ -361,7 +385,6 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       advance();
     }
   }
-  bool drain = false;
   while (valid) {
     // this wave's live row blocks among its kGemmMB
     const int mlive = min(max(T.nblk - kGemmMB * rg, 0), kGemmMB);
@@ -378,8 +401,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       constexpr bool FULL = decltype(full)::value;
       // stage gs complete for this wave, then (barrier) for the block; the
       // barrier also retires every read of the stage refilled below
-      wait_stage(drain);
-      drain = false;
+      wait_stage();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       const GemmStage& S = stage[gs % kGemmStages];
@@ -452,24 +474,94 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       for (int ks = 0; ks < KS; ++ks) step(std::false_type{});
     }
 
-    // epilogue: lane holds columns 16cb + 4g .. +3 of row r0 + 16mb + l16
+    if constexpr (!ACT) {
+      // epilogue: lane holds columns 16cb + 4g .. +3 of row r0 + 16mb + l16
 #pragma unroll
-    for (int c = 0; c < kGemmCB; ++c) {
-      const int cb = kGemmCB * cg + c;
-      if (cb >= T.ncb) continue;
-      const int n = (T.cb0 + cb) * 16 + 4 * g;
+      for (int c = 0; c < kGemmCB; ++c) {
+        const int cb = kGemmCB * cg + c;
+        if (cb >= T.ncb) continue;
+        const int n = (T.cb0 + cb) * 16 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < kGemmMB; ++i) {
+          const int mr = 16 * (kGemmMB * rg + i) + l16;
+          if (i >= mlive || mr >= T.rows) continue;
+          const v4f v = acc[c][i];
+          const uint2 o = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+          *reinterpret_cast<uint2*>(out + (size_t)(T.r0 + mr) * N + n) = o;
+        }
+      }
+    } else {
+      // fused activation: lane holds h columns 32cg + 16c + 4g .. +3 (c = 0, 1)
+      // of row r0 + 16mb + l16 of the 128-column slice nt = cb0 / 16
+      const int nt = T.cb0 >> 4;
 #pragma unroll
       for (int i = 0; i < kGemmMB; ++i) {
+        if (i >= mlive) continue;                            // wave-uniform
         const int mr = 16 * (kGemmMB * rg + i) + l16;
-        if (i >= mlive || mr >= T.rows) continue;
-        const v4f v = acc[c][i];
-        const uint2 o = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-        *reinterpret_cast<uint2*>(out + (size_t)(T.r0 + mr) * N + n) = o;
+        // gate and up rounded to bf16 (RNE, NaN -> the quiet NaN 0x7FC0: the
+        // values moe_grouped_gemm1 stores), two per conversion
+        float gv[8], uv[8];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const v4f g4 = acc[c][i], u4 = acc[c + 2][i];
+          const float ga[4] = {g4.x, g4.y, g4.z, g4.w};
+          const float ua[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = bf16x2_rne_bits(ga[q], ua[q]);
+            gv[4 * c + q] = ga[q] != ga[q] ? __uint_as_float(0x7FC00000u) : __uint_as_float(w << 16);
+            uv[4 * c + q] = ua[q] != ua[q] ? __uint_as_float(0x7FC00000u) : __uint_as_float(w & 0xFFFF0000u);
+          }
+        }
+        if (act.L > 0.f) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            gv[q] = fminf(gv[q], act.L);
+            uv[q] = fminf(fmaxf(uv[q], -act.L), act.L);
+          }
+        }
+        float sig[8];
+        bool small = false;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          sig[q] = sigmoid_lookup_compact_fast(s_sig, gv[q]);
+          small |= sigmoid_is_small(gv[q]);
+        }
+        if (__builtin_amdgcn_ballot_w64(small)) {                 // rare: |g| < 2^-15
+#pragma unroll
+          for (int q = 0; q < 8; ++q) sig[q] = sigmoid_small_fix(gv[q], sig[q]);
+        }
+        float h[2][4];
+        float amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float sg = gv[q] * sig[q];
+          h[q >> 2][q & 3] = sg * uv[q];
+          amax = fmaxf(amax, fabsf(h[q >> 2][q & 3]));
+        }
+        // the 32-column group of this row spans lanes l16 + 16 g'
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const uint32_t bsc = ue8m0_ceil_byte(amax / 448.0f);
+        const float inv = e8m0_reciprocal(bsc);
+        if (mr < T.rows) {
+          const size_t row = (size_t)(T.r0 + mr);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            uint32_t w = 0;
+            w = cvt_e4m3x2<false>(h[c][0] * inv, h[c][1] * inv, w);
+            w = cvt_e4m3x2<true>(h[c][2] * inv, h[c][3] * inv, w);
+            *reinterpret_cast<uint32_t*>(act.hq + row * act.I + 128 * nt + 32 * cg + 16 * c + 4 * g) = w;
+          }
+          // byte cg of the row's scale word of slice nt (group 4 nt + cg)
+          if (g == 0)
+            reinterpret_cast<uint8_t*>(act.hs)[((size_t)nt * M_cap + row) * 4 + cg] = (uint8_t)bsc;
+        }
       }
     }
-    // stores and transfers share one counter and need not complete in
-    // order: the next wait takes everything
-    drain = true;
+    // (the stores above share the counter with the transfers; they may
+    // complete before older transfers, but the transfers complete in order,
+    // so counting transfers alone in wait_stage still waits for the stage)
     item = item_at(++kc);
     valid = item >= 0;
     if (valid) locate(item, T);
@@ -484,8 +576,19 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
 //   scales s [E][N][K/32] -> sp [E][K/128][N/16][64 lanes]
 //          byte l of line (e, ks, cb) = group 4ks + l/16 of row 16cb + l%16
 // One wave per 1 KB code chunk; one thread per scale byte.
+//
+// With half > 0 (the gate/up form of w13, half = I/16 gate column blocks)
+// packed column block p takes source block src_cb(p): in each group of 16
+// (one 256-column tile), position 4cg + k holds gate block 8nt + 2cg + k for
+// k < 2 and the matching up block half + 8nt + 2cg + (k - 2) for k >= 2.
+__device__ __forceinline__ int src_cb(int p, int half) {
+  if (half == 0) return p;
+  const int nt = p >> 4, l = p & 15, cg = l >> 2, k = l & 3;
+  return (k < 2 ? 0 : half) + 8 * nt + 2 * cg + (k & 1);
+}
+
 __global__ __launch_bounds__(256) void pack_mx_codes_kernel(const uint8_t* __restrict__ w, int N,
-                                                            int K, uint8_t* __restrict__ wp) {
+                                                            int K, int half, uint8_t* __restrict__ wp) {
   const int KS = K / 128;
   const size_t per_e = (size_t)(N / 16) * KS;
   const size_t chunk = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -494,14 +597,14 @@ __global__ __launch_bounds__(256) void pack_mx_codes_kernel(const uint8_t* __res
   const int lane = threadIdx.x & 63;
   const int cb = (int)(chunk / KS);
   const int ks = (int)(chunk - (size_t)cb * KS);
-  const size_t row = (size_t)e * N + 16 * cb + (lane & 15);
+  const size_t row = (size_t)e * N + 16 * src_cb(cb, half) + (lane & 15);
   const uint4 v =
       *reinterpret_cast<const uint4*>(w + row * (size_t)(K / 2) + 64 * ks + 16 * (lane >> 4));
   *reinterpret_cast<uint4*>(wp + ((size_t)e * per_e + chunk) * 1024 + lane * 16) = v;
 }
 
 __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ s, int N,
-                                                             int K, uint8_t* __restrict__ sp) {
+                                                             int K, int half, uint8_t* __restrict__ sp) {
   const int NB = N / 16;
   const size_t per_e = (size_t)(K / 128) * NB * 64;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -512,12 +615,13 @@ __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __re
   const int ks = (int)(line / NB);
   const int cb = (int)(line - (size_t)ks * NB);
   sp[(size_t)e * per_e + idx] =
-      s[((size_t)e * N + 16 * cb + (l & 15)) * (size_t)(K / 32) + 4 * ks + (l >> 4)];
+      s[((size_t)e * N + 16 * src_cb(cb, half) + (l & 15)) * (size_t)(K / 32) + 4 * ks + (l >> 4)];
 }
 
 static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_t* ends,
                                int E_local, int A, int M_cap, int K, int N, const uint8_t* Wp,
-                               const uint8_t* Sp, uint16_t* out, void* stream) {
+                               const uint8_t* Sp, uint16_t* out, void* stream,
+                               const GemmActOut* act = nullptr) {
   if (E_local < 0 || E_local > kGemmMaxE || A < 1 || M_cap < 0 || K <= 0 || N <= 0)
     return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
@@ -529,23 +633,26 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
   // the in-kernel chunk scan packs full-chunk counts into 16 bits
   if (M_cap / kGemmBM >= (1 << 16)) return MOE_ERR_SHAPE;
   if (E_local == 0 || M_cap == 0) return MOE_OK;
-  if (!X || !Xs || !ends || !Wp || !Sp || !out) return MOE_ERR_NULL;
+  if (!X || !Xs || !ends || !Wp || !Sp || (!out && !act)) return MOE_ERR_NULL;
   // one resident block per CU; each walks its XCD's share of the item list
   const int NT = (N + kGemmBN - 1) / kGemmBN;
   const long long max_items = (long long)((M_cap + kGemmBM - 1) / kGemmBM + E_local) * NT;
   const int resident = 256 * kGemmBlocksPerCU;
   int grid = max_items < resident ? (int)max_items : resident;
   grid = (grid + 7) & ~7;
-  hipLaunchKernelGGL(grouped_mx_gemm_kernel, dim3(grid), dim3(kGemmThreads), 0,
-                     (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, Wp, Sp, out);
+  if (act)
+    hipLaunchKernelGGL(grouped_mx_gemm_kernel<true>, dim3(grid), dim3(kGemmThreads), 0,
+                       (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, Wp, Sp, out, *act);
+  else
+    hipLaunchKernelGGL(grouped_mx_gemm_kernel<false>, dim3(grid), dim3(kGemmThreads), 0,
+                       (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, Wp, Sp, out,
+                       GemmActOut{nullptr, nullptr, 0, 0.f});
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
 
-}  // namespace moe
-
-extern "C" int moe_pack_mx_weights(const uint8_t* w, const uint8_t* w_scale, int E, int N, int K,
-                                   uint8_t* w_packed, uint8_t* w_scale_packed, void* stream) {
+static int pack_mx(const uint8_t* w, const uint8_t* w_scale, int E, int N, int K, int half,
+                   uint8_t* w_packed, uint8_t* w_scale_packed, void* stream) {
   if (E < 0 || N < 0 || K <= 0 || E > 65535) return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 16 != 0) return MOE_ERR_ALIGN;
   if (E == 0 || N == 0) return MOE_OK;
@@ -554,13 +661,27 @@ extern "C" int moe_pack_mx_weights(const uint8_t* w, const uint8_t* w_scale, int
   const size_t scale_bytes = (size_t)N * (K / 32);
   if ((chunks + 3) / 4 > 0x7fffffffu || (scale_bytes + 255) / 256 > 0x7fffffffu) return MOE_ERR_SHAPE;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(moe::pack_mx_codes_kernel, dim3((unsigned)((chunks + 3) / 4), (unsigned)E),
-                     dim3(256), 0, st, w, N, K, w_packed);
+  hipLaunchKernelGGL(pack_mx_codes_kernel, dim3((unsigned)((chunks + 3) / 4), (unsigned)E),
+                     dim3(256), 0, st, w, N, K, half, w_packed);
   MOE_CHECK_LAUNCH();
-  hipLaunchKernelGGL(moe::pack_mx_scales_kernel, dim3((unsigned)((scale_bytes + 255) / 256), (unsigned)E),
-                     dim3(256), 0, st, w_scale, N, K, w_scale_packed);
+  hipLaunchKernelGGL(pack_mx_scales_kernel, dim3((unsigned)((scale_bytes + 255) / 256), (unsigned)E),
+                     dim3(256), 0, st, w_scale, N, K, half, w_scale_packed);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" int moe_pack_mx_weights(const uint8_t* w, const uint8_t* w_scale, int E, int N, int K,
+                                   uint8_t* w_packed, uint8_t* w_scale_packed, void* stream) {
+  return moe::pack_mx(w, w_scale, E, N, K, 0, w_packed, w_scale_packed, stream);
+}
+
+extern "C" int moe_pack_mx_weights_gateup(const uint8_t* w13, const uint8_t* w13_scale, int E,
+                                          int I, int H, uint8_t* w_packed,
+                                          uint8_t* w_scale_packed, void* stream) {
+  if (I <= 0 || I % 128 != 0) return MOE_ERR_ALIGN;
+  return moe::pack_mx(w13, w13_scale, E, 2 * I, H, I / 16, w_packed, w_scale_packed, stream);
 }
 
 extern "C" int moe_grouped_gemm1(const uint8_t* xq, const int32_t* xs, const int32_t* expert_ends,
@@ -578,4 +699,31 @@ extern "C" int moe_grouped_gemm2(const uint8_t* hq, const int32_t* hs, const int
                                  uint16_t* down, void* stream) {
   return moe::launch_grouped_gemm(hq, hs, expert_ends, E_local, A, M_cap, I, H, w2_packed,
                                   w2_scale_packed, down, stream);
+}
+
+extern "C" int moe_grouped_gemm1_act_quant(const uint8_t* xq, const int32_t* xs,
+                                           const int32_t* expert_ends, int E_local, int A,
+                                           int M_cap, int H, int I,
+                                           const uint8_t* w13_gateup_packed,
+                                           const uint8_t* w13_gateup_scale_packed,
+                                           float clamp_limit, uint8_t* hq, int32_t* hs,
+                                           void* stream) {
+  if (I <= 0 || I % 128 != 0) return MOE_ERR_ALIGN;
+  // the clamp rule of moe_act_quant_liverows: L <= 0 or +inf: none; a finite
+  // L > 0 must be exactly representable in bf16; NaN is rejected
+  float L = 0.f;
+  if (clamp_limit > 0.f && clamp_limit < __builtin_inff()) {
+    uint32_t bits;
+    std::memcpy(&bits, &clamp_limit, 4);
+    if (bits & 0xFFFFu) return MOE_ERR_UNSUPPORTED;
+    L = clamp_limit;
+  } else if (!(clamp_limit <= 0.f) && !(clamp_limit == __builtin_inff())) {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if ((long long)M_cap * I >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (E_local > 0 && M_cap > 0 && (!hq || !hs)) return MOE_ERR_NULL;
+  const moe::GemmActOut act{hq, hs, I, L};
+  return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I,
+                                  w13_gateup_packed, w13_gateup_scale_packed, nullptr, stream,
+                                  &act);
 }

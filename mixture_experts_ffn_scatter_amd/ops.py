@@ -161,6 +161,42 @@ def moe_pack_mx_weights(w, w_scale):
     return wp, sp
 
 
+def moe_pack_mx_weights_gateup(w13, w13_scale):
+    """moe_pack_mx_weights for the fused GEMM1 + activation path: w13 u8
+    [E, 2I, H/2] and its scales -> the same packed shapes with the column
+    blocks of gate and up interleaved per 128-column slice of h."""
+    _req(w13, "w13", (torch.uint8,))
+    E, twoI, H2 = w13.shape
+    H = 2 * H2
+    _req(w13_scale, "w13_scale", (torch.uint8,), (E, twoI, H // 32))
+    wp = torch.empty_like(w13)
+    sp = torch.empty(packed_scale_shape(E, twoI, H), dtype=torch.uint8, device=w13.device)
+    st = lib().moe_pack_mx_weights_gateup(_ptr(w13), _ptr(w13_scale), E, twoI // 2, H, _ptr(wp),
+                                          _ptr(sp), _stream())
+    check(st, "moe_pack_mx_weights_gateup")
+    return wp, sp
+
+
+def moe_grouped_gemm1_act_quant(xq, xs, expert_ends, A: int, w13_gateup_packed,
+                                w13_gateup_scale_packed, clamp_limit: float, hq, hs):
+    M_cap, H = xq.shape
+    E_local, twoI, _ = w13_gateup_packed.shape
+    I = twoI // 2
+    _req(xq, "xq", (torch.uint8,))
+    _req(xs, "xs", (torch.int32,), (H // 128, M_cap))
+    _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
+    _req(w13_gateup_packed, "w13_gateup_packed", (torch.uint8,), (E_local, 2 * I, H // 2))
+    _req(w13_gateup_scale_packed, "w13_gateup_scale_packed", (torch.uint8,),
+         packed_scale_shape(E_local, 2 * I, H))
+    _req(hq, "hq", (torch.uint8,), (M_cap, I))
+    _req(hs, "hs", (torch.int32,), (I // 128, M_cap))
+    st = lib().moe_grouped_gemm1_act_quant(_ptr(xq), _ptr(xs), _ptr(expert_ends), E_local, A, M_cap,
+                                           H, I, _ptr(w13_gateup_packed),
+                                           _ptr(w13_gateup_scale_packed), float(clamp_limit),
+                                           _ptr(hq), _ptr(hs), _stream())
+    check(st, "moe_grouped_gemm1_act_quant")
+
+
 def moe_grouped_gemm1(xq, xs, expert_ends, A: int, w13_packed, w13_scale_packed, gateup):
     M_cap, H = xq.shape
     E_local, twoI, _ = w13_packed.shape
@@ -261,6 +297,23 @@ def moe_ffn_prefill(x, topk_ids, topk_weights, expert_start: int, A: int, w13_pa
     moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, A, w13_packed, w13_scale_packed,
                       buf.gateup)
     moe_act_quant_liverows(buf.gateup, buf.expert_ends, A, clamp_limit, buf.hq, buf.hs)
+    moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, A, w2_packed, w2_scale_packed, buf.down)
+    moe_combine(buf.down, buf.route_row, topk_weights, routed_scale, buf.out)
+    return buf.out
+
+
+def moe_ffn_prefill_fused(x, topk_ids, topk_weights, expert_start: int, A: int,
+                          w13_gateup_packed, w13_gateup_scale_packed, w2_packed, w2_scale_packed,
+                          buf: GroupedBuffers, clamp_limit: float = 0.0,
+                          routed_scale: float = 1.0):
+    """moe_ffn_prefill with GEMM1 and the live-row act-quant in one kernel
+    (w13 from moe_pack_mx_weights_gateup); byte-identical results, and the
+    bf16 gate/up rows (buf.gateup) are never written."""
+    E_local = w13_gateup_packed.shape[0]
+    moe_scatter_endpoints(topk_ids, expert_start, E_local, A, x, buf.expert_ends, buf.route_row,
+                          buf.xq, buf.xs, buf.workspace)
+    moe_grouped_gemm1_act_quant(buf.xq, buf.xs, buf.expert_ends, A, w13_gateup_packed,
+                                w13_gateup_scale_packed, clamp_limit, buf.hq, buf.hs)
     moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, A, w2_packed, w2_scale_packed, buf.down)
     moe_combine(buf.down, buf.route_row, topk_weights, routed_scale, buf.out)
     return buf.out

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     for s in range(0, -8, -1):
         assert lib.moe_status_string(s).decode()
     assert lib.moe_status_string(5).decode() == "unknown status"
@@ -119,3 +119,38 @@ def test_hip_side_sigmoid_table_equals_oracle(tmp_path):
     idx = (b >> 15) * rows * 128 + (np.clip(ex, lo, hi) - lo) * 128 + (b & 0x7F)
     want = F.sigmoid_f32(F.bf16_to_f32(b.astype(np.uint16))).view(np.uint32)
     assert np.array_equal(tab[idx], want)
+
+
+def test_compact_sigmoid_lookup_equals_full_table(tmp_path):
+    """The fused GEMM1 epilogue's compact sigmoid (rows 112..131 / 112..133 of
+    the table, 1/2 + g/4 rounded with ties toward 1/2 below |g| = 2^-15, 1.0 /
+    0.0 beyond the kept rows), restated here in the same IEEE operations,
+    equals the full table's lookup for every bf16 pattern (inf and NaN
+    included)."""
+    exe = tmp_path / "gen"
+    src = os.path.join(ROOT, "mixture_experts_ffn_scatter_amd", "csrc", "gen_sigmoid_table.cpp")
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-ffp-contract=off", src, "-o", str(exe)])
+    txt = subprocess.check_output([str(exe)], text=True)
+    lo = int(re.search(r"MOE_SIGMOID_EXP_LO (\d+)", txt).group(1))
+    hi = int(re.search(r"MOE_SIGMOID_EXP_HI (\d+)", txt).group(1))
+    tab = np.array([int(v, 16) for v in re.findall(r"0x([0-9a-f]{8})u", txt)], np.uint32)
+    rows = hi - lo + 1
+    b = np.arange(65536, dtype=np.uint32)
+    neg, ex, m = b >> 15, (b >> 7) & 0xFF, b & 0x7F
+    full = tab[neg * rows * 128 + (np.clip(ex, lo, hi) - lo) * 128 + m]
+    # the compact rule
+    pos_lo, pos_hi, neg_lo, neg_hi = 112, 131, 112, 133
+    g = (b << 16).view(np.float32)
+    out = np.empty(65536, np.uint32)
+    small = ex < pos_lo
+    q = (g[small] * np.float32(0.25)).astype(np.float64)
+    nudge = np.where(neg[small] == 1, 2.0 ** -50, -(2.0 ** -50))
+    out[small] = (0.5 + q + nudge).astype(np.float32).view(np.uint32)
+    p = (~small) & (neg == 0)
+    out[p] = np.where(ex[p] > pos_hi, np.float32(1.0).view(np.uint32),
+                      tab[(np.clip(ex[p], pos_lo, pos_hi) - lo) * 128 + m[p]])
+    n = (~small) & (neg == 1)
+    out[n] = np.where(ex[n] > neg_hi, np.uint32(0),
+                      tab[rows * 128 + (np.clip(ex[n], neg_lo, neg_hi) - lo) * 128 + m[n]])
+    bad = np.flatnonzero(out != full)
+    assert bad.size == 0, f"{bad.size} patterns differ, first {[hex(v) for v in bad[:8]]}"

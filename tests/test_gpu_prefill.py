@@ -459,3 +459,97 @@ def test_gemm_edge_layouts(ops, K, N):
 def test_gemm_all_empty_writes_nothing(ops):
     say("gemm all-empty")
     _gemm_edge_case(ops, [0, 0, 0], 128, 256, 256, seed=5)
+
+
+# ------------------------------------------------- fused GEMM1 + act-quant
+
+def _fused_vs_two_call(ops, xq, xs, ends, A, w13, s13, clamp):
+    """(hq, hs) of moe_grouped_gemm1_act_quant and of moe_grouped_gemm1 ->
+    moe_act_quant_liverows, both on sentinel-filled buffers."""
+    M_cap = xq.shape[0]
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    ends_d = dev(np.asarray(ends, np.int32))
+    wp, sp = ops.moe_pack_mx_weights(dev(w13), dev(s13))
+    gp, gs = ops.moe_pack_mx_weights_gateup(dev(w13), dev(s13))
+    gateup = torch.full((M_cap, twoI), BF16_SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    outs = []
+    for fused in (False, True):
+        hq = torch.full((M_cap, I), BYTE_SENT, dtype=torch.uint8, device="cuda")
+        hs = torch.full((I // 128, M_cap), int(WORD_SENT), dtype=torch.int32, device="cuda")
+        if fused:
+            ops.moe_grouped_gemm1_act_quant(dev(xq), dev(xs), ends_d, A, gp, gs, clamp, hq, hs)
+        else:
+            ops.moe_grouped_gemm1(dev(xq), dev(xs), ends_d, A, wp, sp, gateup)
+            ops.moe_act_quant_liverows(gateup, ends_d, A, clamp, hq, hs)
+        outs.append((host(hq), host(hs)))
+    return outs
+
+
+@pytest.mark.parametrize("I,clamp", [(128, 0.0), (256, 6.0), (384, 0.0)])
+def test_gemm1_act_quant_fused_equals_two_calls(ops, I, clamp):
+    """Byte-identical hq / hs against the two-call path on the edge layouts
+    (empty, exactly 128, 129, single-row and multi-chunk experts), padding
+    untouched; and the two-call path itself against the oracle's act-quant."""
+    say(f"fused gemm1+act-quant I={I} clamp={clamp}")
+    rng = np.random.default_rng(I)
+    A, H = 128, 256
+    counts = [0, 128, 129, 1, 300, 0, 17]
+    ends, prev = [], 0
+    for cnt in counts:
+        start = ((prev + A - 1) // A) * A
+        ends.append(start + cnt)
+        prev = start + cnt
+    M_cap = ((prev + A - 1) // A) * A
+    xq = rng.integers(0, 256, size=(M_cap, H), dtype=np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x3C
+    xsb = rng.integers(118, 128, size=(M_cap, H // 32), dtype=np.uint8)
+    xs = np.ascontiguousarray(F.pack_ue8m0_words(xsb).T)
+    w13 = rng.integers(0, 256, size=(len(counts), 2 * I, H // 2), dtype=np.uint8)
+    s13 = rng.integers(118, 128, size=(len(counts), 2 * I, H // 32), dtype=np.uint8)
+    (hq0, hs0), (hq1, hs1) = _fused_vs_two_call(ops, xq, xs, ends, A, w13, s13, clamp)
+    assert np.array_equal(hq0, hq1) and np.array_equal(hs0, hs1)
+    live = np.zeros(M_cap, bool)
+    for rows in _expert_rows(ends, A):
+        live[rows] = True
+    assert np.all(hq1[~live] == BYTE_SENT) and np.all(hs1[:, ~live] == WORD_SENT)
+
+
+def test_prefill_fused_chain_equals_unfused_full_size(ops):
+    """The prefill EP-share layer through moe_ffn_prefill_fused equals
+    moe_ffn_prefill byte for byte (down rows and combined output)."""
+    c = W.prefill()
+    w = c.weights
+    ids, wts = M.route_softmax(c.logits, c.k)
+    say("prefill fused chain vs unfused, full size")
+    outs = []
+    for fused in (False, True):
+        buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, fill=True)
+        w13p = (ops.moe_pack_mx_weights_gateup if fused else ops.moe_pack_mx_weights)(dev(w.w13), dev(w.s13))
+        w2p = ops.moe_pack_mx_weights(dev(w.w2), dev(w.s2))
+        fn = ops.moe_ffn_prefill_fused if fused else ops.moe_ffn_prefill
+        y = fn(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A, *w13p, *w2p, buf)
+        outs.append((host(buf.hq), host(buf.hs), host(buf.down), host(y)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_pack_mx_weights_gateup_permutation(ops):
+    """moe_pack_mx_weights_gateup equals moe_pack_mx_weights of w13 with its
+    16-row blocks reordered as documented (gate / up pairs per 128 columns)."""
+    rng = np.random.default_rng(77)
+    for E, I, H in ((2, 128, 256), (1, 384, 512)):
+        say(f"pack gateup E={E} I={I} H={H}")
+        w = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
+        s = rng.integers(0, 256, size=(E, 2 * I, H // 32), dtype=np.uint8)
+        src = []
+        for p in range(2 * I // 16):
+            t, l = divmod(p, 16)
+            c, k = divmod(l, 4)
+            src.append((8 * t + 2 * c + k) if k < 2 else (I // 16 + 8 * t + 2 * c + k - 2))
+        rows = (16 * np.asarray(src)[:, None] + np.arange(16)[None, :]).reshape(-1)
+        assert sorted(rows.tolist()) == list(range(2 * I))
+        gp, gs = ops.moe_pack_mx_weights_gateup(dev(w), dev(s))
+        rp, rs = ops.moe_pack_mx_weights(dev(np.ascontiguousarray(w[:, rows])),
+                                         dev(np.ascontiguousarray(s[:, rows])))
+        assert np.array_equal(host(gp), host(rp)) and np.array_equal(host(gs), host(rs))
