@@ -44,9 +44,10 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix peak
 # Counter-derived HBM traffic of the dominant kernel is taken from the
 # committed rocprofv3 summary; it is reported only while the kernel's sources
 # still hash to the value recorded when the counters were read.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_mx_gemm1_prefill_ep_share_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_mx_gemm1_act_quant_prefill_ep_share_hbm_traffic.txt")
 GEMM_SOURCES = ("mixture_experts_ffn_scatter_amd/csrc/gemm.hip",
-                "mixture_experts_ffn_scatter_amd/csrc/common.h")
+                "mixture_experts_ffn_scatter_amd/csrc/common.h",
+                "mixture_experts_ffn_scatter_amd/csrc/sigmoid_lookup.h")
 
 
 def gemm_source_hash() -> str:

@@ -37,10 +37,13 @@ def _logit_sets(c, n):
     return sets
 
 
-def test_prefill_chain_graph_replays_follow_new_routing(ops):
+@pytest.mark.parametrize("fused", [False, True])
+def test_prefill_chain_graph_replays_follow_new_routing(ops, fused):
     c = W.tiny()
     w = c.weights
-    w13p, s13p = ops.moe_pack_mx_weights(dev(w.w13), dev(w.s13))
+    pack13 = ops.moe_pack_mx_weights_gateup if fused else ops.moe_pack_mx_weights
+    prefill = ops.moe_ffn_prefill_fused if fused else ops.moe_ffn_prefill
+    w13p, s13p = pack13(dev(w.w13), dev(w.s13))
     w2p, s2p = ops.moe_pack_mx_weights(dev(w.w2), dev(w.s2))
     x = dev_bf16(c.x)
 
@@ -52,12 +55,12 @@ def test_prefill_chain_graph_replays_follow_new_routing(ops):
 
     def chain(logits, ids, wts, buf):
         ops.moe_route(logits, c.k, "softmax", None, ids, wts)
-        ops.moe_ffn_prefill(x, ids, wts, 0, c.A, w13p, s13p, w2p, s2p, buf)
+        prefill(x, ids, wts, 0, c.A, w13p, s13p, w2p, s2p, buf)
 
     g_logits, g_ids, g_wts, g_buf = buffers()
     e_logits, e_ids, e_wts, e_buf = buffers()
     g_logits.copy_(dev(c.logits))
-    say("capture the prefill chain")
+    say(f"capture the prefill chain (fused={fused})")
     graph = ops.capture_graph(lambda: chain(g_logits, g_ids, g_wts, g_buf))
     torch.cuda.synchronize()
     for r, lg in enumerate(_logit_sets(c, 4)):
