@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 enum moe_status {
     MOE_OK = 0,
@@ -164,10 +164,10 @@ int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_star
  *                   k-step ks = k/128 a 1 KB chunk at ((e*N/16 + cb)*K/128 + ks)*1024
  *                   whose 16 bytes at lane*16 are bytes [64ks + 16(lane/16), +16)
  *                   of row 16cb + lane%16
- *   w_scale_packed  u8, E*(K/128)*(N/16)*64 bytes (= E*N*K/32), out: for k-step
- *                   ks and column block cb a 64-byte line at
- *                   ((e*K/128 + ks)*N/16 + cb)*64 whose byte lane is the E8M0
- *                   byte of group 4ks + lane/16 of row 16cb + lane%16
+ *   w_scale_packed  u8, E*(K/128)*64*(N/16) bytes (= E*N*K/32), out: for k-step
+ *                   ks and lane l (0..63) a row of N/16 bytes at
+ *                   ((e*K/128 + ks)*64 + l)*N/16 whose byte cb is the E8M0
+ *                   byte of group 4ks + l/16 of row 16cb + l%16
  * Pure data movement (bit-exact). Requires K % 128 == 0, N % 16 == 0,
  * E <= 65535. The caller owns all four buffers; the packed buffers are what
  * moe_grouped_gemm1 / moe_grouped_gemm2 take.

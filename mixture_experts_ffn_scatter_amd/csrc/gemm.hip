@@ -27,9 +27,10 @@
 // (sglang)", section 2.1: weights are rearranged into the layout the GEMM
 // consumes, so that the run-time GEMM never touches the checkpoint layout):
 // codes are stored in MFMA fragment order, one contiguous 1 KB chunk per
-// (16-column block, 128-wide k-step), and scales as one 64-byte line per
-// (k-step, 16-column block) holding each lane's byte, so that one k-step of
-// a 256-column tile's scales is a single contiguous 1 KB run.
+// (16-column block, 128-wide k-step), and scales per (k-step, lane) as one
+// row of N/16 bytes (the byte lane l of the MFMA needs for each column
+// block), so that one k-step of a 256-column tile's scales is 16 contiguous
+// bytes per lane and a wave reads its 4 column blocks' scales as one word.
 //
 // Work decomposition. An item is (n-tile of 256 columns, expert, m-chunk of
 // up to 128 live rows). Items are listed n-tile-major and the list is cut
@@ -106,12 +107,12 @@ constexpr int kDmaOps = kDmaCB + 2 * kDmaXR;
 //             of row 16mb + l%16 at k 64h + 16(l/16))
 //   w[cb]:    weight codes of column block cb in A-fragment order
 //   xs[row]:  the row's 4 UE8M0 bytes (k-blocks 0..3 of the step)
-//   ws[cb]:   lane l's E8M0 byte of column block cb
+//   ws[l]:    lane l's E8M0 bytes of the tile's 16 column blocks
 struct __attribute__((aligned(16))) GemmStage {
   uint8_t x[kGemmBM / 16][2][1024];
   uint8_t w[kGemmBN / 16][1024];
   uint32_t xs[kGemmBM];
-  uint8_t ws[kGemmBN / 16][64];
+  uint8_t ws[64][kGemmBN / 16];
 };
 constexpr int kOffW = kGemmBM / 16 * 2 * 1024;
 constexpr int kOffXs = kOffW + kGemmBN / 16 * 1024;
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     q.xo = (live && 16 * kDmaXR * wid < T.rows)
                ? (uint32_t)(16 * kDmaXR * wid + l16) * (uint32_t)K + 16 * g : kOob;
     q.xso = (live && 64 * wid < T.rows) ? (uint32_t)(64 * wid + lane) * 4u : kOob;
-    q.so = live ? (uint32_t)T.cb0 * 64u + lane * 16 : kOob;
+    q.so = live ? (uint32_t)(lane * NB + T.cb0) : kOob;
     return q;
   };
 
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       } else if (wid == 2) {
         // the tile's weight-scale line: 64 bytes per column block
         if (kGemmBN / 16 * 4 >= 64 || lane < kGemmBN / 16 * 4)
-          dma16(q.sr, q.so + (uint32_t)(st * NB) * 64u, base + kOffWs);
+          dma16(q.sr, q.so + (uint32_t)(st * 64 * NB), base + kOffWs);
       }
     }
   };
@@ -405,14 +406,14 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       const GemmStage& S = stage[gs % kGemmStages];
-      // this wave's weight fragments and scale bytes
+      // this wave's weight fragments, and its 4 scale bytes in one word
+      // (byte c for column block c, selected by the MFMA's op_sel)
       v4i af[kGemmCB];
-      int sa[kGemmCB];
 #pragma unroll
-      for (int c = 0; c < kGemmCB; ++c) {
+      for (int c = 0; c < kGemmCB; ++c)
         af[c] = *reinterpret_cast<const v4i*>(&S.w[kGemmCB * cg + c][lane * 16]);
-        sa[c] = S.ws[kGemmCB * cg + c][lane];
-      }
+      static_assert(kGemmCB == 4, "one scale word covers the wave's 4 column blocks");
+      const int sa = (int)*reinterpret_cast<const uint32_t*>(&S.ws[lane][kGemmCB * cg]);
       // the scale words of the lane's row in every row block (two per LDS
       // read); k-block g is byte g, moved to byte 0 for the MFMA
       uint32_t xw[kGemmMB];
@@ -443,10 +444,16 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
         if (i + kGemmRD - 1 < kGemmMB) read_b(i + kGemmRD - 1);
         if (FULL || i < mlive) {
           const int sb = (int)(xw[i] >> (8 * g));
-#pragma unroll
-          for (int c = 0; c < kGemmCB; ++c)
+          // op_sel must be a constant: one call per column block
+          auto mfma = [&](auto cc) {
+            constexpr int c = decltype(cc)::value;
             acc[c][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[c].xyzwxyzw, bf[i % kGemmRD], acc[c][i], 4, 0, 0, sa[c], 0, sb);
+                af[c].xyzwxyzw, bf[i % kGemmRD], acc[c][i], 4, 0, c, sa, 0, sb);
+          };
+          mfma(std::integral_constant<int, 0>{});
+          mfma(std::integral_constant<int, 1>{});
+          mfma(std::integral_constant<int, 2>{});
+          mfma(std::integral_constant<int, 3>{});
         }
 #if GEMM_DMA_SPREAD
         // two transfers after each row block's MFMAs, so the block's
@@ -573,8 +580,8 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
 // Load-time weight preparation (bit-exact data movement):
 //   codes  w [E][N][K/2] -> wp [E][N/16][K/128][64 lanes][16 B]
 //          lane l of chunk (e, cb, ks) = bytes [64ks + 16(l/16), +16) of row 16cb + l%16
-//   scales s [E][N][K/32] -> sp [E][K/128][N/16][64 lanes]
-//          byte l of line (e, ks, cb) = group 4ks + l/16 of row 16cb + l%16
+//   scales s [E][N][K/32] -> sp [E][K/128][64 lanes][N/16]
+//          byte cb of lane row (e, ks, l) = group 4ks + l/16 of row 16cb + l%16
 // One wave per 1 KB code chunk; one thread per scale byte.
 //
 // With half > 0 (the gate/up form of w13, half = I/16 gate column blocks)
@@ -606,14 +613,14 @@ __global__ __launch_bounds__(256) void pack_mx_codes_kernel(const uint8_t* __res
 __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ s, int N,
                                                              int K, int half, uint8_t* __restrict__ sp) {
   const int NB = N / 16;
-  const size_t per_e = (size_t)(K / 128) * NB * 64;
+  const size_t per_e = (size_t)(K / 128) * 64 * NB;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= per_e) return;
   const int e = blockIdx.y;
-  const int l = (int)(idx & 63);
-  const size_t line = idx >> 6;                  // ks * NB + cb
-  const int ks = (int)(line / NB);
-  const int cb = (int)(line - (size_t)ks * NB);
+  const size_t line = idx / NB;                  // ks * 64 + lane
+  const int cb = (int)(idx - line * NB);
+  const int l = (int)(line & 63);
+  const int ks = (int)(line >> 6);
   sp[(size_t)e * per_e + idx] =
       s[((size_t)e * N + 16 * src_cb(cb, half) + (l & 15)) * (size_t)(K / 32) + 4 * ks + (l >> 4)];
 }

@@ -338,13 +338,13 @@ def _expected_packing(w, s):
     KS = K // 128
     lane = np.arange(64)
     wp = np.empty((E, N // 16, KS, 64, 16), np.uint8)
-    sp = np.empty((E, KS, N // 16, 64), np.uint8)
+    sp = np.empty((E, KS, 64, N // 16), np.uint8)
     for cb in range(N // 16):
         rows = 16 * cb + lane % 16
         for ks in range(KS):
             cols = 64 * ks + 16 * (lane // 16)
             wp[:, cb, ks] = w[:, rows[:, None], cols[:, None] + np.arange(16)[None, :]]
-            sp[:, ks, cb, :] = s[:, rows, 4 * ks + lane // 16]
+            sp[:, ks, :, cb] = s[:, rows, 4 * ks + lane // 16]
     return wp.reshape(E, N, K2), sp
 
 
