@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
       }
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-      const uint32_t bsc = ue8m0_ceil_byte(amax / 448.0f);
+      const uint32_t bsc = ue8m0_byte_of_amax(amax);
       const float inv = e8m0_reciprocal(bsc);
       uint32_t lo = 0, hi = 0;
       lo = cvt_e4m3x2<false>(h[0] * inv, h[1] * inv, lo);

@@ -59,6 +59,25 @@ __device__ __forceinline__ uint32_t ue8m0_ceil_byte(float q) {
   return (ex + (up ? 1u : 0u)) & 0xFFu;
 }
 
+// The same byte for q = fl32(amax / 448), taken from amax's own bits when
+// the quotient is normal (amax's exponent field >= 10). With amax = 1.m *
+// 2^(ex-127), amax/448 = (1.m/1.75) * 2^(ex-135): the power of two at or
+// above it is 2^(ex-135) when 1.m <= 1.75 (mantissa field <= 0x600000),
+// else 2^(ex-134). Rounding a normal quotient to fp32 never moves it onto a
+// power of two from above (448 * 2^j is an fp32 value and its neighbours
+// are more than half an ulp of the quotient away), so the exact quotient
+// decides. A subnormal quotient can round onto 2^-127 from above, so
+// smaller amax takes the division. Infinity gives 0xFF and NaN 0x00, as the
+// rule gives for inf/448 and NaN/448.
+__device__ __forceinline__ uint32_t ue8m0_byte_of_amax(float amax) {
+  const uint32_t bits = __float_as_uint(amax);
+  const int ex = (int)((bits >> 23) & 0xFFu);
+  const uint32_t m = bits & 0x7FFFFFu;
+  if (ex < 10) return ue8m0_ceil_byte(amax / 448.0f);
+  if (ex == 0xFF) return m == 0u ? 0xFFu : 0x00u;
+  return (uint32_t)(ex - 8) + (m > 0x600000u ? 1u : 0u);
+}
+
 // 2^(127-b) as an fp32, exactly (b <= 254): the reciprocal of the E8M0
 // scale 2^(b-127). Multiplying by it equals dividing by the scale, since
 // both are one correctly rounded operation on the same real value.

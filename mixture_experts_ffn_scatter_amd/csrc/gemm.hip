@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
         // the 32-column group of this row spans lanes l16 + 16 g'
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const uint32_t bsc = ue8m0_ceil_byte(amax / 448.0f);
+        const uint32_t bsc = ue8m0_byte_of_amax(amax);
         const float inv = e8m0_reciprocal(bsc);
         if (mr < T.rows) {
           const size_t row = (size_t)(T.r0 + mr);

@@ -5,87 +5,42 @@
 // boundary", section 2: start_e = align_up(end_{e-1}, A), end_e = start_e +
 // count_e; the scatter writes the int32 ends itself, with no device-to-host
 // read of the counts. Rows of one expert follow the flattened route order
-// t*k+s, so the permutation is unique.
+// r = t*k+s, so the permutation is unique.
 //
-// Three launches, none of which depends on a host-visible count:
-//   1. rank   - one block per 64-token block: walks the block's routes in
-//               flattened order, 256 at a time; inside a wave, routes with
-//               the same expert are found with ballots (one round per
-//               distinct expert) and ranked by lane order; per-wave counts
-//               in LDS give the order across waves, and a running count per
-//               expert carries it across rounds. Writes each local route's
-//               rank inside the token block and the block's expert counts.
-//   2. scan   - one block: per-expert totals, the aligned exclusive scan
-//               over experts (the endpoint recurrence), expert_ends, and the
-//               per-token-block row offsets (in place over the counts).
-//   3. rows   - one block per token: route row = block offset + rank, and
-//               the quantised copy of x[t] into every destination row (codes
-//               coalesced 8 bytes per lane, packed scales assembled across
-//               16 lanes and stored MN-major).
+// Two launches, neither of which depends on a host-visible count. Tokens are
+// grouped in blocks of TB (64, doubled while the block-by-expert count table
+// would not fit in LDS). With a small table (<= 64 token blocks, <= 256
+// local experts):
+//   1. count - one block per token block: its routes counted per expert
+//              with LDS atomics (counts need no order) into counts[w][e].
+//   2. rows  - every block first redoes the small scan from the counts
+//              (expert totals, the aligned exclusive scan over experts - the
+//              endpoint recurrence - and its token block's offset inside
+//              each expert; block 0 writes expert_ends), then one wave per
+//              token: the rank of each local route is the number of earlier
+//              routes of its token block with the same id (ballots over the
+//              block's ids, read with the token's own ids), row = start_e +
+//              block offset + rank; the x row is loaded after the ids,
+//              quantised in registers and copied into every destination row
+//              (codes coalesced 8 bytes per lane, packed scales assembled
+//              across 16 lanes and stored MN-major).
+// With a larger table, launch 1 is one block that counts every route and
+// does the scans once (block offsets and starts in the workspace), and the
+// rows kernel reads them instead of scanning.
 #include "common.h"
 
 namespace moe {
 
-constexpr int kTokBlock = 64;      // tokens per rank block
+constexpr int kTokBlock = 64;       // smallest token block
 constexpr int kScatterMaxE = 1024;
 constexpr int kScatterMaxK = 32;
+constexpr int kCountLds = 32768;    // (token block, expert) counters held in LDS
 
-__global__ __launch_bounds__(256) void scatter_rank_kernel(const int32_t* __restrict__ ids, int T,
-                                                           int k, int expert_start, int E_local,
-                                                           int32_t* __restrict__ counts,
-                                                           int32_t* __restrict__ route_rank) {
-  __shared__ int base[kScatterMaxE];        // routes of each expert in earlier rounds
-  __shared__ int wcnt[4][kScatterMaxE];     // this round's routes per wave and expert
-  const int w = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  for (int e = tid; e < E_local; e += 256) {
-    base[e] = 0;
-    wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
-  }
-  __syncthreads();
-  const int rb = w * kTokBlock * k;
-  const int re = min(T, (w + 1) * kTokBlock) * k;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r0 = rb; r0 < re; r0 += 256) {             // block-uniform rounds
-    const int r = r0 + tid;
-    int e = -1;
-    if (r < re) {
-      const int v = ids[r] - expert_start;
-      e = (v >= 0 && v < E_local) ? v : -1;
-    }
-    // in-wave rank: one ballot round per distinct expert present
-    uint64_t todo = __ballot(e >= 0);
-    int inwave = 0, lead = -1;
-    while (todo) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int key = __shfl(e, leader, 64);
-      const uint64_t m = __ballot(e == key);
-      if (e == key) inwave = __popcll(m & below);
-      if (lane == leader) {
-        wcnt[wid][key] = __popcll(m);
-        lead = key;
-      }
-      todo &= ~m;
-    }
-    __syncthreads();
-    if (r < re) {
-      int rank = -1;
-      if (e >= 0) {
-        rank = base[e] + inwave;
-        for (int v = 0; v < wid; ++v) rank += wcnt[v][e];
-      }
-      route_rank[r] = rank;
-    }
-    __syncthreads();
-    if (lead >= 0) {
-      atomicAdd(&base[lead], wcnt[wid][lead]);
-      wcnt[wid][lead] = 0;
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < E_local; e += 256) counts[(size_t)w * E_local + e] = base[e];
+// token block size: 64, doubled until ceil(T / TB) * E_local counters fit
+inline int scatter_token_block(int T, int E_local) {
+  int tb = kTokBlock;
+  while ((long long)((T + tb - 1) / tb) * E_local > kCountLds) tb *= 2;
+  return tb;
 }
 
 // Block-wide exclusive scan of one int per thread (1024 threads).
@@ -114,121 +69,285 @@ __device__ int block_exclusive_scan_1024(int v, int* wave_tot) {
   return wave_tot[16 + wid] + incl - v;
 }
 
-constexpr int kScanLds = 8192;    // counts staged in LDS when W * E_local fits
+constexpr int kCountBatch = 32;     // ids in flight per lane
 
-__global__ __launch_bounds__(1024) void scatter_scan_kernel(int W, int E_local, int A,
-                                                            int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ expert_ends) {
+__global__ __launch_bounds__(1024) void scatter_count_scan_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int A, int TB,
+    int W, int32_t* __restrict__ offsets, int32_t* __restrict__ starts,
+    int32_t* __restrict__ expert_ends) {
+  __shared__ int s_cnt[kCountLds];
+  __shared__ int s_tot[kScatterMaxE];
   __shared__ int wave_tot[32];
-  __shared__ int s_cnt[kScanLds];
-  const int e = threadIdx.x;
-  const int n = W * E_local;
-  const bool staged = n <= kScanLds;          // block-uniform
-  if (staged) {
-    for (int i = threadIdx.x; i < n; i += 1024) s_cnt[i] = counts[i];
-    __syncthreads();
-  }
-  int total = 0;
-  if (e < E_local) {
-    if (staged) {
-#pragma unroll 8
-      for (int w = 0; w < W; ++w) total += s_cnt[w * E_local + e];
-    } else {
-#pragma unroll 8
-      for (int w = 0; w < W; ++w) total += counts[(size_t)w * E_local + e];
-    }
-  }
-  const int aligned = e < E_local ? align_up_dev(total, A) : 0;
-  const int start = block_exclusive_scan_1024(aligned, wave_tot);
-  if (e < E_local) expert_ends[e] = start + total;
-  // counts -> per-block row offsets (exclusive over token blocks, plus start_e)
-  if (staged) {
-    if (e < E_local) {
-      int run = start;
-      for (int w = 0; w < W; ++w) {
-        const int c = s_cnt[w * E_local + e];
-        s_cnt[w * E_local + e] = run;
-        run += c;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = T * k;
+  const int rpb = TB * k;                // routes per token block
+  // wave wid counts token blocks wid, wid+16, ...: a flat list of 64-route
+  // chunks (block j of the wave, chunk c of the block) walked with
+  // wave-uniform counters, so no route needs a division
+  const int cpb = (rpb + 63) / 64;       // chunks per block
+  const int nq = ((W - wid + 15) / 16) * cpb;
+  int id[kCountBatch];
+  int blk[kCountBatch];
+  int qj = 0, qc = 0;                    // position of the next chunk to load
+  auto load = [&](int q0) {
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) {
+      const int b = wid + 16 * qj;
+      const int o = qc * 64 + lane;
+      const int r = b * rpb + o;
+      // unpredicated, in-bounds load; validity goes in blk (-1: no route)
+      id[u] = ids[min(r, n - 1)];
+      blk[u] = (q0 + u < nq && o < rpb && r < n) ? b : -1;
+      if (++qc == cpb) {
+        qc = 0;
+        ++qj;
       }
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 1024) counts[i] = s_cnt[i];
-  } else if (e < E_local) {
-    int run = start;
-    for (int w = 0; w < W; ++w) {
-      int32_t* p = counts + (size_t)w * E_local + e;
-      const int c = *p;
-      *p = run;
-      run += c;
+  };
+  if (nq > 0) load(0);                   // in flight while the counters are cleared
+  for (int i = tid; i < W * E_local; i += 1024) s_cnt[i] = 0;
+  __syncthreads();
+  for (int q0 = 0; q0 < nq; q0 += kCountBatch) {
+#pragma unroll
+    for (int u = 0; u < kCountBatch; ++u) {
+      const int e = id[u] - expert_start;
+      if (blk[u] >= 0 && e >= 0 && e < E_local) atomicAdd(&s_cnt[blk[u] * E_local + e], 1);
     }
+    if (q0 + kCountBatch < nq) load(q0 + kCountBatch);
+  }
+  __syncthreads();
+  // per expert: exclusive scan over the token blocks, 64 blocks at a time
+  for (int e = wid; e < E_local; e += 16) {
+    int carry = 0;
+    for (int w0 = 0; w0 < W; w0 += 64) {
+      const int w = w0 + lane;
+      const int c = w < W ? s_cnt[w * E_local + e] : 0;
+      int incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+      }
+      if (w < W) offsets[(size_t)w * E_local + e] = carry + incl - c;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) s_tot[e] = carry;
+  }
+  __syncthreads();
+  const int e = tid;
+  const int total = e < E_local ? s_tot[e] : 0;
+  const int aligned = e < E_local ? align_up_dev(total, A) : 0;
+  const int start = block_exclusive_scan_1024(aligned, wave_tot);
+  if (e < E_local) {
+    starts[e] = start;
+    expert_ends[e] = start + total;
   }
 }
 
-// One block per token. Lanes < k turn their route's rank into its row; the
-// block then quantises x[t]: each thread owns 8 consecutive columns per
-// 2048-column chunk, a 32-column group spans 4 lanes and a packed scale word
-// (128 columns) 16 lanes; codes go to every destination row (8 bytes per
-// lane, coalesced) and scale words MN-major.
-constexpr int kRowsThreads = 256;
+// One block per token block: its routes counted per expert with LDS
+// atomics, written to counts[w][e]. Used when the rows kernel scans the
+// counts itself.
+constexpr int kCntBatch = 4;        // ids in flight per thread
 
-__global__ __launch_bounds__(kRowsThreads) void scatter_rows_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int M_cap,
-    const uint16_t* __restrict__ x, int H, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ route_row, uint8_t* __restrict__ xq, int32_t* __restrict__ xs) {
-  __shared__ int s_row[kScatterMaxK];
-  __shared__ int s_any;
-  const int t = blockIdx.x;
+__global__ __launch_bounds__(256) void scatter_count_kernel(const int32_t* __restrict__ ids,
+                                                            int n, int expert_start, int E_local,
+                                                            int rpb,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int s[kScatterMaxE];
+  const int w = blockIdx.x;
   const int tid = threadIdx.x;
-  const int w = t / kTokBlock;
-  if (tid == 0) s_any = 0;
+  const int rb = w * rpb;
+  const int re = min(n, rb + rpb);
+  int id[kCntBatch];
+  auto load = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < kCntBatch; ++u) id[u] = ids[min(r0 + u * 256 + tid, n - 1)];
+  };
+  load(rb);                           // in flight while the counters are cleared
+  for (int e = tid; e < E_local; e += 256) s[e] = 0;
   __syncthreads();
-  if (tid < k) {
-    // route_row holds the rank from the rank pass (or -1); turn it into the row
-    const int rank = route_row[(size_t)t * k + tid];
-    int row = -1;
-    if (rank >= 0) {
-      const int e = ids[(size_t)t * k + tid] - expert_start;
-      row = offsets[(size_t)w * E_local + e] + rank;
-      if (row >= M_cap) row = -1;           // corrupt metadata: never write past the buffer
+  for (int r0 = rb; r0 < re; r0 += 256 * kCntBatch) {
+#pragma unroll
+    for (int u = 0; u < kCntBatch; ++u) {
+      const int e = id[u] - expert_start;
+      if (r0 + u * 256 + tid < re && e >= 0 && e < E_local) atomicAdd(&s[e], 1);
     }
-    s_row[tid] = row;
-    route_row[(size_t)t * k + tid] = row;
-    if (row >= 0) atomicOr(&s_any, 1);
+    if (r0 + 256 * kCntBatch < re) load(r0 + 256 * kCntBatch);
   }
   __syncthreads();
-  if (!s_any) return;  // block-uniform: no local route for this token
+  for (int e = tid; e < E_local; e += 256) counts[(size_t)w * E_local + e] = s[e];
+}
 
-  const uint16_t* xr = x + (size_t)t * H;
-  const int nchunks = (H + 8 * kRowsThreads - 1) / (8 * kRowsThreads);
-  for (int i = 0; i < nchunks; ++i) {
-    const int base = tid * 8 + i * 8 * kRowsThreads;
-    const bool act = base < H;              // whole 16-lane groups (H % 128 == 0)
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (act) raw = *reinterpret_cast<const uint4*>(xr + base);
-    float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                  bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-    float amax = 0.f;
+constexpr int kRowsWaves = 4;    // tokens per block
+constexpr int kRowsBatch = 8;    // 512-column chunks held in registers at once
+constexpr int kPrevBatch = 8;    // 64-route chunks of earlier ids loaded at once
+
+constexpr int kScanMaxW = 64;    // rows-kernel scan: token blocks
+constexpr int kScanMaxE = 256;   // rows-kernel scan: local experts
+
+// SCAN: `meta` holds the per-(token block, expert) counts and every block
+// redoes the small scan itself (start_e plus the token block's offset inside
+// expert e, for all e; block 0 also writes expert_ends). Otherwise `meta`
+// holds the block offsets and `starts` the expert starts.
+template <bool SCAN>
+__global__ __launch_bounds__(64 * kRowsWaves) void scatter_rows_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int A,
+    int M_cap, int TB, int W, const uint16_t* __restrict__ x, int H,
+    const int32_t* __restrict__ meta, const int32_t* __restrict__ starts,
+    int32_t* __restrict__ expert_ends, int32_t* __restrict__ route_row,
+    uint8_t* __restrict__ xq, int32_t* __restrict__ xs) {
+  __shared__ int s_base[SCAN ? kScanMaxE : 1];
+  __shared__ int s_wsum[kRowsWaves];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x * kRowsWaves + wid;
+  const bool tok = t < T;                // wave-uniform
+  const int wblk = blockIdx.x * kRowsWaves / TB;   // TB % kRowsWaves == 0: one token block
+  const int rt = t * k;                  // the token's first route
+  const int rb = wblk * TB * k;          // its token block's first route
+  const int nprev = rt - rb;             // earlier routes of the block
+  // an id no local route has, for lanes past the earlier routes
+  const int none = expert_start > INT_MIN ? expert_start - 1 : INT_MAX;
+  // level 1: the token's ids (lanes < k) and the block's earlier ids, together
+  int id = none;
+  if (tok && lane < k) id = ids[rt + lane];
+  int prev[kPrevBatch];
+  auto load_prev = [&](int c0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    const uint32_t b = ue8m0_ceil_byte(amax / 448.0f);
-    const float inv = e8m0_reciprocal(b);
-    uint32_t lo = 0, hi = 0;
-    lo = cvt_e4m3x2<false>(v[0] * inv, v[1] * inv, lo);
-    lo = cvt_e4m3x2<true>(v[2] * inv, v[3] * inv, lo);
-    hi = cvt_e4m3x2<false>(v[4] * inv, v[5] * inv, hi);
-    hi = cvt_e4m3x2<true>(v[6] * inv, v[7] * inv, hi);
-    uint32_t word = b << (8 * ((tid >> 2) & 3));
-    word |= __shfl_xor(word, 4, 64);
-    word |= __shfl_xor(word, 8, 64);
-    if (act) {
-      const int c = base >> 7;
-      for (int s = 0; s < k; ++s) {
-        const int row = s_row[s];
-        if (row < 0) continue;
-        *reinterpret_cast<uint2*>(xq + (size_t)row * H + base) = make_uint2(lo, hi);
-        if ((tid & 15) == 0) xs[(size_t)c * M_cap + row] = (int32_t)word;
+    for (int u = 0; u < kPrevBatch; ++u) {
+      const int j = c0 + u * 64 + lane;
+      prev[u] = (tok && j < nprev) ? ids[rb + j] : none;
+    }
+  };
+  load_prev(0);
+  if constexpr (SCAN) {
+    // thread e: expert e's total and its count in earlier token blocks; then
+    // the aligned exclusive scan over experts across the block's threads
+    const int e = threadIdx.x;
+    int total = 0, before = 0;
+    if (e < E_local) {
+      int c[kScanMaxW];
+#pragma unroll
+      for (int w = 0; w < kScanMaxW; ++w) c[w] = meta[(size_t)min(w, W - 1) * E_local + e];
+#pragma unroll
+      for (int w = 0; w < kScanMaxW; ++w) {
+        const int v = w < W ? c[w] : 0;
+        total += v;
+        before += w < wblk ? v : 0;
+      }
+    }
+    const int aligned = e < E_local ? align_up_dev(total, A) : 0;
+    int incl = aligned;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wsum[wid] = incl;
+    __syncthreads();
+    int start = incl - aligned;
+    for (int v = 0; v < wid; ++v) start += s_wsum[v];
+    if (e < E_local) {
+      s_base[e] = start + before;
+      if (blockIdx.x == 0) expert_ends[e] = start + total;
+    }
+    __syncthreads();
+  }
+  if (!tok) return;
+  const int ev = id - expert_start;
+  const bool local = lane < k && id != none && ev >= 0 && ev < E_local;
+  const uint64_t lmask = __ballot(local);
+  if (lmask == 0ull) {                   // wave-uniform: no local route
+    if (lane < k) route_row[rt + lane] = -1;
+    return;
+  }
+  // rank of each local slot: earlier slots of the token, then earlier
+  // routes of the block, with the same id (lane s keeps slot s's rank).
+  // Done before the next loads are issued: a loop with loads in it would
+  // make every load in flight complete before it.
+  int rank = 0;
+  for (uint64_t m = lmask; m; m &= m - 1) {
+    const int s = __ffsll((unsigned long long)m) - 1;
+    const int key = __builtin_amdgcn_readlane(id, s);
+    const int c = __popcll(__ballot(lane < s && id == key));
+    if (lane == s) rank = c;
+  }
+  for (int c0 = 0;;) {
+    for (uint64_t m = lmask; m; m &= m - 1) {
+      const int s = __ffsll((unsigned long long)m) - 1;
+      const int key = __builtin_amdgcn_readlane(id, s);
+      int c = 0;
+#pragma unroll
+      for (int u = 0; u < kPrevBatch; ++u) c += __popcll(__ballot(prev[u] == key));
+      if (lane == s) rank += c;
+    }
+    c0 += 64 * kPrevBatch;
+    if (c0 >= nprev) break;              // wave-uniform
+    load_prev(c0);
+  }
+  // level 2: start and block offset of the local slots' experts, and the x row
+  const int ec = local ? ev : 0;         // unpredicated: every lane reads a valid entry
+  int base;
+  if constexpr (SCAN) {
+    base = s_base[ec];
+  } else {
+    base = starts[ec] + meta[(size_t)wblk * E_local + ec];
+  }
+  const uint16_t* xr = x + (size_t)t * H;
+  const int nch = (H + 511) / 512;
+  uint4 raw[kRowsBatch];
+  // unpredicated loads (columns past H read the row's last 8 and are not
+  // used), so that each chunk waits only for its own load
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < kRowsBatch; ++j) {
+      const int col = min((c0 + j) * 512 + lane * 8, H - 8);
+      raw[j] = *reinterpret_cast<const uint4*>(xr + col);
+    }
+  };
+  load_batch(0);
+  int row = -1;
+  if (local) {
+    row = base + rank;
+    if (row >= M_cap) row = -1;           // corrupt metadata: never write past the buffer
+  }
+  const uint64_t live = __ballot(row >= 0);
+  if (lane < k) route_row[rt + lane] = row;
+
+  for (int c0 = 0; c0 < nch; c0 += kRowsBatch) {
+    if (c0 > 0) load_batch(c0);
+    // chunk by chunk: the stores of one chunk overlap the next chunk's math
+#pragma unroll
+    for (int j = 0; j < kRowsBatch; ++j) {
+      const int col = (c0 + j) * 512 + lane * 8;
+      if ((c0 + j) * 512 >= H) break;     // wave-uniform
+      const float v[8] = {bf16_lo(raw[j].x), bf16_hi(raw[j].x), bf16_lo(raw[j].y),
+                          bf16_hi(raw[j].y), bf16_lo(raw[j].z), bf16_hi(raw[j].z),
+                          bf16_lo(raw[j].w), bf16_hi(raw[j].w)};
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const uint32_t b = ue8m0_byte_of_amax(amax);
+      const float inv = e8m0_reciprocal(b);
+      uint32_t lo = 0, hi = 0;
+      lo = cvt_e4m3x2<false>(v[0] * inv, v[1] * inv, lo);
+      lo = cvt_e4m3x2<true>(v[2] * inv, v[3] * inv, lo);
+      hi = cvt_e4m3x2<false>(v[4] * inv, v[5] * inv, hi);
+      hi = cvt_e4m3x2<true>(v[6] * inv, v[7] * inv, hi);
+      uint32_t wd = b << (8 * ((lane >> 2) & 3));
+      wd |= __shfl_xor(wd, 4, 64);
+      wd |= __shfl_xor(wd, 8, 64);
+      for (uint64_t m = live; m; m &= m - 1) {   // wave-uniform loop over destination rows
+        const int s = __ffsll((unsigned long long)m) - 1;
+        const int r = __builtin_amdgcn_readlane(row, s);
+        if (col < H) {
+          *reinterpret_cast<uint2*>(xq + (size_t)r * H + col) = make_uint2(lo, hi);
+          if ((lane & 15) == 0) xs[(size_t)(col >> 7) * M_cap + r] = (int32_t)wd;
+        }
       }
     }
   }
@@ -253,8 +372,9 @@ static int fill_i32(int32_t* p, int n, int32_t v, hipStream_t st) {
 extern "C" size_t moe_scatter_workspace_bytes(int T, int k, int E_local) {
   (void)k;
   if (T <= 0 || E_local <= 0) return 0;
-  const size_t W = (size_t)(T + moe::kTokBlock - 1) / moe::kTokBlock;
-  return W * (size_t)E_local * sizeof(int32_t);
+  const int tb = moe::scatter_token_block(T, E_local);
+  const size_t W = (size_t)(T + tb - 1) / tb;
+  return (W + 1) * (size_t)E_local * sizeof(int32_t);   // block offsets, then starts
 }
 
 extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_start,
@@ -264,7 +384,7 @@ extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int 
                                      void* stream) {
   using namespace moe;
   if (T < 0 || k < 1 || k > kScatterMaxK || E_local < 0 || E_local > kScatterMaxE || A < 1 ||
-      M_cap < 0 || H <= 0)
+      M_cap < 0 || H <= 0 || (long long)T * k > INT_MAX)
     return MOE_ERR_SHAPE;
   if (H % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
   if ((long long)M_cap < (long long)T * k + (long long)E_local * A) return MOE_ERR_CAPACITY;
@@ -279,16 +399,28 @@ extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int 
   const size_t need = moe_scatter_workspace_bytes(T, k, E_local);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const int W = (T + kTokBlock - 1) / kTokBlock;
-  int32_t* counts = (int32_t*)workspace;
-  hipLaunchKernelGGL(scatter_rank_kernel, dim3(W), dim3(256), 0, st, topk_ids, T, k, expert_start,
-                     E_local, counts, route_row);
-  MOE_CHECK_LAUNCH();
-  hipLaunchKernelGGL(scatter_scan_kernel, dim3(1), dim3(1024), 0, st, W, E_local, A, counts,
-                     expert_ends);
-  MOE_CHECK_LAUNCH();
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3(T), dim3(kRowsThreads), 0, st, topk_ids, T, k,
-                     expert_start, E_local, M_cap, x, H, counts, route_row, xq, xs);
-  MOE_CHECK_LAUNCH();
+  const int TB = scatter_token_block(T, E_local);
+  const int W = (T + TB - 1) / TB;
+  int32_t* meta = (int32_t*)workspace;   // counts or block offsets [W][E_local]
+  int32_t* starts = meta + (size_t)W * E_local;
+  const dim3 rows_grid((T + kRowsWaves - 1) / kRowsWaves);
+  if (W <= kScanMaxW && E_local <= kScanMaxE) {
+    // small count table: per-block counts, and each rows block scans them
+    hipLaunchKernelGGL(scatter_count_kernel, dim3(W), dim3(256), 0, st, topk_ids, T * k,
+                       expert_start, E_local, TB * k, meta);
+    MOE_CHECK_LAUNCH();
+    hipLaunchKernelGGL(scatter_rows_kernel<true>, rows_grid, dim3(64 * kRowsWaves), 0, st,
+                       topk_ids, T, k, expert_start, E_local, A, M_cap, TB, W, x, H, meta,
+                       starts, expert_ends, route_row, xq, xs);
+    MOE_CHECK_LAUNCH();
+  } else {
+    hipLaunchKernelGGL(scatter_count_scan_kernel, dim3(1), dim3(1024), 0, st, topk_ids, T, k,
+                       expert_start, E_local, A, TB, W, meta, starts, expert_ends);
+    MOE_CHECK_LAUNCH();
+    hipLaunchKernelGGL(scatter_rows_kernel<false>, rows_grid, dim3(64 * kRowsWaves), 0, st,
+                       topk_ids, T, k, expert_start, E_local, A, M_cap, TB, W, x, H, meta,
+                       starts, expert_ends, route_row, xq, xs);
+    MOE_CHECK_LAUNCH();
+  }
   return MOE_OK;
 }

@@ -51,7 +51,11 @@ def test_abi_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.moe_scatter_workspace_bytes(4096, 6, 32) == 64 * 32 * 4   # 64-token blocks
+    # per (64-token block, expert) offsets, then one start per expert
+    assert lib.moe_scatter_workspace_bytes(4096, 6, 32) == (64 + 1) * 32 * 4
+    # blocks double until the block-by-expert table holds <= 32768 counters
+    assert lib.moe_scatter_workspace_bytes(65536, 8, 1024) == (32 + 1) * 1024 * 4
+    assert lib.moe_scatter_workspace_bytes(2048, 16, 896) == (32 + 1) * 896 * 4
     assert lib.moe_scatter_workspace_bytes(0, 6, 32) == 0
 
 
@@ -154,3 +158,31 @@ def test_compact_sigmoid_lookup_equals_full_table(tmp_path):
                       tab[rows * 128 + (np.clip(ex[n], neg_lo, neg_hi) - lo) * 128 + m[n]])
     bad = np.flatnonzero(out != full)
     assert bad.size == 0, f"{bad.size} patterns differ, first {[hex(v) for v in bad[:8]]}"
+
+
+def test_division_free_scale_byte_equals_rounding_rule():
+    """The kernels' UE8M0 byte taken straight from amax's bits when amax's
+    exponent field is >= 10 (field minus 8, plus one when the mantissa field
+    exceeds 0x600000, i.e. 1.m > 1.75; 0xFF for inf and 0 for NaN), restated
+    here, equals the oracle's round-up rule on fl32(amax / 448) for every
+    mantissa at exponent fields 10..12, 127 and 250..255. While amax and the
+    quotient are normal (field >= 10), scaling amax by a power of two scales
+    the rounded quotient by the same power, so these fields cover every
+    case. Below field 10 the quotient is subnormal, its rounding can land on
+    2^-127 from above (amax = 0x04600001 does), and the kernels divide."""
+    from oracle import formats as F
+    m = np.arange(1 << 23, dtype=np.uint32)
+    for ex in [10, 11, 12, 127] + list(range(250, 256)):
+        bits = (np.uint32(ex) << np.uint32(23)) | m
+        amax = bits.view(np.float32)
+        with np.errstate(invalid="ignore", over="ignore"):
+            want = F.ue8m0_ceil_byte((amax / np.float32(448.0)).astype(np.float32))
+        if ex == 255:
+            got = np.where(m == 0, 0xFF, 0x00).astype(np.uint8)
+        else:
+            got = (ex - 8 + (m > 0x600000).astype(np.int64)).astype(np.uint8)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"exponent field {ex}: {bad.size} differ, first {hex(int(bits[bad[0]]))}"
+    # the subnormal-quotient case the division is kept for
+    q = np.array([0x04600001], np.uint32).view(np.float32) / np.float32(448.0)
+    assert F.ue8m0_ceil_byte(q.astype(np.float32))[0] == 0

@@ -150,6 +150,59 @@ def test_scatter_fp8_rounding_edges(ops):
     _check_scatter(ids, xb, 0, 8, 128, M_cap, got)
 
 
+def test_scatter_scale_byte_edges(ops):
+    """Group maxima at 448 * 2^j and the bf16 values just above and below it,
+    for j over the whole bf16 range (subnormal quotients included), plus
+    bf16 subnormal and all-zero groups: the UE8M0 byte decision at every
+    power-of-two boundary."""
+    say("scatter scale-byte edges")
+    rng = np.random.default_rng(22)
+    T, H = 64, 1024
+    G = H // 32
+    js = np.arange(-141, 120)
+    x = np.empty((T, H), np.float64)
+    for t in range(T):
+        for g in range(G):
+            j = int(js[(t * G + g) % js.size])
+            top = 448.0 * 2.0 ** j
+            kind = (t * G + g) // js.size % 4
+            if kind == 1:
+                top *= 1.0 + 2.0 ** -7        # next bf16 above
+            elif kind == 2:
+                top *= 1.0 - 2.0 ** -8        # next bf16 below
+            elif kind == 3:
+                top = 2.0 ** -133 * int(rng.integers(0, 128))   # bf16 subnormals (and zero)
+            vals = rng.uniform(-1.0, 1.0, 32) * top
+            vals[int(rng.integers(0, 32))] = top * rng.choice([-1.0, 1.0])
+            x[t, g * 32:(g + 1) * 32] = vals
+    xb = F.round_to_bf16(x)
+    assert np.all(np.isfinite(F.bf16_to_f32(xb)))
+    ids = np.stack([np.arange(T) % 5, 5 + np.arange(T) % 3], axis=1).astype(np.int32)
+    M_cap = W.capacity(T, 2, 8, 128)
+    got = _run_scatter(ops, ids, xb, 0, 8, 128, M_cap)
+    _check_scatter(ids, xb, 0, 8, 128, M_cap, got)
+
+
+@pytest.mark.parametrize("T,k,E,start,E_local", [(2048, 16, 896, 0, 896), (4096, 8, 1200, 100, 1024)])
+def test_scatter_long_token_blocks(ops, T, k, E, start, E_local):
+    """Many routes per token block (more than 512 earlier routes for a
+    token's rank), and a block-by-expert table too large for 64-token blocks
+    (4096 tokens x 1024 local experts), with skewed ids, -1 slots and ids
+    outside the window."""
+    say(f"scatter T={T} k={k} E={E} window [{start}, {start + E_local})")
+    rng = np.random.default_rng(T + k)
+    # Gumbel-top-k over Zipf(1.0) popularity on a shuffled expert order
+    logp = -np.log(1.0 + rng.permutation(E))
+    keys = logp[None, :] + rng.gumbel(size=(T, E))
+    ids = np.argsort(-keys, axis=1)[:, :k].astype(np.int32)
+    ids[rng.random((T, k)) < 0.02] = -1
+    H, A = 128, 128
+    x = F.round_to_bf16(rng.standard_normal((T, H)))
+    M_cap = W.capacity(T, k, E_local, A)
+    got = _run_scatter(ops, ids, x, start, E_local, A, M_cap)
+    _check_scatter(ids, x, start, E_local, A, M_cap, got)
+
+
 def test_scatter_prefill_group_full_size(ops):
     say("scatter prefill EP group 4096x6 -> 32 local experts")
     c = W.prefill(with_weights=False)
