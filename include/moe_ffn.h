@@ -328,8 +328,8 @@ int moe_combine(const uint16_t* rows, int64_t n_rows, const int32_t* row_of_slot
  *                   (glu_limit <= 0: no clamp).
  *   out          row t*k+s is written only when slot (t,s) is local
  *   slot_row     int32 [T*k] out or NULL: t*k+s when local, else -1
- * Requires K % 32 == 0 (FP8: K % 16 == 0 suffices), N % 2 == 0 when glu,
- * 1 <= T*k <= 64, E_local <= 1024.
+ * Requires K % 32 == 0 (FP8: K % 16 == 0 suffices), K <= 8192, N % 2 == 0
+ * when glu, 1 <= T*k <= 64, E_local <= 1024.
  * ------------------------------------------------------------------------ */
 int moe_sparse_gemv(const uint16_t* act, int act_per_slot, const int32_t* topk_ids, int T, int k,
                     int expert_start, int E_local, int N, int K, int wfmt, const uint8_t* w,

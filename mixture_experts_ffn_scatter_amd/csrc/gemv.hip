@@ -11,17 +11,18 @@
 // Differences from the page's kernel: blocks are keyed by slot, but only
 // the first slot (in t*k+s order) of each distinct local expert does work,
 // and it computes every slot routed to that expert, so each selected
-// expert's weights are read once per call instead of once per slot. The
-// slot ids are copied to LDS in one parallel load and the duplicate test
-// runs there. A wave owns 8 weight rows (4 output columns: 4 gate + 4 up
-// rows when the GLU is fused; else 8 output columns) and issues all their
-// 16-byte chunks (strided by the wave over K) before the activations of the
-// expert's slots are staged in LDS as bf16, so the two loads overlap; each
-// chunk is converted to exact bf16 pairs and accumulated with bf16 dot
-// products in fp32 against the LDS activations, and the 64 partial sums of
-// a row are folded by shuffles. With the GLU fused, the GLU is applied to
-// the bf16-rounded gate and up results before the single bf16 store.
+// expert's weights are read once per call instead of once per slot. A
+// block owns 8 weight rows (4 gate + 4 up rows when the GLU is fused, else 8
+// output columns); its 256 threads split K: thread i holds the 16-weight
+// chunk i (and i+256) of every row, 16 or 8 bytes each, all loaded at once,
+// and reads the matching 16 activations of each slot straight from memory
+// into registers. Each chunk is converted once to exact bf16 pairs and dotted
+// in fp32 against every slot of a batch; the partial sums are folded inside
+// each wave with DPP adds and across the 4 waves through LDS in a fixed
+// order. With the GLU fused, the GLU is applied to the bf16-rounded gate and
+// up results before the single bf16 store.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 
@@ -29,10 +30,10 @@ namespace moe {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / 64;
-constexpr int kGemvRows = 8;          // weight rows per wave (GLU: 4 gate + 4 up)
+constexpr int kGemvRows = 8;          // weight rows per block (GLU: 4 gate + 4 up)
 constexpr int kGemvMaxSlots = 64;     // T*k
-constexpr int kGemvSlotBatch = 8;     // slots whose activations are staged in LDS at once
-constexpr int kGemvMaxChunks = 4;     // 16-byte weight chunks per lane and row (K <= 4096 FP8)
+constexpr int kGemvSlotBatch = 2;     // slots accumulated together
+constexpr int kGemvMaxCh = 2;         // 16-weight chunks per thread and row (K <= 8192)
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
@@ -45,22 +46,41 @@ __device__ __forceinline__ float glu_apply(float g, float u, float alpha, float 
   return g * sig * (u + beta);
 }
 
-// 16 weight bytes -> bf16 pairs (exact: E4M3 and E2M1 values fit bf16).
-// FP8: 16 weights -> 8 pairs; MXFP4: 32 weights -> 16 pairs (low nibble first).
-template <bool MXFP4>
-__device__ __forceinline__ void weights_to_bf16(const v4i raw, v2bf* wp) {
+// Sum over the wave, left in lane 63: inclusive scan inside each 16-lane row
+// (row_shr 1, 2, 4, 8), then rows 1 and 3 add row 0's and row 2's totals
+// (row_bcast:15) and rows 2 and 3 add lane 31 (row_bcast:31). Fixed order.
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  auto step = [](float x, auto ctrl, auto rmask) -> float {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                          decltype(rmask)::value, 0xF, false));
+  };
+  v = step(v, std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xF>{});
+  v = step(v, std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xF>{});
+  v = step(v, std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xF>{});
+  v = step(v, std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xF>{});
+  v = step(v, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});
+  v = step(v, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});
+  return v;
+}
+
+// 16 weights -> 8 exact bf16 pairs. FP8: 16 bytes (4 dwords); MXFP4: 8
+// bytes (2 dwords, low nibble first).
+__device__ __forceinline__ void weights_to_bf16(const v2i raw, v2bf* wp) {   // MXFP4
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t d = (uint32_t)(q == 0 ? raw.x : raw.y);
+    wp[4 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 0);
+    wp[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 1);
+    wp[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 2);
+    wp[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 3);
+  }
+}
+__device__ __forceinline__ void weights_to_bf16(const v4i raw, v2bf* wp) {   // FP8
   const uint32_t d[4] = {(uint32_t)raw.x, (uint32_t)raw.y, (uint32_t)raw.z, (uint32_t)raw.w};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (MXFP4) {
-      wp[4 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[q], 1.0f, 0);
-      wp[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[q], 1.0f, 1);
-      wp[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[q], 1.0f, 2);
-      wp[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[q], 1.0f, 3);
-    } else {
-      wp[2 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[q], 1.0f, false);
-      wp[2 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[q], 1.0f, true);
-    }
+    wp[2 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[q], 1.0f, false);
+    wp[2 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[q], 1.0f, true);
   }
 }
 
@@ -70,11 +90,12 @@ __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
     int k, int expert_start, int E_local, int N, int K, const uint8_t* __restrict__ W,
     const void* __restrict__ w_scale, const uint16_t* __restrict__ bias, float alpha,
     float beta, float limit, uint16_t* __restrict__ out, int32_t* __restrict__ slot_row) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_act[];  // [kGemvSlotBatch][K] bf16
+  __shared__ float s_red[kGemvWaves][kGemvSlotBatch][kGemvRows];
 
   const int q = blockIdx.y;  // flattened slot t*k+s
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nq = T * k;      // <= 64: one id per lane
   // every wave reads all slot ids at once; the same ballots in every wave
   // give the duplicate test and the list of slots routed to this expert
@@ -87,15 +108,12 @@ __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
   const uint64_t same = __ballot(my_id == id);
   // the first slot of each distinct local expert does the work
   if (same & ((1ull << q) - 1ull)) return;   // block-uniform
-  uint64_t slot_mask = same;                  // slots p >= q routed to this expert
 
-  const int wid = tid >> 6;
   const int n_out = GLU ? N / 2 : N;
-  constexpr int kOuts = GLU ? kGemvRows / 2 : kGemvRows;    // output columns per wave
-  const int col0 = (blockIdx.x * kGemvWaves + wid) * kOuts;
+  constexpr int kOuts = GLU ? kGemvRows / 2 : kGemvRows;    // output columns per block
+  const int col0 = blockIdx.x * kOuts;
   const size_t row_bytes = MXFP4 ? (size_t)K / 2 : (size_t)K;
-  const int kchunk = MXFP4 ? 32 : 16;  // weights per 16-byte chunk
-  const int nchunks = K / kchunk;
+  const int nch = K / 16;              // 16-weight chunks per row
   const uint8_t* We = W + (size_t)e * N * row_bytes;
   const float fp8_scale = MXFP4 ? 1.f : reinterpret_cast<const float*>(w_scale)[e];
   const uint8_t* Ws = MXFP4 ? reinterpret_cast<const uint8_t*>(w_scale) + (size_t)e * N * (K / 32)
@@ -107,90 +125,108 @@ __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
     return min(col0 + r, N - 1);
   };
 
-  // every weight chunk of this wave's rows goes out first
-  v4i raw[kGemvRows][CH];
+  // every weight chunk of this thread goes out first (unpredicated: a
+  // thread past the last chunk reads the last one and does not use it)
+  using RawT = std::conditional_t<MXFP4, v2i, v4i>;
+  RawT raw[kGemvRows][CH];
   float gsc[kGemvRows][CH];
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r) {
-    const uint8_t* wr = We + (size_t)row_of(r) * row_bytes;
+  for (int j = 0; j < CH; ++j) {
+    const int ch = min(tid + kGemvThreads * j, nch - 1);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = lane + 64 * c;
-      raw[r][c] = v4i{0, 0, 0, 0};
-      gsc[r][c] = 0.f;
-      if (ch < nchunks) {
-        raw[r][c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wr + (size_t)ch * 16));
-        if (MXFP4) gsc[r][c] = e8m0_value(Ws[(size_t)row_of(r) * (K / 32) + ch]);
-      }
+    for (int r = 0; r < kGemvRows; ++r) {
+      const uint8_t* wr = We + (size_t)row_of(r) * row_bytes;
+      raw[r][j] = __builtin_nontemporal_load(
+          reinterpret_cast<const RawT*>(wr + (size_t)ch * sizeof(RawT)));
+      gsc[r][j] = MXFP4 ? e8m0_value(Ws[(size_t)row_of(r) * (K / 32) + ch / 2]) : 1.f;
     }
   }
-  const int nslots = __popcll(slot_mask);
-  // slot number of the i-th set bit of slot_mask (i < nslots)
-  auto nth_slot = [&](int i) {
-    uint64_t m = slot_mask;
-    for (int j = 0; j < i; ++j) m &= m - 1ull;
-    return __ffsll((unsigned long long)m) - 1;
-  };
 
-  for (int sb = 0; sb < nslots; sb += kGemvSlotBatch) {
-    const int S = min(kGemvSlotBatch, nslots - sb);
-    if (sb > 0) __syncthreads();   // the previous batch is done with s_act
-    for (int i = tid; i < S * (K / 8); i += kGemvThreads) {
-      const int s = i / (K / 8), c8 = i - s * (K / 8);
-      const int p = nth_slot(sb + s);
-      const int arow = act_per_slot ? p : p / k;
-      reinterpret_cast<v4i*>(s_act + (size_t)s * K)[c8] =
-          reinterpret_cast<const v4i*>(act + (size_t)arow * K)[c8];
+  for (uint64_t rest = same; rest;) {
+    // the next batch of this expert's slots
+    int p[kGemvSlotBatch];
+    int S = 0;
+#pragma unroll
+    for (int b = 0; b < kGemvSlotBatch; ++b) {
+      p[b] = -1;
+      if (rest) {
+        p[b] = __ffsll((unsigned long long)rest) - 1;
+        rest &= rest - 1ull;
+        S = b + 1;
+      }
     }
-    __syncthreads();
-
-    // one slot at a time: 8 row accumulators live, the weights stay in
-    // registers and are converted again for every slot
-    for (int s = 0; s < S; ++s) {
-      float acc[kGemvRows];
+    float acc[kGemvSlotBatch][kGemvRows];
 #pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) acc[r] = 0.f;
-      const uint16_t* as = s_act + (size_t)s * K;
+    for (int b = 0; b < kGemvSlotBatch; ++b)
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch >= nchunks) break;
-        const v2bf* ap = reinterpret_cast<const v2bf*>(as + ch * kchunk);
-        v2bf av[MXFP4 ? 16 : 8];
+      for (int r = 0; r < kGemvRows; ++r) acc[b][r] = 0.f;
 #pragma unroll
-        for (int i = 0; i < (MXFP4 ? 16 : 8); ++i) av[i] = ap[i];
+    for (int j = 0; j < CH; ++j) {
+      const int ch = tid + kGemvThreads * j;
+      const bool valid = ch < nch;
+      const int chc = min(ch, nch - 1);
+      // this chunk's 16 activations of each slot of the batch
+      v2bf av[kGemvSlotBatch][8];
+#pragma unroll
+      for (int b = 0; b < kGemvSlotBatch; ++b) {
+        const int arow = p[b] < 0 ? 0 : (act_per_slot ? p[b] : p[b] / k);
+        const v4i* ap = reinterpret_cast<const v4i*>(act + (size_t)arow * K + (size_t)chc * 16);
+        const v4i a0 = ap[0], a1 = ap[1];
+        const int w8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) av[b][i] = __builtin_bit_cast(v2bf, w8[i]);
+      }
+      if (valid) {
 #pragma unroll
         for (int r = 0; r < kGemvRows; ++r) {
-          v2bf wp[16];
-          weights_to_bf16<MXFP4>(raw[r][c], wp);
-          float part = 0.f;
+          // converted per batch, row by row (keeps 8 converted registers
+          // live instead of all 16 rows' worth)
+          RawT rw = raw[r][j];
+          asm volatile("" : "+v"(rw));
+          v2bf wp[8];
+          weights_to_bf16(rw, wp);
 #pragma unroll
-          for (int i = 0; i < (MXFP4 ? 16 : 8); ++i)
-            part = __builtin_amdgcn_fdot2_f32_bf16(wp[i], av[i], part, false);
-          acc[r] = MXFP4 ? fmaf(part, gsc[r][c], acc[r]) : acc[r] + part;
+          for (int b = 0; b < kGemvSlotBatch; ++b) {
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              part = __builtin_amdgcn_fdot2_f32_bf16(wp[i], av[b][i], part, false);
+            acc[b][r] = MXFP4 ? fmaf(part, gsc[r][j], acc[b][r]) : acc[b][r] + part;
+          }
         }
       }
-      // fold, epilogue (scale, bias, bf16), GLU, store
-      const int p = nth_slot(sb + s);
+    }
+    // fold: inside the wave (DPP, lane 63), then the 4 waves in order
 #pragma unroll
-      for (int r = 0; r < kOuts; ++r) {
-        const int j = col0 + r;
+    for (int b = 0; b < kGemvSlotBatch; ++b)
+#pragma unroll
+      for (int r = 0; r < kGemvRows; ++r) {
+        const float v = wave_sum_to_lane63(acc[b][r]);
+        if (lane == 63) s_red[wid][b][r] = v;
+      }
+    __syncthreads();
+    // epilogue: thread (b, c) owns output column c of slot b
+    if (tid < kGemvSlotBatch * kOuts) {
+      const int b = tid / kOuts, c = tid % kOuts;
+      const int j = col0 + c;
+      if (b < S && j < n_out) {
         float y[2];
 #pragma unroll
         for (int hf = 0; hf < (GLU ? 2 : 1); ++hf) {
-          const int rr = r + hf * kOuts;
+          const int rr = c + hf * kOuts;
           const int n = row_of(rr);
+          float tot = s_red[0][b][rr];
+#pragma unroll
+          for (int w = 1; w < kGemvWaves; ++w) tot += s_red[w][b][rr];
           const float bv = bias ? bf16_to_f32(bias[(size_t)e * N + n]) : 0.f;
-          const float tot = wave_sum_f32(acc[rr]);
           const float yv = MXFP4 ? __fadd_rn(tot, bv) : __fadd_rn(__fmul_rn(tot, fp8_scale), bv);
           y[hf] = bf16_to_f32((uint16_t)f32_to_bf16_bits(yv));
         }
-        if (lane == 0 && j < n_out) {
-          const float v = GLU ? glu_apply(y[0], y[1], alpha, beta, limit) : y[0];
-          out[(size_t)p * n_out + j] = (uint16_t)f32_to_bf16_bits(v);
-        }
+        const float v = GLU ? glu_apply(y[0], y[1], alpha, beta, limit) : y[0];
+        out[(size_t)p[b] * n_out + j] = (uint16_t)f32_to_bf16_bits(v);
       }
     }
+    if (rest) __syncthreads();   // s_red is reused by the next batch
   }
 }
 
@@ -209,27 +245,22 @@ extern "C" int moe_sparse_gemv(const uint16_t* act, int act_per_slot, const int3
   if (K % 8 != 0) return MOE_ERR_ALIGN;
   if (glu && N % 2 != 0) return MOE_ERR_ALIGN;
   if (act_per_slot != 0 && act_per_slot != 1) return MOE_ERR_UNSUPPORTED;
-  const size_t lds = (size_t)kGemvSlotBatch * K * sizeof(uint16_t);
-  const int kchunk = wfmt == MOE_W_MXFP4_G32 ? 32 : 16;
-  const int chunks_per_lane = (K / kchunk + 63) / 64;
-  if (chunks_per_lane > kGemvMaxChunks) return MOE_ERR_SHAPE;  // K <= 4096 (FP8) / 8192 (MXFP4)
-  if (lds > 64 * 1024) return MOE_ERR_SHAPE;
+  const int chunks_per_thread = (K / 16 + kGemvThreads - 1) / kGemvThreads;
+  if (chunks_per_thread > kGemvMaxCh) return MOE_ERR_SHAPE;  // K <= 8192
   if (T == 0) return MOE_OK;
   if (!act || !topk_ids || !w || !w_scale || !out) return MOE_ERR_NULL;
   const int n_out = glu ? N / 2 : N;
-  const int outs_per_block = kGemvWaves * (glu ? kGemvRows / 2 : kGemvRows);
+  const int outs_per_block = glu ? kGemvRows / 2 : kGemvRows;
   dim3 grid((n_out + outs_per_block - 1) / outs_per_block, T * k);
   hipStream_t st = (hipStream_t)stream;
-#define MOE_GEMV_LAUNCH(MX, G, CHN)                                                             \
-  hipLaunchKernelGGL((sparse_gemv_kernel<MX, G, CHN>), grid, dim3(kGemvThreads), lds, st, act,  \
+#define MOE_GEMV_LAUNCH(MX, G, CHN)                                                            \
+  hipLaunchKernelGGL((sparse_gemv_kernel<MX, G, CHN>), grid, dim3(kGemvThreads), 0, st, act,  \
                      act_per_slot, topk_ids, T, k, expert_start, E_local, N, K, w, w_scale, bias, \
                      glu_alpha, glu_beta, glu_limit, out, slot_row)
 #define MOE_GEMV_CH(MX, G)                       \
-  switch (chunks_per_lane) {                     \
+  switch (chunks_per_thread) {                   \
     case 1: MOE_GEMV_LAUNCH(MX, G, 1); break;    \
-    case 2: MOE_GEMV_LAUNCH(MX, G, 2); break;    \
-    case 3: MOE_GEMV_LAUNCH(MX, G, 3); break;    \
-    default: MOE_GEMV_LAUNCH(MX, G, 4); break;   \
+    default: MOE_GEMV_LAUNCH(MX, G, 2); break;   \
   }
   const bool mx = wfmt == MOE_W_MXFP4_G32;
   if (mx && glu) MOE_GEMV_CH(true, true)
