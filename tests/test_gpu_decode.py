@@ -91,3 +91,29 @@ def test_decode_windows_skip_not_zero(ops):
     full = M.decode_chain(c, 0, 32, ids=ids, weights=wts)
     total = parts[0] + parts[1]
     assert np.allclose(total, _bf(full.out), rtol=2e-2, atol=1e-2 * np.abs(_bf(full.out)).max())
+
+
+@pytest.mark.parametrize("wfmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("H", [2880, 4608])
+def test_decode_wide_rows_many_slots(ops, wfmt, H):
+    """Full-width rows (K = 2880: the 180 weight chunks of a row end inside
+    the block's third wave; K = 4608: two chunks per thread) and every
+    token routed to both local experts, so each expert serves 8 slots in
+    several slot batches."""
+    say(f"decode wide {wfmt} H={H}")
+    c = W.decode(T=8, H=H, experts=2, wfmt=wfmt)
+    c.logits = c.logits.copy()
+    c.logits[:, :2] += 8.0
+    ids, wts = M.route_softmax(c.logits, c.k)
+    assert np.all((ids == 0).any(axis=1) & (ids == 1).any(axis=1))
+    ref = M.decode_chain(c, 0, 2, ids=ids, weights=wts)
+    buf = ops.alloc_decode(8, c.k, c.H, fill=True)
+    y = ops.moe_ffn_decode(dev_bf16(c.x), dev(ids), dev(wts), 0, 2, wfmt, *_dev_case(c, slice(0, 2)),
+                           buf)
+    slot_row = host(buf.slot_row)
+    assert np.array_equal(slot_row, ref.slot_row)
+    act = host(buf.act)
+    for (t, s), a in ref.act.items():
+        _check_stage(act[t * c.k + s], a)
+    ok, mx, mean = end_to_end_ok(host(y), ref.out)
+    assert ok, (mx, mean)
