@@ -42,7 +42,10 @@ constexpr int kActWaves = kActThreads / 64;
 constexpr int kActBatch = 8;       // items per wave per batch
 constexpr int kActMaxE = 1024;
 constexpr int kActMaxWordsPerRow = 64;  // I <= 8192
-constexpr int kActMaxRowsPerBlock = 2048;  // live rows per block (M_cap <= 256 * 2048)
+// live rows per block (M_cap <= 256 * 12288); the 48 KB this takes also keeps
+// the block alone on its CU (over 80 KB of LDS), so that no CU runs two of
+// the 256 equal shares
+constexpr int kActMaxRowsPerBlock = 12288;
 constexpr uint32_t kActOob = 0x80000000u;
 
 __device__ int act_block_scan(int v, int* tmp) {
@@ -75,31 +78,43 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
-  // the sigmoid table's loads go out first (loads complete in order)
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // this thread's two experts' endpoints go out first, then the sigmoid
+  // table; loads complete in order, so the scan waits only for the
+  // endpoints. Unpredicated (clamped) so that the waits count exactly.
+  int endv[2], prevv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = min(2 * tid + j, max(E_local - 1, 0));
+    endv[j] = expert_ends[e];
+    prevv[j] = expert_ends[max(e - 1, 0)];
+  }
+  __builtin_amdgcn_sched_barrier(0);     // keep the endpoints ahead of the table
   static_assert(MOE_SIGMOID_TABLE_SIZE % 4 == 0, "table copied as 16-byte vectors");
   constexpr int kVec = MOE_SIGMOID_TABLE_SIZE / 4;
   constexpr int kPer = (kVec + kActThreads - 1) / kActThreads;
   v4i tv[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int i = tid + j * kActThreads;
-    tv[j] = i < kVec ? reinterpret_cast<const v4i*>(g_sigmoid_table)[i] : v4i{0, 0, 0, 0};
+    // each block starts at its own place in the table, so that the 32 CUs
+    // of a cache slice do not all ask for the same lines at once
+    int i = tid + j * kActThreads + (int)(blockIdx.x * 97u % (unsigned)kVec);
+    i = i >= kVec ? i - kVec : i;
+    tv[j] = reinterpret_cast<const v4i*>(g_sigmoid_table)[min(i, kVec - 1)];
   }
-  // expert ranges and the exclusive scan of their live-row counts (2 per thread)
+  // expert ranges (start_e = align_up(end_{e-1}, A), clamped into [0, M_cap]
+  // so that corrupt endpoints cannot leave the buffers) and the exclusive
+  // scan of their live-row counts (2 experts per thread)
   int cnt[2], st[2];
   int sum = 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int e = 2 * tid + j;
-    cnt[j] = 0;
-    st[j] = 0;
-    if (e < E_local) {
-      int s, en;
-      expert_range(expert_ends, e, A, M_cap, s, en);
-      st[j] = s;
-      cnt[j] = en - s;
-    }
+    const int prev = e == 0 ? 0 : min(max(prevv[j], 0), M_cap);
+    const int s0 = min(align_up_dev(prev, A), M_cap);
+    const int en = min(max(endv[j], s0), M_cap);
+    st[j] = s0;
+    cnt[j] = e < E_local ? en - s0 : 0;
     sum += cnt[j];
   }
   int run = act_block_scan(sum, s_tmp);
@@ -146,18 +161,27 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(gateup), (short)0, (int)((uint32_t)M_cap * (uint32_t)(4 * I)), 0x00020000);
 
-  // item it of this block: local live row it / nchunks, chunk it % nchunks
+  // item it of this block: local live row it / nchunks, chunk it % nchunks.
+  // The batch's 8 items are resolved together: lane j < 8 finds item j's
+  // row and byte offset (one LDS read for all), then each load takes its
+  // offset from that lane.
   auto load_batch = [&](int b, v4i* G, v4i* U) {
-#pragma unroll
-    for (int j = 0; j < kActBatch; ++j) {
-      const int it = (b * kActBatch + j) * kActWaves + wid;
-      uint32_t off = kActOob;
+    uint32_t my_off = kActOob, my_colb = 0;
+    if (lane < kActBatch) {
+      const int it = (b * kActBatch + lane) * kActWaves + wid;
       if (it < items) {
         int rl, ch;
         split(it, rl, ch);
-        const int col = ch * 512 + lane * 8;
-        if (col < I) off = (uint32_t)s_rows[rl] * (uint32_t)(4 * I) + (uint32_t)col * 2u;
+        my_colb = (uint32_t)ch * 1024u;                     // chunk start, bytes into the gate half
+        my_off = (uint32_t)s_rows[rl] * (uint32_t)(4 * I) + my_colb;
       }
+    }
+#pragma unroll
+    for (int j = 0; j < kActBatch; ++j) {
+      const uint32_t base = __builtin_amdgcn_readlane(my_off, j);
+      const uint32_t colb = __builtin_amdgcn_readlane(my_colb, j) + (uint32_t)lane * 16u;
+      const uint32_t off = (base != kActOob && colb < (uint32_t)I * 2u) ? base + (uint32_t)lane * 16u
+                                                                          : kActOob;
       G[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
       U[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off == kActOob ? kActOob : off + (uint32_t)I * 2u, 0, 0);
     }
@@ -208,21 +232,25 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     }
   };
 
+  // batch loads are unconditional (items past the end read out of range,
+  // which returns zeros and touches no memory), so every wait counts loads
+  // exactly: the table's stores below wait only for the table
   v4i GA[kActBatch], UA[kActBatch], GB[kActBatch], UB[kActBatch];
-  if (nbatch > 0) load_batch(0, GA, UA);
+  load_batch(0, GA, UA);
   // the table goes to LDS while the first batch is in flight (it waits only
   // for the table's own loads, which were issued first)
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int i = tid + j * kActThreads;
-    if (i < kVec) reinterpret_cast<v4i*>(s_tab)[i] = tv[j];
+    int i = tid + j * kActThreads + (int)(blockIdx.x * 97u % (unsigned)kVec);
+    i = i >= kVec ? i - kVec : i;
+    if (tid + j * kActThreads < kVec) reinterpret_cast<v4i*>(s_tab)[i] = tv[j];
   }
   __syncthreads();
   for (int b = 0; b < nbatch; b += 2) {
-    if (b + 1 < nbatch) load_batch(b + 1, GB, UB);
+    load_batch(b + 1, GB, UB);
     compute_batch(b, GA, UA);
     if (b + 1 >= nbatch) break;
-    if (b + 2 < nbatch) load_batch(b + 2, GA, UA);
+    load_batch(b + 2, GA, UA);
     compute_batch(b + 1, GB, UB);
   }
 }
