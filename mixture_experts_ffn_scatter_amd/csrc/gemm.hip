@@ -32,14 +32,16 @@
 // block), so that one k-step of a 256-column tile's scales is 16 contiguous
 // bytes per lane and a wave reads its 4 column blocks' scales as one word.
 //
-// Work decomposition. An item is (n-tile of 256 columns, expert, m-chunk of
-// up to 128 live rows). Items are listed n-tile-major and the list is cut
-// into 8 equal contiguous ranges, one per XCD (block b runs on XCD b % 8);
-// the blocks of an XCD take its items round-robin, so the m-chunks of one
-// (expert, n-tile) run side by side on one XCD and share its weight slice
-// in that L2, and every XCD streams about 1/8 of the weights. The list is
-// rebuilt inside every block from expert_ends (a block-wide scan), so the
-// grid depends only on host-known sizes and no count is read back.
+// Work decomposition. An item is (expert, n-tile of 256 columns, m-chunk of
+// up to 128 live rows). Items are listed expert-major (n-tile-major inside
+// an expert) and the list is cut into 8 equal contiguous ranges, one per
+// XCD (block b runs on XCD b % 8); the blocks of an XCD take its items
+// round-robin, so the items running at once on one XCD share activation
+// chunks (one expert, neighbouring n-tiles) and weight slices (one n-tile,
+// its m-chunks) in that XCD's L2, and every XCD streams about 1/8 of the
+// weights. The list is rebuilt inside every block from expert_ends (a
+// block-wide scan), so the grid depends only on host-known sizes and no
+// count is read back.
 //
 // Data path. Every operand travels global -> LDS by the buffer-to-LDS
 // transfer of gfx950 (no register staging) into a ring of 4 stages of one
