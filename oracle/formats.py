@@ -242,3 +242,43 @@ def sigmoid_f32(x) -> np.ndarray:
     for i in risky:
         out[i] = _decimal_to_f32_rne(sigmoid_exact_decimal(float(x32.ravel()[i])))
     return out.reshape(x32.shape)
+
+
+def scaled_tanh_exact_decimal(x: float, beta: float, prec: int = 120) -> Decimal:
+    """beta * tanh(x / beta) in decimal arithmetic, as (1 - e^(-2y)) /
+    (1 + e^(-2y)) for y = |x| / beta (120 digits, so that the cancellation in
+    1 - e^(-2y) for the smallest bf16 inputs still leaves far more than
+    fp32's precision)."""
+    getcontext().prec = prec
+    b = Decimal(float(beta))
+    y = Decimal(float(x)) / b
+    neg = y < 0
+    y = -y if neg else y
+    e = (-2 * y).exp()               # e^(-2y) <= 1 never overflows
+    t = (1 - e) / (1 + e)
+    return -(b * t) if neg else b * t
+
+
+def scaled_tanh_f32(x, beta: float) -> np.ndarray:
+    """Correctly rounded fp32 of beta * tanh(x / beta) for fp32 inputs (the
+    two factors of the SiTU activation, "DeepGEMM FusedMoE on Blackwell
+    (sglang)", section 2.4.1, situ branch: gate factor with beta = 4, up
+    factor with beta = 25 for Kimi-K3).
+
+    Evaluated in fp64; where the fp64 value lies too close to an fp32
+    rounding midpoint for fp64's error to be ruled out, it is recomputed
+    with decimal arithmetic and rounded exactly."""
+    x32 = np.asarray(x, dtype=np.float32)
+    xd = x32.astype(np.float64)
+    s = beta * np.tanh(xd / beta)
+    r = s.astype(np.float32)
+    lo = np.nextafter(r, np.float32(-np.inf)).astype(np.float64)
+    hi = np.nextafter(r, np.float32(np.inf)).astype(np.float64)
+    rd = r.astype(np.float64)
+    margin = np.minimum(np.abs(s - (rd + lo) / 2.0), np.abs(s - (rd + hi) / 2.0))
+    bound = 16.0 * np.spacing(np.maximum(np.abs(s), 2.0 ** -1022))
+    risky = np.flatnonzero((margin <= bound).ravel() & np.isfinite(xd).ravel())
+    out = r.ravel().copy()
+    for i in risky:
+        out[i] = _decimal_to_f32_rne(scaled_tanh_exact_decimal(float(x32.ravel()[i]), beta))
+    return out.reshape(x32.shape)

@@ -16,6 +16,9 @@ Parity pins (see ``tests/test_oracle_*.py``):
   brute-force coverage over small count vectors.
 * ``act_quant_rows`` - torch's e4m3 cast and decimal arithmetic pin the
   format and sigmoid steps; special cases pin the activation.
+* ``act_quant_rows_situ`` - the scaled tanh against 120-digit decimal
+  evaluation and its closed-form properties over every bf16 input; the
+  activation's special cases and an fp64 evaluation of the formula.
 * ``mx_gemm`` - an independent pure-Python nibble/byte triple loop, one-hot
   rows and scale doubling.
 * ``combine`` - identity and skip cases; the token-major chain.
@@ -32,7 +35,7 @@ import numpy as np
 
 from .formats import (E2M1_VALUES, E4M3_VALUES, bf16_to_f32, e2m1_decode, e2m1_unpack,
                       e4m3_decode, e8m0_decode, pack_ue8m0_words, quant_mx_e4m3, round_to_bf16,
-                      sigmoid_f32)
+                      scaled_tanh_f32, sigmoid_f32)
 
 GROUP = 32
 
@@ -187,6 +190,41 @@ def act_quant_rows(gateup_bits: np.ndarray, I: int, clamp: float = 0.0):
     live-row boundary", sections 1-3: the activation kernel covers only
     [start, end) and leaves padding unwritten)."""
     return quant_mx_e4m3(act_rows_f32(gateup_bits, I, clamp), GROUP)
+
+
+SITU_BETA_GATE = 4.0     # Kimi-K3's SiTU parameters ("Kimi-K3 on SM120
+SITU_BETA_UP = 25.0      # FlashInfer MXFP4": situ_beta 4, situ_linear_beta 25)
+
+
+def act_rows_f32_situ(gateup_bits: np.ndarray, I: int, beta_g: float = SITU_BETA_GATE,
+                      beta_u: float = SITU_BETA_UP) -> np.ndarray:
+    """SiTU of gate/up rows, kept in fp32 ("DeepGEMM FusedMoE on Blackwell
+    (sglang)", section 2.4.1, situ branch; "Kimi-K3 on SM120 FlashInfer
+    MXFP4", the reference formula):
+
+      gate' = beta_g * tanh(g / beta_g) * sigmoid(g),  up' = beta_u * tanh(u / beta_u)
+      h = gate' * up'
+
+    taken as the fixed fp32 sequence (every function value correctly rounded
+    to fp32, each product rounded once):
+      t = fl32(beta_g tanh(g / beta_g)), sig = fl32(sigmoid(g)),
+      a = fl32(t * sig), v = fl32(beta_u tanh(u / beta_u)), h = fl32(a * v).
+    No clamp: the clamp belongs to the SiLU branch."""
+    gu = bf16_to_f32(gateup_bits)
+    g = gu[..., :I].astype(np.float32)
+    u = gu[..., I:2 * I].astype(np.float32)
+    t = scaled_tanh_f32(g, beta_g)
+    sig = sigmoid_f32(g)
+    a = (t * sig).astype(np.float32)
+    v = scaled_tanh_f32(u, beta_u)
+    return (a * v).astype(np.float32)
+
+
+def act_quant_rows_situ(gateup_bits: np.ndarray, I: int, beta_g: float = SITU_BETA_GATE,
+                        beta_u: float = SITU_BETA_UP):
+    """SiTU + FP8/UE8M0 quantisation of live rows, with the same group-32
+    ceil-then-divide quantiser as the SiLU path."""
+    return quant_mx_e4m3(act_rows_f32_situ(gateup_bits, I, beta_g, beta_u), GROUP)
 
 
 def scales_mn_major(bytes_rows: np.ndarray, rows: np.ndarray, M_cap: int, fill=None):
