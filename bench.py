@@ -15,7 +15,8 @@ The same line carries:
                 duration measured by HIP events around it in the timed loop
   kernels       per-kernel durations, algorithmic bytes / FLOP, GB/s, TFLOP/s
   actquant      the standalone live-row act-quant benchmark (3,072 live of
-                28,672 rows, width 2,048) and its full-buffer control, cold
+                28,672 rows, width 2,048; SiLU and SiTU) and its full-buffer
+                control, cold
   decode        the sparse decode path at 1 and 8 tokens (FP8 and MXFP4)
   cpu_baseline  the CPU oracle timed on the host on the same layer
 
@@ -301,27 +302,31 @@ def bench_actquant(ops, torch, up, up_bf16, log, iters=20):
         hs = torch.empty((case.I // 128, case.M_cap), dtype=torch.int32, device="cuda")
         R = int(case.counts.sum())
         B = R * (2 * case.I * 2 + case.I + case.I // 32) + 4 * case.E_local
-        for _ in range(3):
-            ops.moe_act_quant_liverows(gate, ends, case.A, 0.0, hq, hs)
-        cold, warm = [], []
-        for i in range(iters):
-            _flush_caches(torch, scratch)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            ops.moe_act_quant_liverows(gate, ends, case.A, 0.0, hq, hs)
-            e1.record()
-            e2 = torch.cuda.Event(enable_timing=True)
-            ops.moe_act_quant_liverows(gate, ends, case.A, 0.0, hq, hs)
-            e2.record()
-            torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1) * 1e3)
-            warm.append(e1.elapsed_time(e2) * 1e3)
-        t = float(np.median(cold))
-        key = "full_28672_rows" if full else "live_3072_of_28672"
-        out[key] = {"us_cold_median": round(t, 3), "us_warm_median": round(float(np.median(warm)), 3),
-                    "alg_bytes": int(B), "GBps_cold": round(B / (t * 1e-6) / 1e9, 1),
-                    "hbm_frac_cold": round(B / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "live_rows": R}
-        log("actquant", key, out[key])
+        calls = [("", lambda: ops.moe_act_quant_liverows(gate, ends, case.A, 0.0, hq, hs))]
+        if not full:   # the SiTU activation (Kimi-K3's 4 / 25) on the live layout
+            calls.append(("_situ", lambda: ops.moe_act_quant_liverows_situ(gate, ends, case.A, hq, hs)))
+        for suffix, call in calls:
+            for _ in range(3):
+                call()
+            cold, warm = [], []
+            for i in range(iters):
+                _flush_caches(torch, scratch)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                e2 = torch.cuda.Event(enable_timing=True)
+                call()
+                e2.record()
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1) * 1e3)
+                warm.append(e1.elapsed_time(e2) * 1e3)
+            t = float(np.median(cold))
+            key = ("full_28672_rows" if full else "live_3072_of_28672") + suffix
+            out[key] = {"us_cold_median": round(t, 3), "us_warm_median": round(float(np.median(warm)), 3),
+                        "alg_bytes": int(B), "GBps_cold": round(B / (t * 1e-6) / 1e9, 1),
+                        "hbm_frac_cold": round(B / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "live_rows": R}
+            log("actquant", key, out[key])
         del gate, hq, hs
     del scratch
     torch.cuda.empty_cache()

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 enum moe_status {
     MOE_OK = 0,
@@ -263,6 +263,26 @@ int moe_grouped_gemm1(const uint8_t* xq, const int32_t* xs, const int32_t* exper
 int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends, int E_local,
                            int A, int M_cap, int I, float clamp_limit,
                            uint8_t* hq, int32_t* hs, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_act_quant_liverows_situ - moe_act_quant_liverows with the SiTU
+ * activation instead of SiLU.
+ * [SGL] section 2.4.1, situ branch (gate' = b_s tanh(g/b_s) sigmoid(g),
+ * up' = b_l tanh(u/b_l), then gate' * up' and the group quantisation);
+ * [KIMI] (Kimi-K3's reference formula with b_s = 4, b_l = 25).
+ *
+ *   gateup, expert_ends, E_local, A, M_cap, I, hq, hs
+ *                as for moe_act_quant_liverows
+ *   situ_beta, situ_linear_beta  must be 4.0 and 25.0 (the function tables
+ *                are built for these; anything else is MOE_ERR_UNSUPPORTED)
+ * Per element: t = 4 tanh(g/4), s = sigmoid(g), v = 25 tanh(u/25), each
+ * rounded to fp32; h = fl32(fl32(t*s) * v); then the per-32 quantisation
+ * of moe_scatter_endpoints on h. No clamp. Same limits as
+ * moe_act_quant_liverows.
+ * ------------------------------------------------------------------------ */
+int moe_act_quant_liverows_situ(const uint16_t* gateup, const int32_t* expert_ends, int E_local,
+                                int A, int M_cap, int I, float situ_beta, float situ_linear_beta,
+                                uint8_t* hq, int32_t* hs, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_grouped_gemm2 - down projection of every live row with its expert's

@@ -10,7 +10,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 c_int, c_i64, c_size, c_float, c_void = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
                                          ctypes.c_float, ctypes.c_void_p)
@@ -32,6 +32,8 @@ SIGNATURES = {
                                   c_void, c_void, c_void, c_void]),
     "moe_act_quant_liverows": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, c_float,
                                        c_void, c_void, c_void]),
+    "moe_act_quant_liverows_situ": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, c_float,
+                                            c_float, c_void, c_void, c_void]),
     "moe_grouped_gemm2": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                   c_void, c_void, c_void, c_void]),
     "moe_combine": (c_int, [c_void, c_i64, c_void, c_void, c_int, c_int, c_int, c_float, c_void,

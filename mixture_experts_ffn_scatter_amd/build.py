@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library ``libmoe_ffn.so`` in-tree.
 
-Steps: compile and run the host generator of the sigmoid table, compile
+Steps: compile and run the host generators of the sigmoid and SiTU tables, compile
 every ``csrc/*.hip`` with hipcc for gfx950 (in parallel), link one shared
 library next to this file. Run ``python -m mixture_experts_ffn_scatter_amd.build``.
 """
@@ -36,15 +36,18 @@ def _run(cmd):
 
 
 def generate_tables():
+    """The sigmoid table and the SiTU scaled-tanh tables, from their host
+    generators (long double; each checks its own rounding margins)."""
     os.makedirs(GEN, exist_ok=True)
-    exe = os.path.join(BUILD, "gen_sigmoid_table")
-    _run(["g++", "-O2", "-std=c++17", "-ffp-contract=off",
-          os.path.join(CSRC, "gen_sigmoid_table.cpp"), "-o", exe])
-    out = _run([exe])
-    path = os.path.join(GEN, "sigmoid_table.inc")
-    with open(path + ".tmp", "w") as f:
-        f.write(out)
-    os.replace(path + ".tmp", path)
+    for gen, inc in (("gen_sigmoid_table", "sigmoid_table.inc"), ("gen_situ_table", "situ_table.inc")):
+        exe = os.path.join(BUILD, gen)
+        _run(["g++", "-O2", "-std=c++17", "-ffp-contract=off",
+              os.path.join(CSRC, gen + ".cpp"), "-o", exe])
+        out = _run([exe])
+        path = os.path.join(GEN, inc)
+        with open(path + ".tmp", "w") as f:
+            f.write(out)
+        os.replace(path + ".tmp", path)
 
 
 def compile_one(src):

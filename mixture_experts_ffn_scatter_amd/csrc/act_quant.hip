@@ -18,6 +18,14 @@
 // (amax by two shuffles), a packed scale word spans 16 lanes and is stored
 // by its first lane (MN-major).
 //
+// moe_act_quant_liverows_situ runs the same kernel with the SiTU activation
+// of "DeepGEMM FusedMoE on Blackwell (sglang)", section 2.4.1 (situ branch)
+// with Kimi-K3's parameters ("Kimi-K3 on SM120 FlashInfer MXFP4"):
+//   t = 4 tanh(g/4), v = 25 tanh(u/25), each correctly rounded to fp32 and
+//   looked up in LDS by the bf16 pattern (rows of exponents where the value
+//   is neither the input itself nor +-b; generated at build time),
+//   h = (t * sigma(g)) * v, no clamp.
+//
 // Arithmetic per element, all IEEE fp32 with no contraction:
 //   g = bf16 gate, u = bf16 up; optional clamp g = min(g, L), u = med3(u, -L, L)
 //   sig = sigma(g) correctly rounded (looked up in LDS by g's bf16 pattern)
@@ -33,9 +41,26 @@ namespace moe {
 // sigma(g) for every bf16 g, generated at build time (gen_sigmoid_table.cpp)
 #define MOE_SIGMOID_TABLE_STORAGE __device__ const __attribute__((aligned(16)))
 #include "sigmoid_table.inc"
+// b*tanh(x/b) for every bf16 x, b = 4 and 25 (gen_situ_table.cpp)
+#define MOE_SITU_TABLE_STORAGE __device__ const __attribute__((aligned(16)))
+#include "situ_table.inc"
 }  // namespace moe
 #include "sigmoid_lookup.h"
 namespace moe {
+
+// b*tanh(x/b) for a bf16-valued x: x itself below exponent field LO, +-b
+// above HI (both checked over every bf16 pattern by the generator), the
+// table row in between.
+template <int LO, int HI>
+__device__ __forceinline__ float scaled_tanh_lookup(const float* tab, float x, float b) {
+  const uint32_t bits = __float_as_uint(x) >> 16;   // x is an exact bf16 value
+  const int ex = (int)((bits >> 7) & 0xFFu);
+  const uint32_t neg = bits >> 15;
+  const int idx = (int)neg * ((HI - LO + 1) * 128) + (min(max(ex, LO), HI) - LO) * 128 +
+                  (int)(bits & 0x7Fu);
+  const float tv = tab[idx];
+  return ex < LO ? x : (ex > HI ? (neg ? -b : b) : tv);
+}
 
 constexpr int kActThreads = 512;   // 8 waves
 constexpr int kActWaves = kActThreads / 64;
@@ -65,11 +90,15 @@ __device__ int act_block_scan(int v, int* tmp) {
   return off + incl - v;
 }
 
-template <bool CLAMP>
+// SITU: the SiTU activation (Kimi-K3's b_s = 4, b_l = 25) instead of SiLU,
+// with its two scaled-tanh tables beside the sigmoid table in LDS; no clamp.
+template <bool CLAMP, bool SITU>
 __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     const uint16_t* __restrict__ gateup, const int32_t* __restrict__ expert_ends, int E_local,
     int A, int M_cap, int I, float L, uint8_t* __restrict__ hq, int32_t* __restrict__ hs) {
   __shared__ __attribute__((aligned(16))) float s_tab[MOE_SIGMOID_TABLE_SIZE];
+  __shared__ __attribute__((aligned(16))) float s_t4[SITU ? MOE_TANH4_TABLE_SIZE : 4];
+  __shared__ __attribute__((aligned(16))) float s_t25[SITU ? MOE_TANH25_TABLE_SIZE : 4];
   __shared__ int s_start[kActMaxE];   // first row of expert e
   __shared__ int s_pref[kActMaxE];    // live rows of the experts before e
   __shared__ int s_tmp[kActWaves];
@@ -102,6 +131,15 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     i = i >= kVec ? i - kVec : i;
     tv[j] = reinterpret_cast<const v4i*>(g_sigmoid_table)[min(i, kVec - 1)];
   }
+  static_assert(MOE_TANH4_TABLE_SIZE % (4 * kActThreads) == 0 &&
+                MOE_TANH25_TABLE_SIZE % (4 * kActThreads) == 0, "whole 16-byte vectors per thread");
+  constexpr int kPer4 = SITU ? MOE_TANH4_TABLE_SIZE / (4 * kActThreads) : 0;
+  constexpr int kPer25 = SITU ? MOE_TANH25_TABLE_SIZE / (4 * kActThreads) : 0;
+  v4i t4v[kPer4 > 0 ? kPer4 : 1], t25v[kPer25 > 0 ? kPer25 : 1];
+#pragma unroll
+  for (int j = 0; j < kPer4; ++j) t4v[j] = reinterpret_cast<const v4i*>(g_tanh4_table)[tid + j * kActThreads];
+#pragma unroll
+  for (int j = 0; j < kPer25; ++j) t25v[j] = reinterpret_cast<const v4i*>(g_tanh25_table)[tid + j * kActThreads];
   // expert ranges (start_e = align_up(end_{e-1}, A), clamped into [0, M_cap]
   // so that corrupt endpoints cannot leave the buffers) and the exclusive
   // scan of their live-row counts (2 experts per thread)
@@ -209,8 +247,16 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
           uv = fminf(fmaxf(uv, -L), L);
         }
         const float sig = sigmoid_lookup_table(s_tab, gv);
-        const float sg = gv * sig;
-        h[q] = sg * uv;
+        if (SITU) {
+          // h = fl32(fl32(4 tanh(g/4) * sigma(g)) * 25 tanh(u/25))
+          const float t = scaled_tanh_lookup<MOE_TANH4_EXP_LO, MOE_TANH4_EXP_HI>(s_t4, gv, 4.0f);
+          const float a = t * sig;
+          const float v = scaled_tanh_lookup<MOE_TANH25_EXP_LO, MOE_TANH25_EXP_HI>(s_t25, uv, 25.0f);
+          h[q] = a * v;
+        } else {
+          const float sg = gv * sig;
+          h[q] = sg * uv;
+        }
         amax = fmaxf(amax, fabsf(h[q]));
       }
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
@@ -245,6 +291,10 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     i = i >= kVec ? i - kVec : i;
     if (tid + j * kActThreads < kVec) reinterpret_cast<v4i*>(s_tab)[i] = tv[j];
   }
+#pragma unroll
+  for (int j = 0; j < kPer4; ++j) reinterpret_cast<v4i*>(s_t4)[tid + j * kActThreads] = t4v[j];
+#pragma unroll
+  for (int j = 0; j < kPer25; ++j) reinterpret_cast<v4i*>(s_t25)[tid + j * kActThreads] = t25v[j];
   __syncthreads();
   for (int b = 0; b < nbatch; b += 2) {
     load_batch(b + 1, GB, UB);
@@ -257,9 +307,11 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
 
 }  // namespace moe
 
-extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends,
-                                      int E_local, int A, int M_cap, int I, float clamp_limit,
-                                      uint8_t* hq, int32_t* hs, void* stream) {
+namespace {
+
+// shapes and limits shared by the SiLU and SiTU entry points
+int act_quant_check(const uint16_t* gateup, const int32_t* expert_ends, int E_local, int A,
+                    int M_cap, int I, uint8_t* hq, int32_t* hs) {
   using namespace moe;
   if (E_local < 0 || E_local > kActMaxE || A < 1 || M_cap < 0 || I <= 0) return MOE_ERR_SHAPE;
   if (I % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
@@ -268,6 +320,17 @@ extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* exp
   // at most kActMaxRowsPerBlock live rows per block
   if ((long long)M_cap * I * 4 >= (1LL << 31)) return MOE_ERR_SHAPE;
   if (M_cap > 256 * kActMaxRowsPerBlock) return MOE_ERR_SHAPE;
+  if (E_local == 0 || M_cap == 0) return MOE_OK;
+  if (!gateup || !expert_ends || !hq || !hs) return MOE_ERR_NULL;
+  return 1;   // launch
+}
+
+}  // namespace
+
+extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends,
+                                      int E_local, int A, int M_cap, int I, float clamp_limit,
+                                      uint8_t* hq, int32_t* hs, void* stream) {
+  using namespace moe;
   bool clamp = false;
   if (clamp_limit > 0.f && clamp_limit < __builtin_inff()) {
     uint32_t bits;
@@ -277,17 +340,31 @@ extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* exp
   } else if (!(clamp_limit <= 0.f) && !(clamp_limit == __builtin_inff())) {
     return MOE_ERR_UNSUPPORTED;  // NaN
   }
-  if (E_local == 0 || M_cap == 0) return MOE_OK;
-  if (!gateup || !expert_ends || !hq || !hs) return MOE_ERR_NULL;
+  const int rc = act_quant_check(gateup, expert_ends, E_local, A, M_cap, I, hq, hs);
+  if (rc <= 0) return rc;
   hipStream_t st = (hipStream_t)stream;
-  // one block per CU (the sigmoid table takes 33 KB of LDS per block)
   const int grid = 256;         // one block per CU; each takes 1/256 of the live rows
   if (clamp)
-    hipLaunchKernelGGL(act_quant_kernel<true>, dim3(grid), dim3(kActThreads), 0, st, gateup,
-                       expert_ends, E_local, A, M_cap, I, clamp_limit, hq, hs);
+    hipLaunchKernelGGL((act_quant_kernel<true, false>), dim3(grid), dim3(kActThreads), 0, st,
+                       gateup, expert_ends, E_local, A, M_cap, I, clamp_limit, hq, hs);
   else
-    hipLaunchKernelGGL(act_quant_kernel<false>, dim3(grid), dim3(kActThreads), 0, st, gateup,
-                       expert_ends, E_local, A, M_cap, I, 0.f, hq, hs);
+    hipLaunchKernelGGL((act_quant_kernel<false, false>), dim3(grid), dim3(kActThreads), 0, st,
+                       gateup, expert_ends, E_local, A, M_cap, I, 0.f, hq, hs);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_act_quant_liverows_situ(const uint16_t* gateup, const int32_t* expert_ends,
+                                           int E_local, int A, int M_cap, int I, float situ_beta,
+                                           float situ_linear_beta, uint8_t* hq, int32_t* hs,
+                                           void* stream) {
+  using namespace moe;
+  // the scaled-tanh tables are built for Kimi-K3's parameters only
+  if (situ_beta != 4.0f || situ_linear_beta != 25.0f) return MOE_ERR_UNSUPPORTED;
+  const int rc = act_quant_check(gateup, expert_ends, E_local, A, M_cap, I, hq, hs);
+  if (rc <= 0) return rc;
+  hipLaunchKernelGGL((act_quant_kernel<false, true>), dim3(256), dim3(kActThreads), 0,
+                     (hipStream_t)stream, gateup, expert_ends, E_local, A, M_cap, I, 0.f, hq, hs);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -225,6 +225,21 @@ def moe_act_quant_liverows(gateup, expert_ends, A: int, clamp_limit: float, hq, 
     check(st, "moe_act_quant_liverows")
 
 
+def moe_act_quant_liverows_situ(gateup, expert_ends, A: int, hq, hs, situ_beta: float = 4.0,
+                                situ_linear_beta: float = 25.0):
+    _req(gateup, "gateup", _BF16)
+    M_cap, twoI = gateup.shape
+    I = twoI // 2
+    E_local = expert_ends.shape[0]
+    _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
+    _req(hq, "hq", (torch.uint8,), (M_cap, I))
+    _req(hs, "hs", (torch.int32,), (I // 128, M_cap))
+    st = lib().moe_act_quant_liverows_situ(_ptr(gateup), _ptr(expert_ends), E_local, A, M_cap, I,
+                                           float(situ_beta), float(situ_linear_beta), _ptr(hq),
+                                           _ptr(hs), _stream())
+    check(st, "moe_act_quant_liverows_situ")
+
+
 def moe_grouped_gemm2(hq, hs, expert_ends, A: int, w2_packed, w2_scale_packed, down):
     M_cap, I = hq.shape
     E_local, H, _ = w2_packed.shape

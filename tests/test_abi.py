@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
     for s in range(0, -8, -1):
         assert lib.moe_status_string(s).decode()
     assert lib.moe_status_string(5).decode() == "unknown status"
@@ -82,6 +82,13 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
                                       NULL, NULL, NULL) == -5
     assert lib.moe_act_quant_liverows(NULL, NULL, 8, 128, 1152, 100, ctypes.c_float(0.0),
                                       NULL, NULL, NULL) == -3
+    # SiTU act-quant: only Kimi-K3's (4, 25); shape checks as for SiLU
+    assert lib.moe_act_quant_liverows_situ(NULL, NULL, 8, 128, 1152, 128, ctypes.c_float(4.0),
+                                           ctypes.c_float(20.0), NULL, NULL, NULL) == -5
+    assert lib.moe_act_quant_liverows_situ(NULL, NULL, 8, 128, 1152, 100, ctypes.c_float(4.0),
+                                           ctypes.c_float(25.0), NULL, NULL, NULL) == -3
+    assert lib.moe_act_quant_liverows_situ(NULL, NULL, 8, 128, 1152, 128, ctypes.c_float(4.0),
+                                           ctypes.c_float(25.0), NULL, NULL, NULL) == -1
     # GEMMs: K not a multiple of 128
     assert lib.moe_grouped_gemm1(NULL, NULL, NULL, 8, 128, 1152, 192, 128, NULL, NULL, NULL,
                                  NULL) == -3
@@ -186,3 +193,32 @@ def test_division_free_scale_byte_equals_rounding_rule():
     # the subnormal-quotient case the division is kept for
     q = np.array([0x04600001], np.uint32).view(np.float32) / np.float32(448.0)
     assert F.ue8m0_ceil_byte(q.astype(np.float32))[0] == 0
+
+
+def test_hip_side_situ_tables_equal_oracle(tmp_path):
+    """The HIP build's scaled-tanh tables (own generator, long double) with
+    their identity / saturation rule outside the kept exponent rows, against
+    the oracle's correctly rounded b * tanh(x / b), for every finite bf16."""
+    from oracle import formats as F
+    exe = tmp_path / "gen"
+    src = os.path.join(ROOT, "mixture_experts_ffn_scatter_amd", "csrc", "gen_situ_table.cpp")
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-ffp-contract=off", src, "-o", str(exe)])
+    txt = subprocess.check_output([str(exe)], text=True)
+    b = np.arange(65536, dtype=np.uint32)
+    ex = (b >> 7) & 0xFF
+    b = b[ex != 0xFF]
+    ex = ex[ex != 0xFF]
+    x = F.bf16_to_f32(b.astype(np.uint16)).astype(np.float32)
+    for beta, name, macro in ((4.0, "g_tanh4_table", "TANH4"), (25.0, "g_tanh25_table", "TANH25")):
+        lo = int(re.search(rf"MOE_{macro}_EXP_LO (\d+)", txt).group(1))
+        hi = int(re.search(rf"MOE_{macro}_EXP_HI (\d+)", txt).group(1))
+        body = txt.split(name)[1].split("};")[0]
+        tab = np.array([int(v, 16) for v in re.findall(r"0x([0-9a-f]{8})u", body)], np.uint32)
+        rows = hi - lo + 1
+        assert tab.size == 2 * rows * 128
+        got = np.where(ex < lo, x.view(np.uint32),
+                       np.where(ex > hi, np.where(b >> 15, np.float32(-beta), np.float32(beta)).view(np.uint32),
+                                tab[(b >> 15) * rows * 128 + (np.clip(ex, lo, hi) - lo) * 128 + (b & 0x7F)]))
+        want = F.scaled_tanh_f32(x, beta).view(np.uint32)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"beta {beta}: {bad.size} differ, first bf16 {[hex(int(v)) for v in b[bad[:4]]]}"

@@ -269,7 +269,58 @@ def test_act_quant_empty_and_all_empty(ops):
     assert np.all(hq == BYTE_SENT) and np.all(hs == WORD_SENT)
 
 
-# -------------------------------------------------------------------- GEMMs
+def _run_act_situ(ops, case):
+    start, end = M.endpoints(case.counts, case.A)
+    hq = torch.full((case.M_cap, case.I), BYTE_SENT, dtype=torch.uint8, device="cuda")
+    hs = torch.full((case.I // 128, case.M_cap), int(WORD_SENT), dtype=torch.int32, device="cuda")
+    ops.moe_act_quant_liverows_situ(dev_bf16(case.gateup), dev(end.astype(np.int32)), case.A, hq, hs)
+    return start, end, host(hq), host(hs)
+
+
+def _check_act_situ(case, start, end, hq, hs, rows):
+    q, b = M.act_quant_rows_situ(case.gateup[rows], case.I)
+    assert np.array_equal(hq[rows], q), "FP8 codes differ"
+    assert np.array_equal(hs[:, rows].T, F.pack_ue8m0_words(b)), "packed scales differ"
+    live = M.live_row_mask(start, end, case.M_cap)
+    assert np.all(hq[~live] == BYTE_SENT)
+    assert np.all(hs[:, ~live] == WORD_SENT)
+
+
+def test_act_quant_situ_liverows_3072_of_28672(ops):
+    """SiTU (Kimi-K3's 4 / 25) on the act-quant layout: bytes equal the
+    oracle's on every live row, padding (NaN-filled) untouched."""
+    say("act-quant SiTU 3072 live of 28672")
+    case = W.actquant()
+    start, end, hq, hs = _run_act_situ(ops, case)
+    live = np.flatnonzero(M.live_row_mask(start, end, case.M_cap))
+    _check_act_situ(case, start, end, hq, hs, live)
+
+
+@pytest.mark.parametrize("side", ["gate", "up"])
+def test_act_quant_situ_every_bf16(ops, side):
+    """Every finite bf16 value as the gate (up = 1) or as the up input
+    (gate = 1), sorted so that each 32-group holds neighbouring magnitudes:
+    the codes then follow each function value, so every row of the tanh
+    and sigmoid tables and both out-of-table rules are exercised."""
+    say(f"act-quant SiTU every bf16 ({side})")
+    b = np.arange(65536, dtype=np.uint32)
+    b = b[((b >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    vals = np.sort(F.bf16_to_f32(b).astype(np.float64))
+    I = 2048
+    rows = -(-vals.size // I)
+    x = np.zeros(rows * I)
+    x[:vals.size] = vals
+    one = np.ones(rows * I)
+    g, u = (x, one) if side == "gate" else (one, x)
+    gateup = np.concatenate([F.round_to_bf16(g.reshape(rows, I)), F.round_to_bf16(u.reshape(rows, I))], 1)
+    counts = np.array([rows], np.int64)
+    case = W.ActQuantCase("situ-every-bf16", 1, I, 128, 128, counts, gateup.astype(np.uint16))
+    case.gateup = np.concatenate([gateup, np.full((128 - rows, 2 * I), 0x7FC1, np.uint16)])
+    start, end, hq, hs = _run_act_situ(ops, case)
+    _check_act_situ(case, start, end, hq, hs, np.arange(rows))
+
+
+# -------------------------------------------------------------------- GEMMs# -------------------------------------------------------------------- GEMMs
 
 def _tiny_state(ops, c, clamp=0.0):
     ids, wts = M.route_softmax(c.logits, c.k)
