@@ -514,6 +514,96 @@ def test_prefill_group_full_size_gemms_sampled(ops):
         assert ok.all(), f"gemm2 expert {e}: {np.count_nonzero(~ok)} outside bound"
 
 
+def test_large_e_full_size_chain_sampled(ops):
+    """The large-expert-count layer at full size (2,048 tokens, top-16 sigmoid
+    + bias over 896 resident experts, H=3,584, I=3,072, clamp 25): endpoints
+    and permutation bit-exact; quantised x, GEMM1, act-quant and GEMM2 on
+    sampled rows of the hottest, a middle and the coldest live expert; the
+    fused GEMM1 + act-quant byte-identical to the two calls over the whole
+    buffer; combine bit-exact on sampled tokens; one token end to end against
+    the token-major chain."""
+    say("large-E full size: generating inputs (15.7 GB of weights)")
+    c = W.large()
+    w = c.weights
+    ids, wts = M.route_sigmoid_bias(c.logits, c.bias, c.k)
+    say("large-E full size: scatter")
+    buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, fill=True)
+    ops.moe_scatter_endpoints(dev(ids), 0, c.E_local, c.A, dev_bf16(c.x), buf.expert_ends,
+                              buf.route_row, buf.xq, buf.xs, buf.workspace)
+    sc = M.scatter_routes(ids, 0, c.E_local, c.A)
+    ends = host(buf.expert_ends)
+    rr = host(buf.route_row)
+    assert np.array_equal(ends, sc.end.astype(np.int32))
+    assert np.array_equal(rr, sc.route_row)
+    say("large-E full size: packing weights, gemm1 / act-quant / gemm2")
+    w13d, s13d = dev(w.w13), dev(w.s13)
+    w13p, s13p = ops.moe_pack_mx_weights(w13d, s13d)
+    w13g, s13g = ops.moe_pack_mx_weights_gateup(w13d, s13d)
+    del w13d, s13d
+    w2d, s2d = dev(w.w2), dev(w.s2)
+    w2p, s2p = ops.moe_pack_mx_weights(w2d, s2d)
+    del w2d, s2d
+    ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, w13p, s13p, buf.gateup)
+    ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, c.clamp, buf.hq, buf.hs)
+    ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, w2p, s2p, buf.down)
+    say("large-E full size: fused gemm1 + act-quant against the two calls")
+    hq2 = torch.full_like(buf.hq, 0xA5)
+    hs2 = torch.full_like(buf.hs, -1515870811)
+    ops.moe_grouped_gemm1_act_quant(buf.xq, buf.xs, buf.expert_ends, c.A, w13g, s13g, c.clamp,
+                                    hq2, hs2)
+    assert torch.equal(hq2, buf.hq) and torch.equal(hs2, buf.hs)
+    del hq2, hs2, w13g, s13g
+    ops.moe_combine(buf.down, buf.route_row, dev(wts), 1.0, buf.out)
+    torch.cuda.synchronize()
+    segs = _expert_rows(ends, c.A)
+    counts = np.array([r.size for r in segs])
+    live_e = np.flatnonzero(counts)
+    order = live_e[np.argsort(counts[live_e], kind="stable")]
+    picks = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})
+    xq, xs = host(buf.xq), host(buf.xs)
+    gu, hq, hs, dn = host(buf.gateup), host(buf.hq), host(buf.hs), host(buf.down)
+    live = np.zeros(c.M_cap, bool)
+    for rows in segs:
+        live[rows] = True
+    assert np.all(gu[~live] == BF16_SENT) and np.all(dn[~live] == BF16_SENT)
+    assert np.all(hq[~live] == BYTE_SENT) and np.all(xq[~live] == BYTE_SENT)
+    for e in picks:
+        rows = segs[e]
+        rows = np.unique(np.concatenate([rows[:6], rows[-6:]]))
+        say(f"  expert {e}: {segs[e].size} rows, checking {rows.size}")
+        # quantised x of these rows: each row is the token its route came from
+        src = np.array([int(np.flatnonzero(sc.route_row == r)[0]) // c.k for r in rows])
+        q, b = M.quant_rows(c.x[src])
+        assert np.array_equal(xq[rows], q)
+        assert np.array_equal(xs[:, rows].T, F.pack_ue8m0_words(b))
+        ab = F.unpack_ue8m0_words(xs[:, rows].T)
+        _, exact, tsum = M.mx_gemm(xq[rows], ab, w.w13[e], w.s13[e])
+        bm = M.block_max_bound(xq[rows], ab, w.w13[e], w.s13[e])
+        ok, _, _ = gemm_within_bound(gu[rows], exact, tsum, c.H, bm)
+        assert ok.all(), f"gemm1 expert {e}: {np.count_nonzero(~ok)} outside bound"
+        q, b = M.act_quant_rows(gu[rows], c.I, c.clamp)
+        assert np.array_equal(hq[rows], q)
+        assert np.array_equal(hs[:, rows].T, F.pack_ue8m0_words(b))
+        hb = F.unpack_ue8m0_words(hs[:, rows].T)
+        _, exact, tsum = M.mx_gemm(hq[rows], hb, w.w2[e], w.s2[e])
+        bm = M.block_max_bound(hq[rows], hb, w.w2[e], w.s2[e])
+        ok, _, _ = gemm_within_bound(dn[rows], exact, tsum, c.I, bm)
+        assert ok.all(), f"gemm2 expert {e}: {np.count_nonzero(~ok)} outside bound"
+    say("large-E full size: combine on sampled tokens, one token end to end")
+    out = host(buf.out)
+    toks = np.array([0, 1, c.T // 2, c.T - 1])
+    ros = rr.reshape(c.T, c.k)[toks]
+    used = np.unique(ros[ros >= 0])
+    rows_f32 = np.zeros((c.M_cap, c.H), np.float32)    # only the rows these tokens read
+    rows_f32[used] = F.bf16_to_f32(dn[used])
+    want = M.combine(rows_f32, ros.ravel(), wts[toks], 1.0)
+    assert np.array_equal(out[toks], want)
+    ref = M.prefill_token_major(c.x, ids, wts, 0, c.E_local, c.I, w.w13, w.s13, w.w2, w.s2,
+                                clamp=c.clamp, tokens=np.array([c.T // 2]))
+    ok, mx, mean = end_to_end_ok(out[[c.T // 2]], ref)
+    assert ok, (mx, mean)
+
+
 # ------------------------------------------------- GEMM edge layouts
 
 def _gemm_edge_case(ops, counts, A, K, N, seed):
