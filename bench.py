@@ -14,6 +14,7 @@ The same line carries:
   roofline      the dominant kernel (GEMM1) against HBM peak, with its
                 duration measured by HIP events around it in the timed loop
   kernels       per-kernel durations, algorithmic bytes / FLOP, GB/s, TFLOP/s
+  layers        the same chain on the tiny and the large-expert-count layers
   actquant      the standalone live-row act-quant benchmark (3,072 live of
                 28,672 rows, width 2,048; SiLU and SiTU) and its full-buffer
                 control, cold
@@ -271,6 +272,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
+        result["layers"] = bench_other_layers(ops, torch, up, up_bf16, log)
         result["actquant"] = bench_actquant(ops, torch, up, up_bf16, log)
         result["decode"] = bench_decode(ops, torch, up, up_bf16, log)
     if not args.no_cpu_baseline:
@@ -283,6 +285,88 @@ def _flush_caches(torch, scratch):
     leaves clean lines behind; a write-based flush would leave dirty lines
     whose write-back steals bandwidth from the next kernel."""
     scratch.view(torch.int64).sum()
+
+
+def bench_other_layers(ops, torch, up, up_bf16, log, steps=20, warmup=5):
+    """The whole chain (route, scatter, fused GEMM1 + act-quant, GEMM2,
+    combine) on the tiny layer (64 tokens, 8 experts) and on the
+    large-expert-count layer (2,048 tokens, 896 resident experts, top-16
+    sigmoid + bias, clamp 25): graph replay time per layer, and per-kernel
+    HIP-event durations from an eager loop."""
+    import workloads as W
+    out = {}
+    for name, make in (("tiny", W.tiny), ("large_e", W.large)):
+        log(f"layer {name}: generating")
+        c = make()
+        w = c.weights
+        x = up_bf16(c.x)
+        logits = up(c.logits)
+        bias = up(c.bias) if c.bias is not None else None
+        score = "softmax" if c.score == "softmax" else "sigmoid_bias"
+        w13, s13 = ops.moe_pack_mx_weights_gateup(up(w.w13), up(w.s13))
+        w2, s2 = ops.moe_pack_mx_weights(up(w.w2), up(w.s2))
+        ids = torch.empty((c.T, c.k), dtype=torch.int32, device="cuda")
+        wts = torch.empty((c.T, c.k), dtype=torch.float32, device="cuda")
+        buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I)
+        names = ["route", "scatter", "gemm1_act", "gemm2", "combine"]
+
+        def step(ev=None):
+            def mark(i):
+                if ev is not None:
+                    ev[i].record()
+            mark(0)
+            ops.moe_route(logits, c.k, score, bias, ids, wts)
+            mark(1)
+            ops.moe_scatter_endpoints(ids, 0, c.E_local, c.A, x, buf.expert_ends, buf.route_row,
+                                      buf.xq, buf.xs, buf.workspace)
+            mark(2)
+            ops.moe_grouped_gemm1_act_quant(buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13,
+                                            c.clamp, buf.hq, buf.hs)
+            mark(3)
+            ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, w2, s2, buf.down)
+            mark(4)
+            ops.moe_combine(buf.down, buf.route_row, wts, c.routed_scale, buf.out)
+            mark(5)
+
+        for _ in range(warmup):
+            step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        dur = {n: round(float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                       for i in range(steps)])) * 1e3, 3)
+               for j, n in enumerate(names)}
+        graph = ops.capture_graph(lambda: step(None))
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / steps
+        del graph
+        ends = buf.expert_ends.cpu().numpy().astype(np.int64)
+        starts = np.concatenate([[0], ((ends[:-1] + c.A - 1) // c.A) * c.A])
+        R = int((ends - starts).sum())
+        E_ne = int(np.count_nonzero(ends - starts))
+        H, I = c.H, c.I
+        b1 = E_ne * (2 * I * H // 2 + 2 * I * H // 32) + R * (H + H // 32) + R * (I + I // 32)
+        b2 = E_ne * (H * I // 2 + H * I // 32) + R * (I + I // 32) + R * H * 2
+        f1, f2 = 2.0 * R * 2 * I * H, 2.0 * R * H * I
+        out[name] = {
+            "us_per_layer_graph": round(us, 2), "kernels_us": dur, "live_rows": R,
+            "nonempty_experts": E_ne,
+            "gemm1_act": {"alg_bytes": int(b1), "hbm_frac": round(b1 / (dur["gemm1_act"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "TFLOPs": round(f1 / (dur["gemm1_act"] * 1e-6) / 1e12, 1)},
+            "gemm2": {"alg_bytes": int(b2), "hbm_frac": round(b2 / (dur["gemm2"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "TFLOPs": round(f2 / (dur["gemm2"] * 1e-6) / 1e12, 1)},
+        }
+        log(f"layer {name}", out[name])
+        del buf, w13, s13, w2, s2, x, logits, ids, wts, c, w
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_actquant(ops, torch, up, up_bf16, log, iters=20):
