@@ -87,6 +87,8 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run 4 plain 1 GiB device copies (the reference kernel that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--only", choices=["actquant", "decode", "layers"],
+                   help="run only that extra measurement (for per-kernel profiles) and exit")
     return p.parse_args()
 
 
@@ -130,6 +132,12 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
+
+    if args.only:
+        fn = {"actquant": bench_actquant, "decode": bench_decode,
+              "layers": bench_other_layers}[args.only]
+        print(json.dumps({args.only: fn(ops, torch, up, up_bf16, log)}), flush=True)
+        return
 
     # ------------------------------------------------------------ workload
     log("generating the prefill EP-share workload")
