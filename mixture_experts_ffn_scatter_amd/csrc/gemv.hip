@@ -10,17 +10,19 @@
 //
 // Differences from the page's kernel: blocks are keyed by slot, but only
 // the first slot (in t*k+s order) of each distinct local expert does work,
-// and it computes every slot routed to that expert, so each selected
-// expert's weights are read once per call instead of once per slot. A
-// block owns 8 weight rows (4 gate + 4 up rows when the GLU is fused, else 8
-// output columns); its 256 threads split K: thread i holds the 16-weight
-// chunk i (and i+256) of every row, 16 or 8 bytes each, all loaded at once,
-// and reads the matching 16 activations of each slot straight from memory
-// into registers. Each chunk is converted once to exact bf16 pairs and dotted
-// in fp32 against every slot of a batch; the partial sums are folded inside
-// each wave with DPP adds and across the 4 waves through LDS in a fixed
-// order. With the GLU fused, the GLU is applied to the bf16-rounded gate and
-// up results before the single bf16 store.
+// and it computes every slot routed to that expert, one after the other, so
+// each selected expert's weights are read once per call instead of once per
+// slot. A thread's chunk is 16 bytes of a weight row: 16 FP8 weights, or 32
+// E2M1 weights (one E8M0 group). For FP8 a block owns 8 weight rows (4 gate +
+// 4 up rows when the GLU is fused, else 8 output columns) and its 256 threads
+// split K; for MXFP4, whose rows are half as long, a block owns 16 rows in two
+// groups of 8, each split over 128 threads. Every chunk a thread needs is
+// loaded at once, with the bias of its epilogue column; the matching
+// activations are read straight from memory into registers. Chunks are
+// converted to exact bf16 pairs and dotted in fp32; the partial sums are
+// folded inside each wave with DPP adds and across the waves of a row group
+// through LDS in a fixed order. With the GLU fused, the GLU is applied to the
+// bf16-rounded gate and up results before the single bf16 store.
 #include <cmath>
 #include <type_traits>
 
@@ -32,7 +34,9 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kGemvRows = 8;          // weight rows per block (GLU: 4 gate + 4 up)
 constexpr int kGemvMaxSlots = 64;     // T*k
-constexpr int kGemvSlotBatch = 2;     // slots accumulated together
+constexpr int kGemvSlotBatch = 1;     // slots accumulated together (one: the fewer
+                                      // registers, the more waves per SIMD, which
+                                      // measured faster than sharing conversions)
 constexpr int kGemvMaxCh = 2;         // 16-weight chunks per thread and row (K <= 8192)
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -63,19 +67,8 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   return v;
 }
 
-// 16 weights -> 8 exact bf16 pairs. FP8: 16 bytes (4 dwords); MXFP4: 8
-// bytes (2 dwords, low nibble first).
-__device__ __forceinline__ void weights_to_bf16(const v2i raw, v2bf* wp) {   // MXFP4
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t d = (uint32_t)(q == 0 ? raw.x : raw.y);
-    wp[4 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 0);
-    wp[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 1);
-    wp[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 2);
-    wp[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 3);
-  }
-}
-__device__ __forceinline__ void weights_to_bf16(const v4i raw, v2bf* wp) {   // FP8
+// 16 FP8 weights (16 bytes) -> 8 exact bf16 pairs
+__device__ __forceinline__ void fp8x16_to_bf16(const v4i raw, v2bf* wp) {
   const uint32_t d[4] = {(uint32_t)raw.x, (uint32_t)raw.y, (uint32_t)raw.z, (uint32_t)raw.w};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -83,19 +76,41 @@ __device__ __forceinline__ void weights_to_bf16(const v4i raw, v2bf* wp) {   // 
     wp[2 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[q], 1.0f, true);
   }
 }
+// 32 E2M1 weights (16 bytes, low nibble first) -> 16 exact bf16 pairs
+__device__ __forceinline__ void fp4x32_to_bf16(const v4i raw, v2bf* wp) {
+  const uint32_t d[4] = {(uint32_t)raw.x, (uint32_t)raw.y, (uint32_t)raw.z, (uint32_t)raw.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    wp[4 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[q], 1.0f, 0);
+    wp[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[q], 1.0f, 1);
+    wp[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[q], 1.0f, 2);
+    wp[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[q], 1.0f, 3);
+  }
+}
 
+// A thread's chunk is 16 bytes of a row: 16 FP8 weights, or 32 E2M1 weights
+// (one E8M0 scale group). A row group of threads covers K: all 256 threads
+// for FP8; 128 for MXFP4, whose rows are half as long, so that a block
+// holds 2 row groups of 8 rows (16 rows, about the bytes of FP8's 8).
 template <bool MXFP4, bool GLU, int CH>
 __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
     const uint16_t* __restrict__ act, int act_per_slot, const int32_t* __restrict__ ids, int T,
     int k, int expert_start, int E_local, int N, int K, const uint8_t* __restrict__ W,
     const void* __restrict__ w_scale, const uint16_t* __restrict__ bias, float alpha,
     float beta, float limit, uint16_t* __restrict__ out, int32_t* __restrict__ slot_row) {
+  constexpr int kTPR = MXFP4 ? 128 : 256;            // threads per row group
+  constexpr int kRG = kGemvThreads / kTPR;           // row groups per block
+  constexpr int kWPG = kTPR / 64;                    // waves per row group
+  constexpr int kRows = kGemvRows * kRG;             // weight rows per block
+  constexpr int kWpc = MXFP4 ? 32 : 16;              // weights per chunk
   __shared__ float s_red[kGemvWaves][kGemvSlotBatch][kGemvRows];
 
   const int q = blockIdx.y;  // flattened slot t*k+s
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid / kWPG;                        // this thread's row group
+  const int t = tid % kTPR;                          // its place in the group
   const int nq = T * k;      // <= 64: one id per lane
   // every wave reads all slot ids at once; the same ballots in every wave
   // give the duplicate test and the list of slots routed to this expert
@@ -110,35 +125,44 @@ __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
   if (same & ((1ull << q) - 1ull)) return;   // block-uniform
 
   const int n_out = GLU ? N / 2 : N;
-  constexpr int kOuts = GLU ? kGemvRows / 2 : kGemvRows;    // output columns per block
+  constexpr int kOuts = GLU ? kRows / 2 : kRows;     // output columns per block
   const int col0 = blockIdx.x * kOuts;
   const size_t row_bytes = MXFP4 ? (size_t)K / 2 : (size_t)K;
-  const int nch = K / 16;              // 16-weight chunks per row
+  const int nch = K / kWpc;            // chunks per row
   const uint8_t* We = W + (size_t)e * N * row_bytes;
   const float fp8_scale = MXFP4 ? 1.f : reinterpret_cast<const float*>(w_scale)[e];
   const uint8_t* Ws = MXFP4 ? reinterpret_cast<const uint8_t*>(w_scale) + (size_t)e * N * (K / 32)
                             : nullptr;
-  // weight row of register row r (clamped into range; columns past n_out
-  // are computed and never stored)
-  auto row_of = [&](int r) {
-    if (GLU) return min(col0 + (r % kOuts), n_out - 1) + (r < kOuts ? 0 : N / 2);
-    return min(col0 + r, N - 1);
+  // weight row of block row rr (clamped into range; columns past n_out are
+  // computed and never stored); with the GLU, rows [0, kOuts) are gate rows
+  // and [kOuts, 2 kOuts) the matching up rows
+  auto row_of = [&](int rr) {
+    if (GLU) return min(col0 + (rr % kOuts), n_out - 1) + (rr < kOuts ? 0 : N / 2);
+    return min(col0 + rr, N - 1);
   };
+
+  // the bias of this thread's epilogue column(s), fetched before the
+  // weights so that its latency is hidden; read unpredicated (without a bias,
+  // from the weight bytes, which are longer, and then not used)
+  const uint16_t* bsrc = bias ? bias : reinterpret_cast<const uint16_t*>(W);
+  uint16_t bpre[GLU ? 2 : 1];
+#pragma unroll
+  for (int hf = 0; hf < (GLU ? 2 : 1); ++hf)
+    bpre[hf] = bsrc[(size_t)e * N + row_of(tid % kOuts + hf * kOuts)];
 
   // every weight chunk of this thread goes out first (unpredicated: a
   // thread past the last chunk reads the last one and does not use it)
-  using RawT = std::conditional_t<MXFP4, v2i, v4i>;
-  RawT raw[kGemvRows][CH];
-  float gsc[kGemvRows][CH];
+  v4i raw[kGemvRows][CH];
+  float gsc[MXFP4 ? kGemvRows : 1][CH];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    const int ch = min(tid + kGemvThreads * j, nch - 1);
+    const int ch = min(t + kTPR * j, nch - 1);
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r) {
-      const uint8_t* wr = We + (size_t)row_of(r) * row_bytes;
+      const int row = row_of(grp * kGemvRows + r);
       raw[r][j] = __builtin_nontemporal_load(
-          reinterpret_cast<const RawT*>(wr + (size_t)ch * sizeof(RawT)));
-      gsc[r][j] = MXFP4 ? e8m0_value(Ws[(size_t)row_of(r) * (K / 32) + ch / 2]) : 1.f;
+          reinterpret_cast<const v4i*>(We + (size_t)row * row_bytes + (size_t)ch * 16));
+      if constexpr (MXFP4) gsc[r][j] = e8m0_value(Ws[(size_t)row * (K / 32) + ch]);
     }
   }
 
@@ -162,41 +186,47 @@ __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
       for (int r = 0; r < kGemvRows; ++r) acc[b][r] = 0.f;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int ch = tid + kGemvThreads * j;
+      const int ch = t + kTPR * j;
       const bool valid = ch < nch;
       const int chc = min(ch, nch - 1);
-      // this chunk's 16 activations of each slot of the batch
-      v2bf av[kGemvSlotBatch][8];
+      // this chunk's activations of each slot of the batch
+      v2bf av[kGemvSlotBatch][kWpc / 2];
 #pragma unroll
       for (int b = 0; b < kGemvSlotBatch; ++b) {
         const int arow = p[b] < 0 ? 0 : (act_per_slot ? p[b] : p[b] / k);
-        const v4i* ap = reinterpret_cast<const v4i*>(act + (size_t)arow * K + (size_t)chc * 16);
-        const v4i a0 = ap[0], a1 = ap[1];
-        const int w8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const v4i* ap = reinterpret_cast<const v4i*>(act + (size_t)arow * K + (size_t)chc * kWpc);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) av[b][i] = __builtin_bit_cast(v2bf, w8[i]);
+        for (int v = 0; v < kWpc / 8; ++v) {
+          const v4i a4 = ap[v];
+          // components copied out first: a bit cast of a vector component
+          // expression reads the vector's first component
+          const int w4[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) av[b][4 * v + i] = __builtin_bit_cast(v2bf, w4[i]);
+        }
       }
       if (valid) {
 #pragma unroll
         for (int r = 0; r < kGemvRows; ++r) {
-          // converted per batch, row by row (keeps 8 converted registers
-          // live instead of all 16 rows' worth)
-          RawT rw = raw[r][j];
+          // converted per batch, row by row (only one row's pairs live)
+          v4i rw = raw[r][j];
           asm volatile("" : "+v"(rw));
-          v2bf wp[8];
-          weights_to_bf16(rw, wp);
+          v2bf wp[kWpc / 2];
+          if constexpr (MXFP4) fp4x32_to_bf16(rw, wp);
+          else fp8x16_to_bf16(rw, wp);
 #pragma unroll
           for (int b = 0; b < kGemvSlotBatch; ++b) {
             float part = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < kWpc / 2; ++i)
               part = __builtin_amdgcn_fdot2_f32_bf16(wp[i], av[b][i], part, false);
-            acc[b][r] = MXFP4 ? fmaf(part, gsc[r][j], acc[b][r]) : acc[b][r] + part;
+            if constexpr (MXFP4) acc[b][r] = fmaf(part, gsc[r][j], acc[b][r]);
+            else acc[b][r] = acc[b][r] + part;
           }
         }
       }
     }
-    // fold: inside the wave (DPP, lane 63), then the 4 waves in order
+    // fold: inside the wave (DPP, lane 63), then the group's waves in order
 #pragma unroll
     for (int b = 0; b < kGemvSlotBatch; ++b)
 #pragma unroll
@@ -213,12 +243,12 @@ __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
         float y[2];
 #pragma unroll
         for (int hf = 0; hf < (GLU ? 2 : 1); ++hf) {
-          const int rr = c + hf * kOuts;
-          const int n = row_of(rr);
-          float tot = s_red[0][b][rr];
+          const int rr = c + hf * kOuts;                 // block row
+          const int g0 = rr / kGemvRows, r = rr % kGemvRows;
+          float tot = s_red[g0 * kWPG][b][r];
 #pragma unroll
-          for (int w = 1; w < kGemvWaves; ++w) tot += s_red[w][b][rr];
-          const float bv = bias ? bf16_to_f32(bias[(size_t)e * N + n]) : 0.f;
+          for (int w = 1; w < kWPG; ++w) tot += s_red[g0 * kWPG + w][b][r];
+          const float bv = bias ? bf16_to_f32(bpre[hf]) : 0.f;
           const float yv = MXFP4 ? __fadd_rn(tot, bv) : __fadd_rn(__fmul_rn(tot, fp8_scale), bv);
           y[hf] = bf16_to_f32((uint16_t)f32_to_bf16_bits(yv));
         }
@@ -245,12 +275,15 @@ extern "C" int moe_sparse_gemv(const uint16_t* act, int act_per_slot, const int3
   if (K % 8 != 0) return MOE_ERR_ALIGN;
   if (glu && N % 2 != 0) return MOE_ERR_ALIGN;
   if (act_per_slot != 0 && act_per_slot != 1) return MOE_ERR_UNSUPPORTED;
-  const int chunks_per_thread = (K / 16 + kGemvThreads - 1) / kGemvThreads;
+  const bool mx = wfmt == MOE_W_MXFP4_G32;
+  // FP8: 16 weights per thread chunk over 256 threads; MXFP4: 32 over 128
+  const int chunks_per_thread = mx ? (K / 32 + 127) / 128 : (K / 16 + kGemvThreads - 1) / kGemvThreads;
   if (chunks_per_thread > kGemvMaxCh) return MOE_ERR_SHAPE;  // K <= 8192
   if (T == 0) return MOE_OK;
   if (!act || !topk_ids || !w || !w_scale || !out) return MOE_ERR_NULL;
   const int n_out = glu ? N / 2 : N;
-  const int outs_per_block = glu ? kGemvRows / 2 : kGemvRows;
+  const int rows_per_block = mx ? 2 * kGemvRows : kGemvRows;
+  const int outs_per_block = glu ? rows_per_block / 2 : rows_per_block;
   dim3 grid((n_out + outs_per_block - 1) / outs_per_block, T * k);
   hipStream_t st = (hipStream_t)stream;
 #define MOE_GEMV_LAUNCH(MX, G, CHN)                                                            \
@@ -262,7 +295,6 @@ extern "C" int moe_sparse_gemv(const uint16_t* act, int act_per_slot, const int3
     case 1: MOE_GEMV_LAUNCH(MX, G, 1); break;    \
     default: MOE_GEMV_LAUNCH(MX, G, 2); break;   \
   }
-  const bool mx = wfmt == MOE_W_MXFP4_G32;
   if (mx && glu) MOE_GEMV_CH(true, true)
   else if (mx) MOE_GEMV_CH(true, false)
   else if (glu) MOE_GEMV_CH(false, true)
