@@ -33,15 +33,17 @@
 // bytes per lane and a wave reads its 4 column blocks' scales as one word.
 //
 // Work decomposition. An item is (expert, n-tile of 256 columns, m-chunk of
-// up to 128 live rows). Items are listed expert-major (n-tile-major inside
-// an expert) and the list is cut into 8 equal contiguous ranges, one per
-// XCD (block b runs on XCD b % 8); the blocks of an XCD take its items
-// round-robin, so the items running at once on one XCD share activation
-// chunks (one expert, neighbouring n-tiles) and weight slices (one n-tile,
-// its m-chunks) in that XCD's L2, and every XCD streams about 1/8 of the
-// weights. The list is rebuilt inside every block from expert_ends (a
-// block-wide scan), so the grid depends only on host-known sizes and no
-// count is read back.
+// up to 128 live rows); its cost grows with its live row blocks (a full
+// chunk takes about 1.6 times a one-block chunk). Chunks are ranked by
+// cost, full ones first, then partial ones by row blocks descending, and
+// dealt to the 8 XCDs in snake order (rank r to XCD r % 8 in even rounds,
+// 7 - r % 8 in odd ones) with all their n-tiles, so the items of a chunk
+// share its activations in one XCD's L2 (block b runs on XCD b % 8). An
+// XCD lists its items chunk-major, costliest first, and its blocks take
+// them in snake order over rounds, so a block with a costly item in one
+// round gets a cheap one in the next; the ranking is rebuilt inside every
+// block from expert_ends (a block-wide scan and count), so the grid depends
+// only on host-known sizes and no count is read back.
 //
 // Data path. Every operand travels global -> LDS by the buffer-to-LDS
 // transfer of gfx950 (no register staging) into a ring of 4 stages of one
@@ -219,76 +221,116 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   }
   const int NT = (N + kGemmBN - 1) / kGemmBN;
 
-  // chunks per expert: full 128-row chunks and at most one partial one, and
-  // the exclusive scan of both, packed: fulls in the low 16 bits, partials
-  // in the high (at most 1024 experts; the host caps M_cap / 128 < 2^16)
+  // chunks per expert: full 128-row chunks and at most one partial one of
+  // 1-8 row blocks. s_pre[e] holds, in its low 16 bits, the full chunks
+  // before e (the host caps M_cap / 128 < 2^16), and in its high 16 bits
+  // first the row blocks of e's partial chunk (0: none), then its rank among
+  // all partial chunks by row blocks descending, ties by expert (0xFFFF: none)
   constexpr int kEPT = kGemmMaxE / kGemmThreads;   // experts per thread
-  int cnt[kEPT];
+  int fcnt[kEPT], pblk[kEPT];
   int local_sum = 0;
 #pragma unroll
   for (int j = 0; j < kEPT; ++j) {
     const int e = tid * kEPT + j;
-    cnt[j] = 0;
+    fcnt[j] = 0;
+    pblk[j] = 0;
     if (e < E_local) {
       int st, en;
       expert_range(expert_ends, e, A, M_cap, st, en);
-      cnt[j] = (en - st) / kGemmBM | (((en - st) % kGemmBM != 0) << 16);
+      fcnt[j] = (en - st) / kGemmBM;
+      pblk[j] = ((en - st) % kGemmBM + 15) >> 4;
     }
-    local_sum += cnt[j];
+    local_sum += fcnt[j];
   }
   int run = block_exclusive_scan(local_sum, s_tmp);
 #pragma unroll
   for (int j = 0; j < kEPT; ++j) {
     const int e = tid * kEPT + j;
-    if (e < E_local) s_pre[e] = run;
-    run += cnt[j];
+    if (e < E_local) s_pre[e] = run | (pblk[j] << 16);
+    run += fcnt[j];
   }
   if (tid == kGemmThreads - 1) s_pre[E_local] = run;
   __syncthreads();
+  // rank of each partial chunk (every thread walks all experts in step, so
+  // each read is one broadcast); P counts the partial chunks
+  int prank[kEPT];
+#pragma unroll
+  for (int j = 0; j < kEPT; ++j) prank[j] = 0;
+  int P = 0;
+  for (int e2 = 0; e2 < E_local; ++e2) {
+    const int v2 = s_pre[e2] >> 16;
+    P += v2 > 0;
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+      const int e = tid * kEPT + j;
+      prank[j] += (v2 > pblk[j]) || (v2 == pblk[j] && e2 < e);
+    }
+  }
+  __syncthreads();                       // every read of the row-block counts is done
+#pragma unroll
+  for (int j = 0; j < kEPT; ++j) {
+    const int e = tid * kEPT + j;
+    if (e < E_local) s_pre[e] = (s_pre[e] & 0xFFFF) | ((pblk[j] > 0 ? prank[j] : 0xFFFF) << 16);
+  }
+  __syncthreads();
   // LDS and global values the whole block agrees on are made scalar
   // (readfirstlane), so the buffer resources built from them stay in SGPRs
-  const int tot = __builtin_amdgcn_readfirstlane(s_pre[E_local]);
-  const int F = tot & 0xFFFF;            // full chunks over all experts
-  const int P = tot >> 16;               // partial chunks
+  const int F = __builtin_amdgcn_readfirstlane(s_pre[E_local]);   // full chunks
+  P = __builtin_amdgcn_readfirstlane(P);                            // partial chunks
   const int MT = F + P;                  // chunks of one n-tile
-  const int L = MT * NT;                 // items
   if (MT == 0) return;                   // no live rows (uniform over the block)
 
-  // this block's XCD range [i0, i1) of the item list (block b runs on XCD
-  // b % 8); the XCD's blocks take its items round-robin, so neighbouring
-  // items run side by side.
+  // The schedule. Chunks are ranked by cost: the full ones first (expert
+  // order), then the partial ones by row blocks descending. Rank r goes to
+  // XCD r % 8 in even rounds of 8 and 7 - r % 8 in odd ones (snake order),
+  // with all its NT n-tiles, so the items of one chunk share its activations
+  // in that XCD's L2. An XCD lists its items chunk-major (costliest first),
+  // n-tile-minor, and its blocks take them in snake order over rounds of
+  // nslot items, so a block that got a costly item in one round gets a
+  // cheap one in the next. (Block b runs on XCD b % 8.)
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslot = gridDim.x >> 3;      // the grid is a multiple of 8
-  const int i0 = (int)(((long long)L * xcd) / 8);
-  const int i1 = (int)(((long long)L * (xcd + 1)) / 8);
-  // the block's k-th item, or -1 past its last
+  const int kr = MT >> 3, rm = MT & 7;   // full rounds of chunks, remainder
+  const int nx = kr + (((kr & 1) ? 7 - xcd : xcd) < rm);   // chunks of this XCD
+  const int nitems = nx * NT;
+  // the block's k-th item (an index into the XCD's list), or -1 past its last
   auto item_at = [&](int k) {
-    const int u = i0 + slot + k * nslot;
-    return u < i1 ? u : -1;
+    const int u = nslot * k + ((k & 1) ? nslot - 1 - slot : slot);
+    return u < nitems ? u : -1;
   };
 
-  // items are listed expert-major: expert e owns items [NT cb(e), NT cb(e+1))
-  // (cb(e): chunks of the experts before e), n-tile-major inside, so the
-  // items running at once on an XCD share their activation chunks (one
-  // expert, several n-tiles) and their weight slices (one n-tile, several
-  // m-chunks) in its L2
   auto locate = [&](int item, GemmTile& T) {
-    const int jq = item / NT;
-    int lo = 0, hi = E_local - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      const int pm = __builtin_amdgcn_readfirstlane(s_pre[mid]);
-      if ((pm & 0xFFFF) + (pm >> 16) <= jq) lo = mid; else hi = mid - 1;
+    const int kq = item / NT;
+    const int nt = item - kq * NT;
+    const int r = 8 * kq + ((kq & 1) ? 7 - xcd : xcd);       // chunk rank
+    int e, c;
+    if (r < F) {
+      // full chunk r: the last expert whose full-chunk prefix is <= r
+      int lo = 0, hi = E_local - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int pm = __builtin_amdgcn_readfirstlane(s_pre[mid]) & 0xFFFF;
+        if (pm <= r) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+      c = r - (__builtin_amdgcn_readfirstlane(s_pre[e]) & 0xFFFF);
+    } else {
+      // partial chunk of rank r - F: the expert holding that rank
+      const int want = r - F;
+      e = 0;
+      for (int e0 = 0; e0 < E_local; e0 += 64) {
+        const int ee = e0 + lane;
+        const uint64_t hit = __ballot(ee < E_local && (s_pre[min(ee, E_local - 1)] >> 16) == want);
+        if (hit) {
+          e = e0 + __ffsll((unsigned long long)hit) - 1;
+          break;
+        }
+      }
+      e = __builtin_amdgcn_readfirstlane(e);
+      c = (__builtin_amdgcn_readfirstlane(s_pre[e + 1]) & 0xFFFF) -
+          (__builtin_amdgcn_readfirstlane(s_pre[e]) & 0xFFFF);        // e's full chunks
     }
-    const int e = lo;
-    const int pe = __builtin_amdgcn_readfirstlane(s_pre[e]);
-    const int pn = __builtin_amdgcn_readfirstlane(s_pre[e + 1]);
-    const int cb_e = (pe & 0xFFFF) + (pe >> 16);           // chunks before e
-    const int nch = (pn & 0xFFFF) + (pn >> 16) - cb_e;     // chunks of e (>= 1)
-    const int local = item - NT * cb_e;
-    const int nt = local / nch;
-    const int c = local - nt * nch;
     int start, end;
     expert_range(expert_ends, e, A, M_cap, start, end);
     start = __builtin_amdgcn_readfirstlane(start);
