@@ -650,6 +650,25 @@ def test_gemm_edge_layouts(ops, K, N):
     _gemm_edge_case(ops, [0, 128, 129, 1, 300, 0, 17], 128, K, N, seed=K + N)
 
 
+@pytest.mark.parametrize("E,K,N,seed", [(40, 128, 768, 1), (37, 256, 128, 2), (1024, 128, 256, 3)])
+def test_gemm_schedule_random_layouts(ops, E, K, N, seed):
+    """The cost-ranked schedule on random layouts: partial chunks of every
+    size 1-8 row blocks, experts of several full chunks, chunk counts that
+    are not a multiple of the 8 XCDs, an odd number of n-tiles (N = 768), a
+    partial n-tile (N = 128), more items than blocks, and 1,024 experts (the
+    largest rank count and partial-chunk search)."""
+    say(f"gemm schedule random layouts E={E} K={K} N={N}")
+    rng = np.random.default_rng(100 + seed)
+    if E >= 512:
+        counts = rng.integers(0, 24, size=E)
+    else:
+        kind = rng.integers(0, 4, size=E)
+        counts = np.where(kind == 0, 0, np.where(kind == 1, rng.integers(1, 129, size=E),
+                          np.where(kind == 2, 128 * rng.integers(1, 4, size=E),
+                                   rng.integers(129, 520, size=E))))
+    _gemm_edge_case(ops, [int(c) for c in counts], 128, K, N, seed=seed)
+
+
 def test_gemm_all_empty_writes_nothing(ops):
     say("gemm all-empty")
     _gemm_edge_case(ops, [0, 0, 0], 128, 256, 256, seed=5)
