@@ -32,12 +32,12 @@ namespace moe {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / 64;
-constexpr int kGemvRows = 8;          // weight rows per block (GLU: 4 gate + 4 up)
+constexpr int kGemvRows = 8;          // weight rows per row group (FP8: the block; GLU: 4 gate + 4 up)
 constexpr int kGemvMaxSlots = 64;     // T*k
 constexpr int kGemvSlotBatch = 1;     // slots accumulated together (one: the fewer
                                       // registers, the more waves per SIMD, which
                                       // measured faster than sharing conversions)
-constexpr int kGemvMaxCh = 2;         // 16-weight chunks per thread and row (K <= 8192)
+constexpr int kGemvMaxCh = 2;         // 16-byte chunks per thread and row (K <= 8192)
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
