@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 enum moe_status {
     MOE_OK = 0,
@@ -301,6 +301,44 @@ int moe_grouped_gemm2(const uint8_t* hq, const int32_t* hs, const int32_t* exper
                       int E_local, int A, int M_cap, int I, int H,
                       const uint8_t* w2_packed, const uint8_t* w2_scale_packed,
                       uint16_t* down, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Group-128 activation recipe: the four entry points below are the group-32
+ * ones above with activations quantised per 128 columns instead of 32.
+ * [SGL] overview (table of quantised data types) and section 2.1.3 (the
+ * MXFP4-experts recipe quantises activations per (1,128), weights per
+ * (1,32)); section 2.2.4 (with UE8M0 scales the activation scales are int32
+ * words packing 4 consecutive groups, column-major, ceil(K/128/4) words per
+ * token). Per 128-column group: amax, the
+ * UE8M0 round-up of amax/448 and the e4m3 codes exactly as in the group-32
+ * forms, with 128 in place of 32.
+ *
+ *   scales       int32 [ceil(K/512), M_cap]: byte j of word c is the group of
+ *                columns [512c + 128j, +128); bytes of groups past K are 0
+ *                (K = H for the scatter and GEMM1 inputs, I for the
+ *                act-quant output and the GEMM2 input)
+ *   codes        as in the group-32 forms
+ * The GEMMs apply a group's scale to each of its four 32-column blocks (the
+ * weights keep their per-32 E8M0 scales). Same arguments, requirements,
+ * ownership and errors as moe_scatter_endpoints, moe_grouped_gemm1,
+ * moe_act_quant_liverows and moe_grouped_gemm2 respectively, except the
+ * scale layout. No fused GEMM1 + act-quant form exists for this recipe.
+ * ------------------------------------------------------------------------ */
+int moe_scatter_endpoints_g128(const int32_t* topk_ids, int T, int k, int expert_start,
+                               int E_local, int A, int M_cap, const uint16_t* x, int H,
+                               int32_t* expert_ends, int32_t* route_row, uint8_t* xq, int32_t* xs,
+                               void* workspace, size_t workspace_bytes, void* stream);
+int moe_grouped_gemm1_g128(const uint8_t* xq, const int32_t* xs, const int32_t* expert_ends,
+                           int E_local, int A, int M_cap, int H, int I,
+                           const uint8_t* w13_packed, const uint8_t* w13_scale_packed,
+                           uint16_t* gateup, void* stream);
+int moe_act_quant_liverows_g128(const uint16_t* gateup, const int32_t* expert_ends, int E_local,
+                                int A, int M_cap, int I, float clamp_limit, uint8_t* hq,
+                                int32_t* hs, void* stream);
+int moe_grouped_gemm2_g128(const uint8_t* hq, const int32_t* hs, const int32_t* expert_ends,
+                           int E_local, int A, int M_cap, int I, int H,
+                           const uint8_t* w2_packed, const uint8_t* w2_scale_packed,
+                           uint16_t* down, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine - unpermute and weighted top-k sum.

@@ -10,7 +10,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 c_int, c_i64, c_size, c_float, c_void = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
                                          ctypes.c_float, ctypes.c_void_p)
@@ -36,6 +36,15 @@ SIGNATURES = {
                                             c_float, c_void, c_void, c_void]),
     "moe_grouped_gemm2": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                   c_void, c_void, c_void, c_void]),
+    "moe_scatter_endpoints_g128": (c_int, [c_void, c_int, c_int, c_int, c_int, c_int, c_int,
+                                           c_void, c_int, c_void, c_void, c_void, c_void, c_void,
+                                           c_size, c_void]),
+    "moe_grouped_gemm1_g128": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
+                                       c_void, c_void, c_void, c_void]),
+    "moe_act_quant_liverows_g128": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, c_float,
+                                            c_void, c_void, c_void]),
+    "moe_grouped_gemm2_g128": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
+                                       c_void, c_void, c_void, c_void]),
     "moe_combine": (c_int, [c_void, c_i64, c_void, c_void, c_int, c_int, c_int, c_float, c_void,
                             c_void]),
     "moe_sparse_gemv": (c_int, [c_void, c_int, c_void, c_int, c_int, c_int, c_int, c_int, c_int,

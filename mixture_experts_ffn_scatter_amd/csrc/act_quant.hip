@@ -92,7 +92,10 @@ __device__ int act_block_scan(int v, int* tmp) {
 
 // SITU: the SiTU activation (Kimi-K3's b_s = 4, b_l = 25) instead of SiLU,
 // with its two scaled-tanh tables beside the sigmoid table in LDS; no clamp.
-template <bool CLAMP, bool SITU>
+// G128: one UE8M0 byte per 128 columns of h instead of per 32, packed four to
+// a word over 512 columns ([ceil(I/512)][M_cap] words; bytes of groups past I
+// are 0)
+template <bool CLAMP, bool SITU, bool G128>
 __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     const uint16_t* __restrict__ gateup, const int32_t* __restrict__ expert_ends, int E_local,
     int A, int M_cap, int I, float L, uint8_t* __restrict__ hq, int32_t* __restrict__ hs) {
@@ -261,6 +264,10 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
       }
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      if constexpr (G128) {               // the 128-column group: 16 lanes
+        amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
+      }
       const uint32_t bsc = ue8m0_byte_of_amax(amax);
       const float inv = e8m0_reciprocal(bsc);
       uint32_t lo = 0, hi = 0;
@@ -268,12 +275,25 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
       lo = cvt_e4m3x2<true>(h[2] * inv, h[3] * inv, lo);
       hi = cvt_e4m3x2<false>(h[4] * inv, h[5] * inv, hi);
       hi = cvt_e4m3x2<true>(h[6] * inv, h[7] * inv, hi);
-      uint32_t word = bsc << (8 * ((lane >> 2) & 3));
-      word |= __shfl_xor(word, 4, 64);
-      word |= __shfl_xor(word, 8, 64);
+      uint32_t word;
+      if constexpr (G128) {
+        // byte q of the chunk's word: the group of lanes 16q .. 16q + 15
+        const bool in = ch * 512 + 128 * (lane >> 4) < I;
+        word = (in ? bsc : 0u) << (8 * (lane >> 4));
+        word |= __shfl_xor(word, 16, 64);
+        word |= __shfl_xor(word, 32, 64);
+      } else {
+        word = bsc << (8 * ((lane >> 2) & 3));
+        word |= __shfl_xor(word, 4, 64);
+        word |= __shfl_xor(word, 8, 64);
+      }
       if (act) {
         *reinterpret_cast<uint2*>(hq + (size_t)row * I + col) = make_uint2(lo, hi);
-        if ((lane & 15) == 0) hs[(size_t)(col >> 7) * M_cap + row] = (int32_t)word;
+        if constexpr (G128) {
+          if (lane == 0) hs[(size_t)ch * M_cap + row] = (int32_t)word;
+        } else {
+          if ((lane & 15) == 0) hs[(size_t)(col >> 7) * M_cap + row] = (int32_t)word;
+        }
       }
     }
   };
@@ -327,10 +347,10 @@ int act_quant_check(const uint16_t* gateup, const int32_t* expert_ends, int E_lo
 
 }  // namespace
 
-extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends,
-                                      int E_local, int A, int M_cap, int I, float clamp_limit,
-                                      uint8_t* hq, int32_t* hs, void* stream) {
-  using namespace moe;
+namespace moe {
+static int act_quant_silu(const uint16_t* gateup, const int32_t* expert_ends, int E_local, int A,
+                          int M_cap, int I, float clamp_limit, uint8_t* hq, int32_t* hs,
+                          void* stream, bool g128) {
   bool clamp = false;
   if (clamp_limit > 0.f && clamp_limit < __builtin_inff()) {
     uint32_t bits;
@@ -344,14 +364,28 @@ extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* exp
   if (rc <= 0) return rc;
   hipStream_t st = (hipStream_t)stream;
   const int grid = 256;         // one block per CU; each takes 1/256 of the live rows
-  if (clamp)
-    hipLaunchKernelGGL((act_quant_kernel<true, false>), dim3(grid), dim3(kActThreads), 0, st,
-                       gateup, expert_ends, E_local, A, M_cap, I, clamp_limit, hq, hs);
-  else
-    hipLaunchKernelGGL((act_quant_kernel<false, false>), dim3(grid), dim3(kActThreads), 0, st,
-                       gateup, expert_ends, E_local, A, M_cap, I, 0.f, hq, hs);
+  auto kernel = clamp ? (g128 ? act_quant_kernel<true, false, true> : act_quant_kernel<true, false, false>)
+                     : (g128 ? act_quant_kernel<false, false, true> : act_quant_kernel<false, false, false>);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kActThreads), 0, st, gateup, expert_ends, E_local, A,
+                     M_cap, I, clamp ? clamp_limit : 0.f, hq, hs);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends,
+                                      int E_local, int A, int M_cap, int I, float clamp_limit,
+                                      uint8_t* hq, int32_t* hs, void* stream) {
+  return moe::act_quant_silu(gateup, expert_ends, E_local, A, M_cap, I, clamp_limit, hq, hs,
+                             stream, false);
+}
+
+extern "C" int moe_act_quant_liverows_g128(const uint16_t* gateup, const int32_t* expert_ends,
+                                           int E_local, int A, int M_cap, int I,
+                                           float clamp_limit, uint8_t* hq, int32_t* hs,
+                                           void* stream) {
+  return moe::act_quant_silu(gateup, expert_ends, E_local, A, M_cap, I, clamp_limit, hq, hs,
+                             stream, true);
 }
 
 extern "C" int moe_act_quant_liverows_situ(const uint16_t* gateup, const int32_t* expert_ends,
@@ -363,7 +397,7 @@ extern "C" int moe_act_quant_liverows_situ(const uint16_t* gateup, const int32_t
   if (situ_beta != 4.0f || situ_linear_beta != 25.0f) return MOE_ERR_UNSUPPORTED;
   const int rc = act_quant_check(gateup, expert_ends, E_local, A, M_cap, I, hq, hs);
   if (rc <= 0) return rc;
-  hipLaunchKernelGGL((act_quant_kernel<false, true>), dim3(256), dim3(kActThreads), 0,
+  hipLaunchKernelGGL((act_quant_kernel<false, true, false>), dim3(256), dim3(kActThreads), 0,
                      (hipStream_t)stream, gateup, expert_ends, E_local, A, M_cap, I, 0.f, hq, hs);
   MOE_CHECK_LAUNCH();
   return MOE_OK;

@@ -191,7 +191,10 @@ struct GemmActOut {
 
 static_assert(kGemmBN == 256 && kGemmCB == 4, "the fused epilogue pairs 2 gate and 2 up blocks per wave");
 
-template <bool ACT>
+// XG128: activation scales of one UE8M0 byte per 128 columns, packed four
+// k-steps to a word ([ceil(K/512)][M_cap]); the byte of k-step ks is byte
+// ks % 4 of word ks / 4 and serves all four 32-column blocks of the step.
+template <bool ACT, bool XG128>
 __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gemm_kernel(
     const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
     const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int K, int N,
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     q.wr = make_rsrc(Wp + ((size_t)T.e * NB + T.cb0) * KS * 1024, (uint32_t)(T.ncb * KS) * 1024u);
     q.sr = make_rsrc(Sp + (size_t)T.e * KS * NB * 64, (uint32_t)(KS * NB) * 64u);
     q.xr = make_rsrc(X + (size_t)T.r0 * K, (uint32_t)T.rows * (uint32_t)K);
-    q.xsr = make_rsrc(Xs + T.r0, (uint32_t)((KS - 1) * M_cap + T.rows) * 4u);
+    q.xsr = make_rsrc(Xs + T.r0, (uint32_t)(((XG128 ? (KS + 3) / 4 : KS) - 1) * M_cap + T.rows) * 4u);
 #pragma unroll
     for (int c = 0; c < kDmaCB; ++c) {
       const int cb = kDmaCB * wid + c;
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
             base + (kDmaXR * wid + r) * 2048 + h * 1024);
     } else {
       if (wid < 2) {
-        dma4(q.xsr, q.xso + (uint32_t)(st * M_cap) * 4u, base + kOffXs + wid * 256);
+        dma4(q.xsr, q.xso + (uint32_t)((XG128 ? st >> 2 : st) * M_cap) * 4u, base + kOffXs + wid * 256);
       } else if (wid == 2) {
         // the tile's weight-scale line: 64 bytes per column block
         if (kGemmBN / 16 * 4 >= 64 || lane < kGemmBN / 16 * 4)
@@ -442,6 +445,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
 
     // one k-step; FULL (all of the wave's row blocks live) runs without
     // per-row-block branches
+    int cur_ks = 0;                      // the item's k-step (XG128 picks the scale byte by it)
     auto step = [&](auto full) {
       constexpr bool FULL = decltype(full)::value;
       // stage gs complete for this wave, then (barrier) for the block; the
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       for (int i = 0; i < kGemmMB; ++i) {
         if (i + kGemmRD - 1 < kGemmMB) read_b(i + kGemmRD - 1);
         if (FULL || i < mlive) {
-          const int sb = (int)(xw[i] >> (8 * g));
+          const int sb = (int)(xw[i] >> (8 * (XG128 ? (cur_ks & 3) : g)));
           // op_sel must be a constant: one call per column block
           auto mfma = [&](auto cc) {
             constexpr int c = decltype(cc)::value;
@@ -520,9 +524,15 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       ++gs;
     };
     if (mlive == kGemmMB) {
-      for (int ks = 0; ks < KS; ++ks) step(std::true_type{});
+      for (int ks = 0; ks < KS; ++ks) {
+        cur_ks = ks;
+        step(std::true_type{});
+      }
     } else {
-      for (int ks = 0; ks < KS; ++ks) step(std::false_type{});
+      for (int ks = 0; ks < KS; ++ks) {
+        cur_ks = ks;
+        step(std::false_type{});
+      }
     }
 
     if constexpr (!ACT) {
@@ -672,7 +682,7 @@ __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __re
 static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_t* ends,
                                int E_local, int A, int M_cap, int K, int N, const uint8_t* Wp,
                                const uint8_t* Sp, uint16_t* out, void* stream,
-                               const GemmActOut* act = nullptr) {
+                               const GemmActOut* act = nullptr, bool xg128 = false) {
   if (E_local < 0 || E_local > kGemmMaxE || A < 1 || M_cap < 0 || K <= 0 || N <= 0)
     return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
@@ -691,13 +701,16 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
   const int resident = 256 * kGemmBlocksPerCU;
   int grid = max_items < resident ? (int)max_items : resident;
   grid = (grid + 7) & ~7;
-  if (act)
-    hipLaunchKernelGGL(grouped_mx_gemm_kernel<true>, dim3(grid), dim3(kGemmThreads), 0,
+  if (act) {
+    if (xg128) return MOE_ERR_UNSUPPORTED;   // the fused epilogue quantises per 32 columns
+    hipLaunchKernelGGL((grouped_mx_gemm_kernel<true, false>), dim3(grid), dim3(kGemmThreads), 0,
                        (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, Wp, Sp, out, *act);
-  else
-    hipLaunchKernelGGL(grouped_mx_gemm_kernel<false>, dim3(grid), dim3(kGemmThreads), 0,
-                       (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, Wp, Sp, out,
+  } else {
+    auto kernel = xg128 ? grouped_mx_gemm_kernel<false, true> : grouped_mx_gemm_kernel<false, false>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kGemmThreads), 0, (hipStream_t)stream, X, Xs,
+                       ends, E_local, A, M_cap, K, N, Wp, Sp, out,
                        GemmActOut{nullptr, nullptr, 0, 0.f});
+  }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -750,6 +763,25 @@ extern "C" int moe_grouped_gemm2(const uint8_t* hq, const int32_t* hs, const int
                                  uint16_t* down, void* stream) {
   return moe::launch_grouped_gemm(hq, hs, expert_ends, E_local, A, M_cap, I, H, w2_packed,
                                   w2_scale_packed, down, stream);
+}
+
+extern "C" int moe_grouped_gemm1_g128(const uint8_t* xq, const int32_t* xs,
+                                      const int32_t* expert_ends, int E_local, int A, int M_cap,
+                                      int H, int I, const uint8_t* w13_packed,
+                                      const uint8_t* w13_scale_packed, uint16_t* gateup,
+                                      void* stream) {
+  if (I <= 0 || I % 64 != 0) return MOE_ERR_ALIGN;
+  return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I, w13_packed,
+                                  w13_scale_packed, gateup, stream, nullptr, true);
+}
+
+extern "C" int moe_grouped_gemm2_g128(const uint8_t* hq, const int32_t* hs,
+                                      const int32_t* expert_ends, int E_local, int A, int M_cap,
+                                      int I, int H, const uint8_t* w2_packed,
+                                      const uint8_t* w2_scale_packed, uint16_t* down,
+                                      void* stream) {
+  return moe::launch_grouped_gemm(hq, hs, expert_ends, E_local, A, M_cap, I, H, w2_packed,
+                                  w2_scale_packed, down, stream, nullptr, true);
 }
 
 extern "C" int moe_grouped_gemm1_act_quant(const uint8_t* xq, const int32_t* xs,

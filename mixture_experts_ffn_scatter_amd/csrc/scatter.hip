@@ -191,7 +191,10 @@ constexpr int kScanMaxE = 256;   // rows-kernel scan: local experts
 // redoes the small scan itself (start_e plus the token block's offset inside
 // expert e, for all e; block 0 also writes expert_ends). Otherwise `meta`
 // holds the block offsets and `starts` the expert starts.
-template <bool SCAN>
+// G128: one UE8M0 byte per 128 columns instead of per 32, packed four to a
+// word over 512 columns ([ceil(H/512)][M_cap] words; bytes of groups past H
+// are 0).
+template <bool SCAN, bool G128>
 __global__ __launch_bounds__(64 * kRowsWaves) void scatter_rows_kernel(
     const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int A,
     int M_cap, int TB, int W, const uint16_t* __restrict__ x, int H,
@@ -331,6 +334,10 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scatter_rows_kernel(
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      if constexpr (G128) {               // the 128-column group: 16 lanes
+        amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 8, 64));
+      }
       const uint32_t b = ue8m0_byte_of_amax(amax);
       const float inv = e8m0_reciprocal(b);
       uint32_t lo = 0, hi = 0;
@@ -338,15 +345,28 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scatter_rows_kernel(
       lo = cvt_e4m3x2<true>(v[2] * inv, v[3] * inv, lo);
       hi = cvt_e4m3x2<false>(v[4] * inv, v[5] * inv, hi);
       hi = cvt_e4m3x2<true>(v[6] * inv, v[7] * inv, hi);
-      uint32_t wd = b << (8 * ((lane >> 2) & 3));
-      wd |= __shfl_xor(wd, 4, 64);
-      wd |= __shfl_xor(wd, 8, 64);
+      uint32_t wd;
+      if constexpr (G128) {
+        // byte q of the chunk's word: the group of lanes 16q .. 16q + 15
+        const bool in = (c0 + j) * 512 + 128 * (lane >> 4) < H;
+        wd = (in ? b : 0u) << (8 * (lane >> 4));
+        wd |= __shfl_xor(wd, 16, 64);
+        wd |= __shfl_xor(wd, 32, 64);
+      } else {
+        wd = b << (8 * ((lane >> 2) & 3));
+        wd |= __shfl_xor(wd, 4, 64);
+        wd |= __shfl_xor(wd, 8, 64);
+      }
       for (uint64_t m = live; m; m &= m - 1) {   // wave-uniform loop over destination rows
         const int s = __ffsll((unsigned long long)m) - 1;
         const int r = __builtin_amdgcn_readlane(row, s);
         if (col < H) {
           *reinterpret_cast<uint2*>(xq + (size_t)r * H + col) = make_uint2(lo, hi);
-          if ((lane & 15) == 0) xs[(size_t)(col >> 7) * M_cap + r] = (int32_t)wd;
+          if constexpr (G128) {
+            if (lane == 0) xs[(size_t)(c0 + j) * M_cap + r] = (int32_t)wd;
+          } else {
+            if ((lane & 15) == 0) xs[(size_t)(col >> 7) * M_cap + r] = (int32_t)wd;
+          }
         }
       }
     }
@@ -377,12 +397,11 @@ extern "C" size_t moe_scatter_workspace_bytes(int T, int k, int E_local) {
   return (W + 1) * (size_t)E_local * sizeof(int32_t);   // block offsets, then starts
 }
 
-extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_start,
-                                     int E_local, int A, int M_cap, const uint16_t* x, int H,
-                                     int32_t* expert_ends, int32_t* route_row, uint8_t* xq,
-                                     int32_t* xs, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
-  using namespace moe;
+namespace moe {
+static int scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_start, int E_local,
+                             int A, int M_cap, const uint16_t* x, int H, int32_t* expert_ends,
+                             int32_t* route_row, uint8_t* xq, int32_t* xs, void* workspace,
+                             size_t workspace_bytes, void* stream, bool g128) {
   if (T < 0 || k < 1 || k > kScatterMaxK || E_local < 0 || E_local > kScatterMaxE || A < 1 ||
       M_cap < 0 || H <= 0 || (long long)T * k > INT_MAX)
     return MOE_ERR_SHAPE;
@@ -409,18 +428,39 @@ extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int 
     hipLaunchKernelGGL(scatter_count_kernel, dim3(W), dim3(256), 0, st, topk_ids, T * k,
                        expert_start, E_local, TB * k, meta);
     MOE_CHECK_LAUNCH();
-    hipLaunchKernelGGL(scatter_rows_kernel<true>, rows_grid, dim3(64 * kRowsWaves), 0, st,
-                       topk_ids, T, k, expert_start, E_local, A, M_cap, TB, W, x, H, meta,
-                       starts, expert_ends, route_row, xq, xs);
+    auto rows_kernel = g128 ? scatter_rows_kernel<true, true> : scatter_rows_kernel<true, false>;
+    hipLaunchKernelGGL(rows_kernel, rows_grid, dim3(64 * kRowsWaves), 0, st, topk_ids, T, k, expert_start,
+                       E_local, A, M_cap, TB, W, x, H, meta, starts, expert_ends, route_row, xq,
+                       xs);
     MOE_CHECK_LAUNCH();
   } else {
     hipLaunchKernelGGL(scatter_count_scan_kernel, dim3(1), dim3(1024), 0, st, topk_ids, T, k,
                        expert_start, E_local, A, TB, W, meta, starts, expert_ends);
     MOE_CHECK_LAUNCH();
-    hipLaunchKernelGGL(scatter_rows_kernel<false>, rows_grid, dim3(64 * kRowsWaves), 0, st,
-                       topk_ids, T, k, expert_start, E_local, A, M_cap, TB, W, x, H, meta,
-                       starts, expert_ends, route_row, xq, xs);
+    auto rows_kernel = g128 ? scatter_rows_kernel<false, true> : scatter_rows_kernel<false, false>;
+    hipLaunchKernelGGL(rows_kernel, rows_grid, dim3(64 * kRowsWaves), 0, st, topk_ids, T, k, expert_start,
+                       E_local, A, M_cap, TB, W, x, H, meta, starts, expert_ends, route_row, xq,
+                       xs);
     MOE_CHECK_LAUNCH();
   }
   return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_start,
+                                     int E_local, int A, int M_cap, const uint16_t* x, int H,
+                                     int32_t* expert_ends, int32_t* route_row, uint8_t* xq,
+                                     int32_t* xs, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return moe::scatter_endpoints(topk_ids, T, k, expert_start, E_local, A, M_cap, x, H, expert_ends,
+                                route_row, xq, xs, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int moe_scatter_endpoints_g128(const int32_t* topk_ids, int T, int k, int expert_start,
+                                          int E_local, int A, int M_cap, const uint16_t* x, int H,
+                                          int32_t* expert_ends, int32_t* route_row, uint8_t* xq,
+                                          int32_t* xs, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  return moe::scatter_endpoints(topk_ids, T, k, expert_start, E_local, A, M_cap, x, H, expert_ends,
+                                route_row, xq, xs, workspace, workspace_bytes, stream, true);
 }

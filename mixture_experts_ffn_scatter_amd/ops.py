@@ -90,7 +90,18 @@ class GroupedBuffers:
     out: torch.Tensor           # bf16 [T, H]
 
 
-def alloc_grouped(T, k, E_local, M_cap, H, I, device="cuda", fill: bool = False) -> GroupedBuffers:
+def scale_words(K: int, group: int = 32) -> int:
+    """Packed UE8M0 words per row for K columns: K/128 for group 32 (four
+    per-32 bytes a word), ceil(K/512) for group 128 (four per-128 bytes)."""
+    if group == 32:
+        return K // 128
+    if group == 128:
+        return (K + 511) // 512
+    raise ValueError(f"activation group {group} (32 or 128)")
+
+
+def alloc_grouped(T, k, E_local, M_cap, H, I, device="cuda", fill: bool = False,
+                  group: int = 32) -> GroupedBuffers:
     """Allocate every buffer of the prefill chain. ``fill=True`` plants the
     padding sentinels (bf16 NaN 0x7FC1, byte 0xA5, word 0xA5A5A5A5)."""
     def u8(*s):
@@ -115,14 +126,14 @@ def alloc_grouped(T, k, E_local, M_cap, H, I, device="cuda", fill: bool = False)
     return GroupedBuffers(
         expert_ends=torch.empty(E_local, dtype=torch.int32, device=device),
         route_row=torch.empty(T * k, dtype=torch.int32, device=device),
-        xq=u8(M_cap, H), xs=i32(H // 128, M_cap),
+        xq=u8(M_cap, H), xs=i32(scale_words(H, group), M_cap),
         workspace=torch.empty(ws, dtype=torch.uint8, device=device),
-        gateup=bf(M_cap, 2 * I), hq=u8(M_cap, I), hs=i32(I // 128, M_cap),
+        gateup=bf(M_cap, 2 * I), hq=u8(M_cap, I), hs=i32(scale_words(I, group), M_cap),
         down=bf(M_cap, H), out=bf(T, H))
 
 
 def moe_scatter_endpoints(topk_ids, expert_start: int, E_local: int, A: int, x,
-                          expert_ends, route_row, xq, xs, workspace):
+                          expert_ends, route_row, xq, xs, workspace, group: int = 32):
     _req(topk_ids, "topk_ids", (torch.int32,))
     T, k = topk_ids.shape
     _req(x, "x", _BF16)
@@ -132,12 +143,13 @@ def moe_scatter_endpoints(topk_ids, expert_start: int, E_local: int, A: int, x,
     _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
     _req(route_row, "route_row", (torch.int32,), (T * k,))
     _req(xq, "xq", (torch.uint8,), (M_cap, H))
-    _req(xs, "xs", (torch.int32,), (H // 128, M_cap))
+    _req(xs, "xs", (torch.int32,), (scale_words(H, group), M_cap))
     _req(workspace, "workspace", (torch.uint8,))
-    st = lib().moe_scatter_endpoints(_ptr(topk_ids), T, k, expert_start, E_local, A, M_cap,
+    fn = lib().moe_scatter_endpoints if group == 32 else lib().moe_scatter_endpoints_g128
+    st = fn(_ptr(topk_ids), T, k, expert_start, E_local, A, M_cap,
                                      _ptr(x), H, _ptr(expert_ends), _ptr(route_row), _ptr(xq),
                                      _ptr(xs), _ptr(workspace), workspace.numel(), _stream())
-    check(st, "moe_scatter_endpoints")
+    check(st, "moe_scatter_endpoints" + ("" if group == 32 else "_g128"))
 
 
 # ------------------------------------------------------------------ GEMMs
@@ -197,32 +209,36 @@ def moe_grouped_gemm1_act_quant(xq, xs, expert_ends, A: int, w13_gateup_packed,
     check(st, "moe_grouped_gemm1_act_quant")
 
 
-def moe_grouped_gemm1(xq, xs, expert_ends, A: int, w13_packed, w13_scale_packed, gateup):
+def moe_grouped_gemm1(xq, xs, expert_ends, A: int, w13_packed, w13_scale_packed, gateup,
+                      group: int = 32):
     M_cap, H = xq.shape
     E_local, twoI, _ = w13_packed.shape
     I = twoI // 2
     _req(xq, "xq", (torch.uint8,))
-    _req(xs, "xs", (torch.int32,), (H // 128, M_cap))
+    _req(xs, "xs", (torch.int32,), (scale_words(H, group), M_cap))
     _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
     _req(w13_packed, "w13_packed", (torch.uint8,), (E_local, 2 * I, H // 2))
     _req(w13_scale_packed, "w13_scale_packed", (torch.uint8,), packed_scale_shape(E_local, 2 * I, H))
     _req(gateup, "gateup", _BF16, (M_cap, 2 * I))
-    st = lib().moe_grouped_gemm1(_ptr(xq), _ptr(xs), _ptr(expert_ends), E_local, A, M_cap, H, I,
-                                 _ptr(w13_packed), _ptr(w13_scale_packed), _ptr(gateup), _stream())
-    check(st, "moe_grouped_gemm1")
+    fn = lib().moe_grouped_gemm1 if group == 32 else lib().moe_grouped_gemm1_g128
+    st = fn(_ptr(xq), _ptr(xs), _ptr(expert_ends), E_local, A, M_cap, H, I,
+            _ptr(w13_packed), _ptr(w13_scale_packed), _ptr(gateup), _stream())
+    check(st, "moe_grouped_gemm1" + ("" if group == 32 else "_g128"))
 
 
-def moe_act_quant_liverows(gateup, expert_ends, A: int, clamp_limit: float, hq, hs):
+def moe_act_quant_liverows(gateup, expert_ends, A: int, clamp_limit: float, hq, hs,
+                           group: int = 32):
     _req(gateup, "gateup", _BF16)
     M_cap, twoI = gateup.shape
     I = twoI // 2
     E_local = expert_ends.shape[0]
     _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
     _req(hq, "hq", (torch.uint8,), (M_cap, I))
-    _req(hs, "hs", (torch.int32,), (I // 128, M_cap))
-    st = lib().moe_act_quant_liverows(_ptr(gateup), _ptr(expert_ends), E_local, A, M_cap, I,
-                                      float(clamp_limit), _ptr(hq), _ptr(hs), _stream())
-    check(st, "moe_act_quant_liverows")
+    _req(hs, "hs", (torch.int32,), (scale_words(I, group), M_cap))
+    fn = lib().moe_act_quant_liverows if group == 32 else lib().moe_act_quant_liverows_g128
+    st = fn(_ptr(gateup), _ptr(expert_ends), E_local, A, M_cap, I,
+            float(clamp_limit), _ptr(hq), _ptr(hs), _stream())
+    check(st, "moe_act_quant_liverows" + ("" if group == 32 else "_g128"))
 
 
 def moe_act_quant_liverows_situ(gateup, expert_ends, A: int, hq, hs, situ_beta: float = 4.0,
@@ -240,18 +256,20 @@ def moe_act_quant_liverows_situ(gateup, expert_ends, A: int, hq, hs, situ_beta: 
     check(st, "moe_act_quant_liverows_situ")
 
 
-def moe_grouped_gemm2(hq, hs, expert_ends, A: int, w2_packed, w2_scale_packed, down):
+def moe_grouped_gemm2(hq, hs, expert_ends, A: int, w2_packed, w2_scale_packed, down,
+                      group: int = 32):
     M_cap, I = hq.shape
     E_local, H, _ = w2_packed.shape
     _req(hq, "hq", (torch.uint8,))
-    _req(hs, "hs", (torch.int32,), (I // 128, M_cap))
+    _req(hs, "hs", (torch.int32,), (scale_words(I, group), M_cap))
     _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
     _req(w2_packed, "w2_packed", (torch.uint8,), (E_local, H, I // 2))
     _req(w2_scale_packed, "w2_scale_packed", (torch.uint8,), packed_scale_shape(E_local, H, I))
     _req(down, "down", _BF16, (M_cap, H))
-    st = lib().moe_grouped_gemm2(_ptr(hq), _ptr(hs), _ptr(expert_ends), E_local, A, M_cap, I, H,
-                                 _ptr(w2_packed), _ptr(w2_scale_packed), _ptr(down), _stream())
-    check(st, "moe_grouped_gemm2")
+    fn = lib().moe_grouped_gemm2 if group == 32 else lib().moe_grouped_gemm2_g128
+    st = fn(_ptr(hq), _ptr(hs), _ptr(expert_ends), E_local, A, M_cap, I, H,
+            _ptr(w2_packed), _ptr(w2_scale_packed), _ptr(down), _stream())
+    check(st, "moe_grouped_gemm2" + ("" if group == 32 else "_g128"))
 
 
 # ---------------------------------------------------------------- combine

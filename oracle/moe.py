@@ -237,6 +237,43 @@ def scales_mn_major(bytes_rows: np.ndarray, rows: np.ndarray, M_cap: int, fill=N
     return out
 
 
+# ----------------------------------------------- group-128 activation recipe
+
+GROUP_128 = 128
+
+
+def quant_rows_g128(x_bf16_bits: np.ndarray):
+    """The group-128 activation recipe: FP8 e4m3 + UE8M0 per 128 columns
+    ("DeepGEMM FusedMoE on Blackwell (sglang)", overview table of quantised
+    data types and section 2.1.3: the MXFP4-experts recipe quantises
+    activations per (1,128), weights per (1,32)). Same quantiser as
+    quant_rows with 128 in place of 32."""
+    return quant_mx_e4m3(bf16_to_f32(x_bf16_bits), GROUP_128)
+
+
+def act_quant_rows_g128(gateup_bits: np.ndarray, I: int, clamp: float = 0.0):
+    """act_quant_rows with the group-128 recipe."""
+    return quant_mx_e4m3(act_rows_f32(gateup_bits, I, clamp), GROUP_128)
+
+
+def pack_g128_words(b128: np.ndarray) -> np.ndarray:
+    """u8 [R, G] per-128 bytes -> int32 [R, ceil(G/4)]: four consecutive
+    groups per word, group 4c+j in byte j of word c ("DeepGEMM FusedMoE on
+    Blackwell (sglang)", section 2.2.4: with UE8M0 the scales are int32 words
+    of 4 groups, ceil(K/128/4) per token); bytes past the last group are 0."""
+    b128 = np.asarray(b128, dtype=np.uint8)
+    R, G = b128.shape
+    pad = np.zeros((R, (G + 3) // 4 * 4), dtype=np.uint8)
+    pad[:, :G] = b128
+    return pack_ue8m0_words(pad)
+
+
+def expand_g128_bytes(b128: np.ndarray) -> np.ndarray:
+    """u8 [R, K/128] -> u8 [R, K/32]: a group's scale applies to each of its
+    four 32-column blocks (how a per-32 scaled contraction takes it)."""
+    return np.repeat(np.asarray(b128, dtype=np.uint8), 4, axis=-1)
+
+
 # ------------------------------------------------------------------- GEMM
 
 def dequant_e4m3_rows(codes, scale_bytes):
