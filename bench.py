@@ -253,8 +253,8 @@ def main():
     dom = "gemm1_act" if fused else "gemm1"
     ach = bytes_[dom] / (dur_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm",
-                "kernel": ("grouped_mx_gemm_kernel<true> (moe_grouped_gemm1_act_quant)" if fused
-                           else "grouped_mx_gemm_kernel<false> (moe_grouped_gemm1)"),
+                "kernel": ("grouped_mx_gemm_kernel<true, false> (moe_grouped_gemm1_act_quant)" if fused
+                           else "grouped_mx_gemm_kernel<false, false> (moe_grouped_gemm1)"),
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
                 "alg_bytes_per_launch": int(bytes_[dom]), "avg_launch_us": round(dur_us[dom], 3)}
@@ -280,12 +280,70 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
+        result["recipe_g128"] = bench_g128(ops, torch, up, c, ids, wts, logits_own, own_ids,
+                                           own_w, log)
         result["layers"] = bench_other_layers(ops, torch, up, up_bf16, log)
         result["actquant"] = bench_actquant(ops, torch, up, up_bf16, log)
         result["decode"] = bench_decode(ops, torch, up, up_bf16, log)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c, log)
     print(json.dumps(result), flush=True)
+
+
+def bench_g128(ops, torch, up, c, ids, wts, logits_own, own_ids, own_w, log, steps=20, warmup=5):
+    """The same layer with the group-128 activation recipe (scatter, GEMM1,
+    act-quant and GEMM2 with one UE8M0 byte per 128 columns; GEMM1 and the
+    act-quant as two launches, since no fused form exists for this recipe):
+    per-kernel HIP-event times of eager steps and the graph-replayed step."""
+    w = c.weights
+    w13, s13 = ops.moe_pack_mx_weights(up(w.w13), up(w.s13))
+    w2, s2 = ops.moe_pack_mx_weights(up(w.w2), up(w.s2))
+    x = torch.from_numpy(np.ascontiguousarray(c.x).view(np.int16)).cuda().view(torch.bfloat16)
+    buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, group=128)
+    names = ["route", "scatter", "gemm1", "act_quant", "gemm2", "combine"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ops.moe_route(logits_own, c.k, "softmax", None, own_ids, own_w)
+        mark(1)
+        ops.moe_scatter_endpoints(ids, 0, c.E_local, c.A, x, buf.expert_ends, buf.route_row,
+                                  buf.xq, buf.xs, buf.workspace, group=128)
+        mark(2)
+        ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13, buf.gateup, group=128)
+        mark(3)
+        ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, 0.0, buf.hq, buf.hs, group=128)
+        mark(4)
+        ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, w2, s2, buf.down, group=128)
+        mark(5)
+        ops.moe_combine(buf.down, buf.route_row, wts, c.routed_scale, buf.out)
+        mark(6)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    dur = {n: round(float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
+                                   for i in range(steps)])) * 1e3, 3) for j, n in enumerate(names)}
+    graph = ops.capture_graph(lambda: step(None))
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    del graph, buf
+    torch.cuda.empty_cache()
+    log("recipe g128", round(us, 2), dur)
+    return {"us_per_layer_graph": round(us, 2), "kernels_us": dur,
+            "note": "two-call GEMM1 + act-quant (no fused form for group 128)"}
 
 
 def _flush_caches(torch, scratch):
