@@ -94,6 +94,21 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
                                  NULL) == -3
     assert lib.moe_grouped_gemm2(NULL, NULL, NULL, 8, 128, 1152, 100, 256, NULL, NULL, NULL,
                                  NULL) == -3
+    # group-128 forms: the same checks as their group-32 counterparts
+    args = [NULL, 64, 2, 0, 8, 128, 1152, NULL, 200, NULL, NULL, NULL, NULL, NULL, 0, NULL]
+    assert lib.moe_scatter_endpoints_g128(*args) == -3
+    args[8] = 256
+    assert lib.moe_scatter_endpoints_g128(*args) == -1
+    assert lib.moe_act_quant_liverows_g128(NULL, NULL, 8, 128, 1152, 128, ctypes.c_float(7.3),
+                                           NULL, NULL, NULL) == -5
+    assert lib.moe_act_quant_liverows_g128(NULL, NULL, 8, 128, 1152, 100, ctypes.c_float(0.0),
+                                           NULL, NULL, NULL) == -3
+    assert lib.moe_grouped_gemm1_g128(NULL, NULL, NULL, 8, 128, 1152, 192, 128, NULL, NULL, NULL,
+                                      NULL) == -3
+    assert lib.moe_grouped_gemm2_g128(NULL, NULL, NULL, 8, 128, 1152, 100, 256, NULL, NULL, NULL,
+                                      NULL) == -3
+    assert lib.moe_grouped_gemm2_g128(NULL, NULL, NULL, 8, 128, 1152, 256, 256, NULL, NULL, NULL,
+                                      NULL) == -1
     # weight packing: K not a multiple of 128, N not of 16; empty is a no-op
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 256, 96, NULL, NULL, NULL) == -3
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 200, 128, NULL, NULL, NULL) == -3
