@@ -109,8 +109,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path is "
-              "built for one GPU's expert share; see the sharding notes in DESIGN.md)",
-              file=sys.stderr)
+              "built for one GPU's expert share: with expert parallelism each GPU would run "
+              "this same chain on the rows it receives)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
