@@ -35,15 +35,16 @@
 // Work decomposition. An item is (expert, n-tile of 256 columns, m-chunk of
 // up to 128 live rows); its cost grows with its live row blocks (a full
 // chunk takes about 1.6 times a one-block chunk). Chunks are ranked by
-// cost, full ones first, then partial ones by row blocks descending, and
-// dealt to the 8 XCDs in snake order (rank r to XCD r % 8 in even rounds,
-// 7 - r % 8 in odd ones) with all their n-tiles, so the items of a chunk
-// share its activations in one XCD's L2 (block b runs on XCD b % 8). An
-// XCD lists its items chunk-major, costliest first, and its blocks take
-// them in snake order over rounds, so a block with a costly item in one
-// round gets a cheap one in the next; the ranking is rebuilt inside every
-// block from expert_ends (a block-wide scan and count), so the grid depends
-// only on host-known sizes and no count is read back.
+// cost, full ones first, then partial ones by row blocks descending. The
+// full chunks are cut into 8 contiguous runs, one per XCD (block b runs on
+// XCD b % 8), so the chunks of a many-chunk expert share its weights in few
+// L2s; the partial chunks are dealt to the XCDs in snake order. Every chunk
+// goes with all its n-tiles, so the items of a chunk share its activations
+// in one XCD's L2. An XCD lists its items chunk-major, costliest first, and
+// its blocks take them in snake order over rounds, so a block with a costly
+// item in one round gets a cheap one in the next. The ranking is rebuilt
+// inside every block from expert_ends (a block-wide scan and count), so
+// the grid depends only on host-known sizes and no count is read back.
 //
 // Data path. Every operand travels global -> LDS by the buffer-to-LDS
 // transfer of gfx950 (no register staging) into a ring of 4 stages of one
@@ -284,18 +285,23 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   if (MT == 0) return;                   // no live rows (uniform over the block)
 
   // The schedule. Chunks are ranked by cost: the full ones first (expert
-  // order), then the partial ones by row blocks descending. Rank r goes to
-  // XCD r % 8 in even rounds of 8 and 7 - r % 8 in odd ones (snake order),
-  // with all its NT n-tiles, so the items of one chunk share its activations
-  // in that XCD's L2. An XCD lists its items chunk-major (costliest first),
-  // n-tile-minor, and its blocks take them in snake order over rounds of
-  // nslot items, so a block that got a costly item in one round gets a
-  // cheap one in the next. (Block b runs on XCD b % 8.)
+  // order), then the partial ones by row blocks descending. The full chunks
+  // are cut into 8 contiguous runs, one per XCD, so the chunks of an expert
+  // with several share its weights in one L2 where they can; the partial
+  // chunks are dealt in snake order (the j-th partial of XCD x is partial
+  // 8j + x for even j, 8j + 7 - x for odd j). Every chunk goes with all its
+  // NT n-tiles, so the items of a chunk share its activations in that XCD's
+  // L2. An XCD lists its items chunk-major (costliest first), n-tile-minor,
+  // and its blocks take them in snake order over rounds of nslot items, so a
+  // block that got a costly item in one round gets a cheap one in the next.
+  // (Block b runs on XCD b % 8.)
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int nslot = gridDim.x >> 3;      // the grid is a multiple of 8
-  const int kr = MT >> 3, rm = MT & 7;   // full rounds of chunks, remainder
-  const int nx = kr + (((kr & 1) ? 7 - xcd : xcd) < rm);   // chunks of this XCD
+  const int f0 = (int)(((long long)F * xcd) >> 3);          // this XCD's full chunks:
+  const int nf = (int)(((long long)F * (xcd + 1)) >> 3) - f0;   // ranks [f0, f0 + nf)
+  const int kr = P >> 3, rm = P & 7;     // full rounds of partial chunks, remainder
+  const int nx = nf + kr + (((kr & 1) ? 7 - xcd : xcd) < rm);   // chunks of this XCD
   const int nitems = nx * NT;
   // the block's k-th item (an index into the XCD's list), or -1 past its last
   auto item_at = [&](int k) {
@@ -306,7 +312,8 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   auto locate = [&](int item, GemmTile& T) {
     const int kq = item / NT;
     const int nt = item - kq * NT;
-    const int r = 8 * kq + ((kq & 1) ? 7 - xcd : xcd);       // chunk rank
+    const int jp = kq - nf;                                  // partial index, if >= 0
+    const int r = jp < 0 ? f0 + kq : F + 8 * jp + ((jp & 1) ? 7 - xcd : xcd);   // chunk rank
     int e, c;
     if (r < F) {
       // full chunk r: the last expert whose full-chunk prefix is <= r
