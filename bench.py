@@ -75,6 +75,12 @@ def counter_traffic():
     return None
 
 
+def local_counts(ids: np.ndarray, expert_start: int, E_local: int) -> np.ndarray:
+    """Routes per local expert (the live rows the grouped kernels process)."""
+    e = ids.reshape(-1).astype(np.int64) - expert_start
+    return np.bincount(e[(e >= 0) & (e < E_local)], minlength=E_local)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -221,13 +227,11 @@ def main():
     del graph
 
     # algorithmic work per launch, from the routed counts of this input
-    ends = buf.expert_ends.cpu().numpy().astype(np.int64)
-    starts = np.concatenate([[0], ((ends[:-1] + c.A - 1) // c.A) * c.A])
-    counts = ends - starts
+    ids_h = ids.cpu().numpy()
+    counts = local_counts(ids_h, 0, c.E_local)
     R = int(counts.sum())
     E_ne = int(np.count_nonzero(counts))
     H, I, T, k, E = c.H, c.I, c.T, c.k, c.E
-    ids_h = ids.cpu().numpy()
     U_tok = int(np.count_nonzero(np.any((ids_h >= 0) & (ids_h < c.E_local), axis=1)))
     bytes_ = {
         "route": c.own_tokens * E * 4 + c.own_tokens * k * 8,
@@ -413,10 +417,9 @@ def bench_other_layers(ops, torch, up, up_bf16, log, steps=20, warmup=5):
         torch.cuda.synchronize()
         us = (time.perf_counter() - t0) * 1e6 / steps
         del graph
-        ends = buf.expert_ends.cpu().numpy().astype(np.int64)
-        starts = np.concatenate([[0], ((ends[:-1] + c.A - 1) // c.A) * c.A])
-        R = int((ends - starts).sum())
-        E_ne = int(np.count_nonzero(ends - starts))
+        counts = local_counts(ids.cpu().numpy(), 0, c.E_local)
+        R = int(counts.sum())
+        E_ne = int(np.count_nonzero(counts))
         H, I = c.H, c.I
         b1 = E_ne * (2 * I * H // 2 + 2 * I * H // 32) + R * (H + H // 32) + R * (I + I // 32)
         b2 = E_ne * (H * I // 2 + H * I // 32) + R * (I + I // 32) + R * H * 2
@@ -435,19 +438,34 @@ def bench_other_layers(ops, torch, up, up_bf16, log, steps=20, warmup=5):
     return out
 
 
+def product_expert_ends(ops, torch, counts, A):
+    """expert_ends of a layout with the given per-expert live-row counts, made
+    by the library's own scatter: one route per live row (k = 1), routed to
+    its expert in expert order, on a zero x of width 128."""
+    counts = np.asarray(counts, np.int64)
+    E = counts.shape[0]
+    R = int(counts.sum())
+    ids = torch.from_numpy(np.repeat(np.arange(E, dtype=np.int32), counts)[:, None].copy()).cuda()
+    m_cap = ((R + E * A + 3) // 4) * 4
+    x = torch.zeros((R, 128), dtype=torch.bfloat16, device="cuda")
+    buf = ops.alloc_grouped(R, 1, E, m_cap, 128, 128)
+    ops.moe_scatter_endpoints(ids, 0, E, A, x, buf.expert_ends, buf.route_row, buf.xq, buf.xs,
+                              buf.workspace)
+    torch.cuda.synchronize()
+    return buf.expert_ends.clone()
+
+
 def bench_actquant(ops, torch, up, up_bf16, log, iters=20):
     import workloads as W
     out = {}
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     for full in (False, True):
         case = W.actquant(full=full)
-        ends_h = np.zeros(case.E_local, np.int64)
-        pos = 0
-        for e, cnt in enumerate(case.counts):
-            pos = ((pos + case.A - 1) // case.A) * case.A + int(cnt)
-            ends_h[e] = pos
-        gate = up_bf16(case.gateup)
-        ends = up(ends_h.astype(np.int32))
+        ends = product_expert_ends(ops, torch, case.counts, case.A)
+        # every row of the buffer holds N(0,1) data (the kernel reads only the
+        # live ones; where they sit is the layout's business)
+        reps = -(-case.M_cap // case.live.shape[0])
+        gate = up_bf16(np.tile(case.live, (reps, 1))[: case.M_cap])
         hq = torch.empty((case.M_cap, case.I), dtype=torch.uint8, device="cuda")
         hs = torch.empty((case.I // 128, case.M_cap), dtype=torch.int32, device="cuda")
         R = int(case.counts.sum())

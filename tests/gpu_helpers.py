@@ -56,3 +56,14 @@ def end_to_end_ok(y_bits: np.ndarray, ref_bits: np.ndarray, max_rel=2e-2, mean_r
     mx = d.max() / max(np.abs(r).max(), 1e-30)
     mean = d.mean() / max(np.sqrt((r ** 2).mean()), 1e-30)
     return (mx <= max_rel and mean <= mean_rel), mx, mean
+
+
+def actquant_case(**kw):
+    """workloads.actquant with its live rows placed in the grouped buffer at
+    the starts the oracle's endpoint recurrence gives (padding rows NaN)."""
+    import workloads as W
+    from oracle import moe as M
+    case = W.actquant(**kw)
+    start, _ = M.endpoints(case.counts, case.A)
+    case.gateup = W.place_rows(case.live, case.counts, start, case.M_cap)
+    return case

@@ -10,7 +10,7 @@ import torch
 import workloads as W
 from oracle import formats as F
 from oracle import moe as M
-from tests.gpu_helpers import (BF16_SENT, BYTE_SENT, WORD_SENT, dev, dev_bf16, gemm_within_bound,
+from tests.gpu_helpers import (BF16_SENT, BYTE_SENT, WORD_SENT, actquant_case, dev, dev_bf16, gemm_within_bound,
                                host, say)
 
 pytestmark = pytest.mark.gpu
@@ -59,9 +59,9 @@ def test_act_quant_liverows_g128(ops, I, clamp, small):
     say(f"act-quant g128 I={I} clamp={clamp}")
     if small:
         counts = np.array([5, 0, 17, 1, 0, 9, 40], np.int64)
-        case = W.actquant(counts=counts, E_local=7, I=I, A=8, M_cap=128)
+        case = actquant_case(counts=counts, E_local=7, I=I, A=8, M_cap=128)
     else:
-        case = W.actquant()
+        case = actquant_case()
     start, end = M.endpoints(case.counts, case.A)
     hq = torch.full((case.M_cap, case.I), BYTE_SENT, dtype=torch.uint8, device="cuda")
     hs = torch.full((_words(case.I), case.M_cap), int(WORD_SENT), dtype=torch.int32, device="cuda")

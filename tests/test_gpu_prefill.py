@@ -12,7 +12,7 @@ import torch
 import workloads as W
 from oracle import formats as F
 from oracle import moe as M
-from tests.gpu_helpers import (BF16_SENT, BYTE_SENT, WORD_SENT, dev, dev_bf16, end_to_end_ok,
+from tests.gpu_helpers import (BF16_SENT, BYTE_SENT, WORD_SENT, actquant_case, dev, dev_bf16, end_to_end_ok,
                                gemm_within_bound, host, say)
 
 pytestmark = pytest.mark.gpu
@@ -233,7 +233,7 @@ def _check_act(case, start, end, hq, hs, rows, clamp=0.0):
 
 def test_act_quant_liverows_3072_of_28672(ops):
     say("act-quant 3072 live of 28672")
-    case = W.actquant()
+    case = actquant_case()
     start, end, hq, hs = _run_act(ops, case)
     live = np.flatnonzero(M.live_row_mask(start, end, case.M_cap))
     assert live.size == 3072
@@ -242,7 +242,7 @@ def test_act_quant_liverows_3072_of_28672(ops):
 
 def test_act_quant_full_buffer_sampled(ops):
     say("act-quant full buffer 28672 rows")
-    case = W.actquant(full=True)
+    case = actquant_case(full=True)
     start, end, hq, hs = _run_act(ops, case)
     rows = np.sort(np.random.default_rng(3).choice(case.M_cap, 1024, replace=False))
     _check_act(case, start, end, hq, hs, rows)
@@ -252,7 +252,7 @@ def test_act_quant_clamp_small_I_odd_alignment(ops):
     say("act-quant clamp 25, I=384, A=8")
     rng = np.random.default_rng(9)
     counts = np.array([5, 0, 17, 1, 0, 9], np.int64)
-    case = W.actquant(counts=counts, E_local=6, I=384, A=8, M_cap=64)
+    case = actquant_case(counts=counts, E_local=6, I=384, A=8, M_cap=64)
     # scale live rows so that the clamp engages on both sides
     live = M.live_row_mask(*M.endpoints(counts, 8), 64)
     g = F.bf16_to_f32(case.gateup).astype(np.float64) * 30.0
@@ -264,7 +264,7 @@ def test_act_quant_clamp_small_I_odd_alignment(ops):
 
 def test_act_quant_empty_and_all_empty(ops):
     say("act-quant all-empty")
-    case = W.actquant(counts=np.zeros(4, np.int64), E_local=4, I=256, A=128, M_cap=512)
+    case = actquant_case(counts=np.zeros(4, np.int64), E_local=4, I=256, A=128, M_cap=512)
     start, end, hq, hs = _run_act(ops, case)
     assert np.all(hq == BYTE_SENT) and np.all(hs == WORD_SENT)
 
@@ -290,7 +290,7 @@ def test_act_quant_situ_liverows_3072_of_28672(ops):
     """SiTU (Kimi-K3's 4 / 25) on the act-quant layout: bytes equal the
     oracle's on every live row, padding (NaN-filled) untouched."""
     say("act-quant SiTU 3072 live of 28672")
-    case = W.actquant()
+    case = actquant_case()
     start, end, hq, hs = _run_act_situ(ops, case)
     live = np.flatnonzero(M.live_row_mask(start, end, case.M_cap))
     _check_act_situ(case, start, end, hq, hs, live)
@@ -320,7 +320,7 @@ def test_act_quant_situ_every_bf16(ops, side):
     _check_act_situ(case, start, end, hq, hs, np.arange(rows))
 
 
-# -------------------------------------------------------------------- GEMMs# -------------------------------------------------------------------- GEMMs
+# -------------------------------------------------------------------- GEMMs
 
 def _tiny_state(ops, c, clamp=0.0):
     ids, wts = M.route_softmax(c.logits, c.k)

@@ -115,3 +115,84 @@ def test_gemv_fp8_and_mxfp4_special_cases():
     sb = np.full((N, K // 32), 128, np.uint8)        # 2^1
     y4, _ = M.gemv_mxfp4(act, wp, sb, np.zeros(N, np.uint16))
     assert np.array_equal(F.bf16_to_f32(y4), a[:, 1:2 * N:2] * 2)
+
+
+def test_combine_slot_order_in_fp32():
+    """The slot order and the fp32 accumulator are fixed by the combine of
+    "DeepGEMM FusedMoE on Blackwell (sglang)", section 2.6.1 (a running fp32
+    sum over k in order). With weight 1 and rows 2^24, 1, -2^24 in slot order
+    the 1 is absorbed (2^24 + 1 rounds to 2^24 in fp32) and the result is 0;
+    summed in the reverse order, or in fp64, the result is 1."""
+    rows = np.array([[2.0 ** 24], [1.0], [-(2.0 ** 24)]], np.float32)
+    w = np.ones((1, 3), np.float32)
+    out = M.combine(rows, np.array([[0, 1, 2]]), w)
+    assert F.bf16_to_f32(out)[0, 0] == 0.0
+    rev = M.combine(rows, np.array([[2, 1, 0]]), w)
+    assert F.bf16_to_f32(rev)[0, 0] == 1.0
+    # a skipped slot keeps its place: the sum still runs in slot order
+    rows4 = np.vstack([rows, [[7.0]]]).astype(np.float32)
+    out4 = M.combine(rows4, np.array([[0, -1, 1, 2]]), np.ones((1, 4), np.float32))
+    assert F.bf16_to_f32(out4)[0, 0] == 0.0
+
+
+def _fp32_product_rounded_down_onto(target: float, v: float) -> float:
+    """An fp32 w with fl32(w * v) == target while the exact w * v lies above
+    target (so the product's rounding drops a positive remainder)."""
+    from fractions import Fraction
+    w = np.float32(target / v)
+    for _ in range(64):
+        w = np.nextafter(w, np.float32(-np.inf))
+    for _ in range(129):
+        if (np.float32(w) * np.float32(v) == np.float32(target)
+                and Fraction(float(w)) * Fraction(float(v)) > Fraction(target)):
+            return float(w)
+        w = np.nextafter(w, np.float32(np.inf))
+    raise AssertionError("no such w near target / v")
+
+
+def test_combine_rounds_product_then_sum():
+    """Each slot's product w * v is rounded to fp32 before it is added (two
+    roundings, no fused multiply-add). Built so that the difference reaches
+    the bf16 output: slot 0 puts 1.0 in the accumulator, slot 1's product
+    rounds exactly onto 2^-8 + 2^-24, which makes 1 + 2^-8 + 2^-24 an fp32 tie
+    (to even: 1 + 2^-8, itself a bf16 tie that goes to 1.0). Fused, the
+    dropped remainder of the product would push the sum above the tie and
+    the output to the next bf16 value 1 + 2^-7."""
+    from fractions import Fraction
+    v = 1.0 + 2.0 ** -7                       # a bf16 value
+    target = 2.0 ** -8 + 2.0 ** -24
+    w1 = _fp32_product_rounded_down_onto(target, v)
+    rows = np.array([[1.0], [v]], np.float32)
+    w = np.array([[1.0, w1]], np.float32)
+    out = M.combine(rows, np.array([[0, 1]]), w)
+    assert F.bf16_to_f32(out)[0, 0] == 1.0
+    # fused: 1 + w1 * v exactly lies strictly between the fp32 tie 1 + 2^-8 +
+    # 2^-24 and the next fp32 value 1 + 2^-8 + 2^-23, so it rounds up to the
+    # latter, which is above the bf16 midpoint 1 + 2^-8
+    exact = Fraction(1) + Fraction(w1) * Fraction(v)
+    assert Fraction(1) + Fraction(target) < exact < 1 + Fraction(1, 2 ** 8) + Fraction(1, 2 ** 23)
+    up = np.array([1.0 + 2.0 ** -8 + 2.0 ** -23], np.float32)
+    assert F.bf16_to_f32(F.round_to_bf16(up))[0] == 1.0 + 2.0 ** -7
+
+
+def test_glu_alpha_is_the_sigmoid_gelu_approximation():
+    """With beta = 0, u = 1 and no clamp the decode GLU is g * sigma(alpha g).
+    For alpha = 1.702 that is the published sigmoid approximation of GELU
+    (Hendrycks and Gimpel, "Gaussian Error Linear Units", section 2:
+    x * Phi(x) ~ x * sigma(1.702 x)), whose error stays below 0.021 on the
+    whole real line. GELU here is the closed form x * (1 + erf(x / sqrt 2)) / 2.
+    sigma(g) in place of sigma(alpha g) misses by about 0.19 at g = 2."""
+    import math
+    g = F.round_to_bf16(np.linspace(-8.0, 8.0, 2001))
+    gv = F.bf16_to_f32(g).astype(np.float64)
+    one = F.round_to_bf16(np.ones_like(gv))
+    y = F.bf16_to_f32(M.glu(g, one, 1.702, 0.0, 0.0)).astype(np.float64)
+    gelu = np.array([x * 0.5 * (1.0 + math.erf(x / math.sqrt(2.0))) for x in gv])
+    # approximation error plus one bf16 rounding of the output
+    assert np.all(np.abs(y - gelu) <= 0.021 + 2.0 ** -8 * np.abs(gelu))
+    plain = F.bf16_to_f32(M.glu(g, one, 1.0, 0.0, 0.0)).astype(np.float64)
+    assert np.max(np.abs(plain - gelu)) > 0.15
+    # (u + beta), not u * beta or u alone: with u = 0 the factor is beta
+    zero = F.round_to_bf16(np.zeros_like(gv))
+    y_b = F.bf16_to_f32(M.glu(g, zero, 1.702, 1.0, 0.0)).astype(np.float64)
+    assert np.array_equal(y_b, y)

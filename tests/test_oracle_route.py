@@ -53,3 +53,62 @@ def test_sigmoid_bias_only_selects():
     assert ids.tolist() == [[0, 3]]
     s = expit(np.array([0.0, 0.3]))
     assert np.allclose(w[0], s / s.sum(), rtol=2 ** -21)     # weights ignore the bias
+
+
+def _brute_sigmoid_bias(logits_row, bias, k):
+    """Every k-subset of experts, keyed by fl32(fl32(sigma(l)) + b) with sigma
+    from scipy's expit in fp64 (then rounded to fp32): the best subset is the
+    one whose sorted (-key, index) list is smallest."""
+    import itertools
+    s = expit(logits_row.astype(np.float64)).astype(np.float32)
+    key = (s + bias).astype(np.float32)
+    best = None
+    for sub in itertools.combinations(range(len(logits_row)), k):
+        order = sorted(sub, key=lambda e: (-float(key[e]), e))
+        cand = [(-float(key[e]), e) for e in order]
+        if best is None or cand < best[0]:
+            best = (cand, order)
+    ids = best[1]
+    sel = s[ids].astype(np.float64)
+    return ids, sel / sel.sum()
+
+
+def test_sigmoid_bias_bruteforce_nonzero_bias():
+    """Selection with a non-zero correction bias ("Kimi-K3 on SM120
+    FlashInfer MXFP4", Phase 1 call chain: select on sigma + bias, weigh
+    by sigma alone), against every k-subset on small expert counts. Logits
+    and biases are drawn from a few values so that exact key ties occur."""
+    rng = np.random.default_rng(31)
+    for _ in range(150):
+        E = int(rng.integers(2, 8))
+        k = int(rng.integers(1, E + 1))
+        logits = (rng.integers(-4, 5, size=(2, E)) * 0.25).astype(np.float32)
+        bias = (rng.integers(-2, 3, size=E) * 0.0625).astype(np.float32)
+        ids, w = M.route_sigmoid_bias(logits, bias, k)
+        for t in range(2):
+            bids, bw = _brute_sigmoid_bias(logits[t], bias, k)
+            assert ids[t].tolist() == list(bids)
+            assert np.allclose(w[t], bw, rtol=2 ** -21, atol=0)
+
+
+def test_sigmoid_bias_key_is_an_fp32_sum():
+    """The key is fl32(sigma + b): a bias below half an ulp of sigma is lost in
+    the fp32 add, which turns a strict fp64 preference into a tie that goes
+    to the lower expert index. sigma(0) = 0.5 exactly; 2^-25 is half an ulp
+    of 0.5, and the tie rounds to even (0.5)."""
+    logits = np.zeros((1, 3), np.float32)
+    bias = np.array([0.0, 0.0, 2.0 ** -25], np.float32)
+    ids, w = M.route_sigmoid_bias(logits, bias, 1)
+    assert ids.tolist() == [[0]]              # an fp64 key would pick expert 2
+    bias[2] = 2.0 ** -24                      # a whole ulp survives the add
+    ids, _ = M.route_sigmoid_bias(logits, bias, 1)
+    assert ids.tolist() == [[2]]
+    # a bias can reorder experts whose sigmoids differ, and the weights still
+    # come from the sigmoids alone
+    logits = np.array([[1.0, 0.5, -0.5]], np.float32)
+    bias = np.array([-0.3, 0.0, 0.5], np.float32)
+    ids, w = M.route_sigmoid_bias(logits, bias, 2)
+    s = expit(np.array([1.0, 0.5, -0.5]))
+    key = s + np.array([-0.3, 0.0, 0.5])
+    assert ids.tolist() == [list(np.argsort(-key)[:2])] == [[2, 1]]
+    assert np.allclose(w[0], s[[2, 1]] / s[[2, 1]].sum(), rtol=2 ** -21)

@@ -191,8 +191,9 @@ class ActQuantCase:
     A: int
     M_cap: int
     counts: np.ndarray      # int64 [E_local]
-    gateup: np.ndarray      # bf16 bits [M_cap, 2I]; rows outside [start,end) hold NaN
+    live: np.ndarray        # bf16 bits [sum(counts), 2I]: expert 0's rows, then expert 1's, ...
     clamp: float = 0.0
+    gateup: Optional[np.ndarray] = None   # the padded [M_cap, 2I] buffer, once placed
 
 
 def actquant_counts(seed: int = SEEDS["actquant"], E_local: int = 32, live: int = 3072,
@@ -208,24 +209,34 @@ def actquant_counts(seed: int = SEEDS["actquant"], E_local: int = 32, live: int 
 def actquant(seed: int = SEEDS["actquant"], full: bool = False, E_local: int = 32, I: int = 2048,
              A: int = 128, M_cap: int = 28672, live: int = 3072,
              counts: Optional[np.ndarray] = None) -> ActQuantCase:
-    """Standalone act-quant input. ``full=True`` makes every allocated row
-    live (count 896 for each of the 32 experts)."""
+    """Standalone act-quant input: per-expert live-row counts and the live
+    gate/up rows themselves, N(0,1), in expert order. ``full=True`` makes
+    every allocated row live (count 896 for each of the 32 experts). Where
+    the rows sit in the grouped buffer is the method's business: callers
+    place them with ``place_rows`` at the starts of their own layout."""
     if counts is None:
         counts = (np.full(E_local, M_cap // E_local, dtype=np.int64) if full
                   else actquant_counts(seed, E_local, live))
     rng = rng_for(seed + 7919)
-    gateup = np.full((M_cap, 2 * I), BF16_NAN_SENTINEL, dtype=np.uint16)
-    # rows are laid out with the aligned recurrence; the draw fills exactly
-    # the rows a correct layout calls live, everything else stays NaN
-    pos = 0
-    for c in counts:
-        pos = ((pos + A - 1) // A) * A
-        if c:
-            gateup[pos:pos + c] = normal_bf16(rng, (int(c), 2 * I))
-        pos += int(c)
-    assert pos <= M_cap
+    rows = normal_bf16(rng, (int(counts.sum()), 2 * I))
     return ActQuantCase("actquant-full" if full else "actquant", E_local, I, A, M_cap,
-                        counts, gateup)
+                        counts, rows)
+
+
+def place_rows(live: np.ndarray, counts: np.ndarray, starts: np.ndarray, M_cap: int,
+               fill=BF16_NAN_SENTINEL) -> np.ndarray:
+    """Copy expert e's block of ``live`` (counts[e] rows, experts in order) to
+    rows [starts[e], starts[e] + counts[e]) of an [M_cap, width] buffer whose
+    other rows hold ``fill``. Pure data movement: the starts come from the
+    caller's layout."""
+    out = np.full((M_cap, live.shape[1]), fill, dtype=live.dtype)
+    src = 0
+    for c, st in zip(np.asarray(counts, np.int64), np.asarray(starts, np.int64)):
+        c, st = int(c), int(st)
+        if c:
+            out[st:st + c] = live[src:src + c]
+        src += c
+    return out
 
 
 @dataclass
