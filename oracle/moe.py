@@ -277,15 +277,27 @@ def expand_g128_bytes(b128: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------------- GEMM
 
 def dequant_e4m3_rows(codes, scale_bytes):
-    v = e4m3_decode(codes)
-    s = e8m0_decode(scale_bytes)
-    return v * np.repeat(s, GROUP, axis=-1)
+    """code value times 2^(scale - 127) of its 32-column group (fp64, exact)."""
+    codes = np.asarray(codes, np.uint8)
+    v = e4m3_decode(codes).reshape(codes.shape[:-1] + (-1, GROUP))
+    s = e8m0_decode(scale_bytes)[..., None]
+    return (v * s).reshape(codes.shape)
+
+
+# byte -> (value of its low nibble, value of its high nibble): the two E2M1
+# elements a byte packs, even column first
+_E2M1_BYTE_PAIRS = np.stack([E2M1_VALUES[np.arange(256) & 0xF],
+                             E2M1_VALUES[np.arange(256) >> 4]], axis=-1)
 
 
 def dequant_mxfp4_rows(packed, scale_bytes):
-    v = e2m1_decode(e2m1_unpack(packed))
-    s = e8m0_decode(scale_bytes)
-    return v * np.repeat(s, GROUP, axis=-1)
+    """E2M1 element value times 2^(scale - 127) of its 32-column group (fp64,
+    exact); elements 2i and 2i+1 are the low and high nibble of byte i."""
+    packed = np.asarray(packed, np.uint8)
+    lead = packed.shape[:-1]
+    v = _E2M1_BYTE_PAIRS[packed].reshape(lead + (-1, GROUP))
+    s = e8m0_decode(scale_bytes)[..., None]
+    return (v * s).reshape(lead + (2 * packed.shape[-1],))
 
 
 def _code_lsb_table(values: np.ndarray) -> np.ndarray:
@@ -304,12 +316,17 @@ _LSB_E4M3 = _code_lsb_table(E4M3_VALUES)
 _LSB_E2M1 = _code_lsb_table(E2M1_VALUES)
 
 
-def _row_lsb_min(code_lsb: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
+# per packed E2M1 byte: the smaller lowest-set-bit exponent of its two elements
+_LSB_E2M1_BYTE = np.minimum(_LSB_E2M1[np.arange(256) & 0xF], _LSB_E2M1[np.arange(256) >> 4])
+
+
+def _row_lsb_min(code_lsb: np.ndarray, scale_bytes: np.ndarray, per_group: int = GROUP) -> np.ndarray:
     """Per row: the smallest lowest-set-bit exponent over its non-zero
-    entries, where an entry is code * 2^(scale-127) per 32 columns."""
+    entries, where an entry is code * 2^(scale-127) per 32 columns
+    (``code_lsb`` holds ``per_group`` values per 32-column group)."""
     s = scale_bytes.astype(np.int64) - 127
-    per_group = code_lsb.reshape(code_lsb.shape[0], -1, GROUP).min(-1) + s
-    return per_group.min(-1)
+    group_min = code_lsb.reshape(code_lsb.shape[0], -1, per_group).min(-1) + s
+    return group_min.min(-1)
 
 
 def block_max_bound(aq, ab, wq_packed, wb, block: int = 128):
@@ -344,7 +361,7 @@ def mx_gemm(aq, ab, wq_packed, wb, check_exact: bool = True):
         # every term is a multiple of 2^(lsb_a + lsb_w); the fp64 sums are exact
         # while the sum of magnitudes stays below 2^53 such units
         la = _row_lsb_min(_LSB_E4M3[np.asarray(aq, np.uint8)], ab)
-        lw = _row_lsb_min(_LSB_E2M1[e2m1_unpack(wq_packed)], wb)
+        lw = _row_lsb_min(_LSB_E2M1_BYTE[np.asarray(wq_packed, np.uint8)], wb, GROUP // 2)
         lsb = la[:, None] + lw[None, :]
         limit = np.ldexp(1.0, np.minimum(lsb + 53, 1000).astype(np.int64))
         bad = (tsum > 0) & (tsum >= limit)
@@ -400,12 +417,15 @@ class PrefillResult:
 
 def prefill_expert_major(x_bits, ids, weights, expert_start, E_local, A, I,
                          w13, s13, w2, s2, clamp=0.0, routed_scale=1.0,
-                         check_exact=True) -> PrefillResult:
+                         check_exact=True, workers: int = 1) -> PrefillResult:
     """The six-step chain in expert-major order ("Blackwell DeepGEMM
     FusedMoE (sglang)", section 1.1 stages 2-6; "Blackwell FP4 MoE: live-row
     boundary", section 2: scatter -> FC1(endpoint) -> SiLU+mul+quant(endpoint)
     -> FC2(endpoint)): scatter, quantise x per route row, GEMM1 per expert,
-    act-quant, GEMM2 per expert, combine by route row."""
+    act-quant, GEMM2 per expert, combine by route row.
+
+    Experts touch disjoint rows, so ``workers`` > 1 runs the per-expert
+    steps on a thread pool; the results are the same arrays."""
     T, k = np.asarray(ids).shape
     H = x_bits.shape[1]
     sc = scatter_routes(ids, expert_start, E_local, A)
@@ -422,13 +442,21 @@ def prefill_expert_major(x_bits, ids, weights, expert_start, E_local, A, I,
     down = np.zeros((n, H), np.uint16)
     dex = np.zeros((n, H))
     dts = np.zeros((n, H))
-    for e in range(E_local):
+    def one_expert(e):
         sel = np.flatnonzero(le == e)       # ascending route order == ascending row order
         if sel.size == 0:
-            continue
+            return
         gateup[sel], gex[sel], gts[sel] = mx_gemm(xq[sel], xb[sel], w13[e], s13[e], check_exact)
         hq[sel], hb[sel] = act_quant_rows(gateup[sel], I, clamp)
         down[sel], dex[sel], dts[sel] = mx_gemm(hq[sel], hb[sel], w2[e], s2[e], check_exact)
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one_expert, np.unique(le)))
+    else:
+        for e in range(E_local):
+            one_expert(e)
     # combine reads down rows by their layout row index
     rows = np.zeros((max(int(sc.end.max()) if E_local else 0, 1), H), np.float32)
     rows[sc.route_row[lr]] = bf16_to_f32(down)

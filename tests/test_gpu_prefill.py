@@ -520,8 +520,8 @@ def test_large_e_full_size_chain_sampled(ops):
     and permutation bit-exact; quantised x, GEMM1, act-quant and GEMM2 on
     sampled rows of the hottest, a middle and the coldest live expert; the
     fused GEMM1 + act-quant byte-identical to the two calls over the whole
-    buffer; combine bit-exact on sampled tokens; one token end to end against
-    the token-major chain."""
+    buffer; the fused chain run twice bitwise equal; combine bit-exact and
+    64 tokens end to end against the oracle."""
     say("large-E full size: generating inputs (15.7 GB of weights)")
     c = W.large()
     w = c.weights
@@ -589,18 +589,44 @@ def test_large_e_full_size_chain_sampled(ops):
         bm = M.block_max_bound(hq[rows], hb, w.w2[e], w.s2[e])
         ok, _, _ = gemm_within_bound(dn[rows], exact, tsum, c.I, bm)
         assert ok.all(), f"gemm2 expert {e}: {np.count_nonzero(~ok)} outside bound"
-    say("large-E full size: combine on sampled tokens, one token end to end")
+    say("large-E full size: the fused chain again, bitwise equal (determinism)")
     out = host(buf.out)
-    toks = np.array([0, 1, c.T // 2, c.T - 1])
+    w13g, s13g = ops.moe_pack_mx_weights_gateup(dev(w.w13), dev(w.s13))
+    buf2 = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, fill=True)
+    ops.moe_ffn_prefill_fused(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A, w13g, s13g, w2p, s2p,
+                              buf2, clamp_limit=c.clamp)
+    y2 = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, fill=True)
+    ops.moe_ffn_prefill_fused(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A, w13g, s13g, w2p, s2p,
+                              y2, clamp_limit=c.clamp)
+    assert torch.equal(buf2.out.view(torch.int16), y2.out.view(torch.int16))
+    assert torch.equal(buf2.down.view(torch.int16), y2.down.view(torch.int16))
+    assert np.array_equal(host(buf2.out), out)      # and equal to the two-call chain above
+    del buf2, y2, w13g, s13g
+
+    # 64 tokens end to end: a greedy pick that keeps the set of experts they
+    # route to small (so the oracle finishes in seconds), plus the first and
+    # last token
+    toks = [0, c.T - 1]
+    used_e = set(ids[0].tolist()) | set(ids[c.T - 1].tolist())
+    cand = set(range(1, c.T - 1))
+    sets = [set(r.tolist()) for r in ids]
+    while len(toks) < 64:
+        t = max(cand, key=lambda u: (len(sets[u] & used_e), -u))
+        toks.append(t)
+        cand.remove(t)
+        used_e |= sets[t]
+    toks = np.array(sorted(toks))
+    say(f"large-E full size: combine and {toks.size} tokens end to end ({len(used_e)} experts)")
     ros = rr.reshape(c.T, c.k)[toks]
     used = np.unique(ros[ros >= 0])
     rows_f32 = np.zeros((c.M_cap, c.H), np.float32)    # only the rows these tokens read
     rows_f32[used] = F.bf16_to_f32(dn[used])
     want = M.combine(rows_f32, ros.ravel(), wts[toks], 1.0)
     assert np.array_equal(out[toks], want)
-    ref = M.prefill_token_major(c.x, ids, wts, 0, c.E_local, c.I, w.w13, w.s13, w.w2, w.s2,
-                                clamp=c.clamp, tokens=np.array([c.T // 2]))
-    ok, mx, mean = end_to_end_ok(out[[c.T // 2]], ref)
+    ref = M.prefill_expert_major(c.x[toks], ids[toks], wts[toks], 0, c.E_local, c.A, c.I,
+                                 w.w13, w.s13, w.w2, w.s2, clamp=c.clamp, workers=16)
+    ok, mx, mean = end_to_end_ok(out[toks], ref.out)
+    say(f"  max |d| / max |ref| = {mx:.3e}, mean |d| / rms(ref) = {mean:.3e}")
     assert ok, (mx, mean)
 
 
@@ -696,7 +722,7 @@ def _fused_vs_two_call(ops, xq, xs, ends, A, w13, s13, clamp):
             ops.moe_grouped_gemm1(dev(xq), dev(xs), ends_d, A, wp, sp, gateup)
             ops.moe_act_quant_liverows(gateup, ends_d, A, clamp, hq, hs)
         outs.append((host(hq), host(hs)))
-    return outs
+    return outs + [host(gateup)]
 
 
 @pytest.mark.parametrize("I,clamp", [(128, 0.0), (256, 6.0), (384, 0.0)])
@@ -720,12 +746,16 @@ def test_gemm1_act_quant_fused_equals_two_calls(ops, I, clamp):
     xs = np.ascontiguousarray(F.pack_ue8m0_words(xsb).T)
     w13 = rng.integers(0, 256, size=(len(counts), 2 * I, H // 2), dtype=np.uint8)
     s13 = rng.integers(118, 128, size=(len(counts), 2 * I, H // 32), dtype=np.uint8)
-    (hq0, hs0), (hq1, hs1) = _fused_vs_two_call(ops, xq, xs, ends, A, w13, s13, clamp)
+    (hq0, hs0), (hq1, hs1), gu = _fused_vs_two_call(ops, xq, xs, ends, A, w13, s13, clamp)
     assert np.array_equal(hq0, hq1) and np.array_equal(hs0, hs1)
     live = np.zeros(M_cap, bool)
     for rows in _expert_rows(ends, A):
         live[rows] = True
     assert np.all(hq1[~live] == BYTE_SENT) and np.all(hs1[:, ~live] == WORD_SENT)
+    # the two-call path's act-quant against the oracle's, on the GPU's gateup
+    rows = np.flatnonzero(live)
+    q, b = M.act_quant_rows(gu[rows], I, clamp)
+    assert np.array_equal(hq0[rows], q) and np.array_equal(hs0[:, rows].T, F.pack_ue8m0_words(b))
 
 
 def test_prefill_fused_chain_equals_unfused_full_size(ops):
