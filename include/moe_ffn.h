@@ -47,7 +47,9 @@
  *   effects. MOE_ERR_LAUNCH reports a failed kernel launch. There is no
  *   silent fallback path. Zero-sized work (T == 0, E_local == 0) returns
  *   MOE_OK without enqueuing anything.
- * - The library holds no state and is thread-safe.
+ * - The library holds no state and is thread-safe, with one exception:
+ *   moe_scatter_endpoints_noalloc keeps a fixed device array (its scratch)
+ *   on every GPU it runs on, for the life of the process.
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 enum moe_status {
     MOE_OK = 0,
@@ -69,7 +71,9 @@ enum moe_status {
     MOE_ERR_CAPACITY = -4,      /* M_cap cannot hold the worst-case grouped layout */
     MOE_ERR_UNSUPPORTED = -5,   /* an enum or parameter value this build does not support */
     MOE_ERR_LAUNCH = -6,        /* a kernel launch failed (hipGetLastError) */
-    MOE_ERR_WORKSPACE = -7      /* workspace missing or smaller than moe_scatter_workspace_bytes() */
+    MOE_ERR_WORKSPACE = -7,     /* workspace missing or smaller than moe_scatter_workspace_bytes() */
+    MOE_ERR_SCRATCH = -8,       /* the sizes need more than a no-alloc entry point's static scratch */
+    MOE_ERR_DEVICE = -9         /* the current device or its static scratch could not be queried */
 };
 
 enum moe_score_fn {
@@ -148,6 +152,30 @@ int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_star
                           int A, int M_cap, const uint16_t* x, int H,
                           int32_t* expert_ends, int32_t* route_row, uint8_t* xq, int32_t* xs,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_scatter_endpoints_noalloc - moe_scatter_endpoints without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, outputs, limits and errors as moe_scatter_endpoints
+ * (group-32 recipe), minus workspace / workspace_bytes. The per-(token block,
+ * expert) counters live in a static device array of 135,168 bytes instead
+ * (32,768 counters plus 1,024 expert starts, the most any call within the
+ * limits needs; sizes that would need more return MOE_ERR_SCRATCH before
+ * anything is enqueued). The array exists once per GPU, for the life of the
+ * process; its address on the current device is looked up on the first call
+ * on that device (MOE_ERR_DEVICE if that fails), so `stream` must belong to
+ * the current device. The call allocates nothing. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race on it and must be
+ * ordered by the caller. Contents left by an earlier call are never read:
+ * each call writes every counter before reading it.
+ * ------------------------------------------------------------------------ */
+int moe_scatter_endpoints_noalloc(const int32_t* topk_ids, int T, int k, int expert_start,
+                                  int E_local, int A, int M_cap, const uint16_t* x, int H,
+                                  int32_t* expert_ends, int32_t* route_row, uint8_t* xq,
+                                  int32_t* xs, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_pack_mx_weights - one-time, load-time relayout of MXFP4 expert weights

@@ -10,7 +10,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 c_int, c_i64, c_size, c_float, c_void = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
                                          ctypes.c_float, ctypes.c_void_p)
@@ -24,6 +24,9 @@ SIGNATURES = {
     "moe_scatter_endpoints": (c_int, [c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_void,
                                       c_int, c_void, c_void, c_void, c_void, c_void, c_size,
                                       c_void]),
+    "moe_scatter_endpoints_noalloc": (c_int, [c_void, c_int, c_int, c_int, c_int, c_int, c_int,
+                                              c_void, c_int, c_void, c_void, c_void, c_void,
+                                              c_void]),
     "moe_pack_mx_weights": (c_int, [c_void, c_void, c_int, c_int, c_int, c_void, c_void, c_void]),
     "moe_pack_mx_weights_gateup": (c_int, [c_void, c_void, c_int, c_int, c_int, c_void, c_void, c_void]),
     "moe_grouped_gemm1_act_quant": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,

@@ -13,6 +13,8 @@ extern "C" const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported enum or parameter value";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_SCRATCH: return "the sizes need more than the entry point's static scratch";
+    case MOE_ERR_DEVICE: return "the current device or its static scratch could not be queried";
     default: return "unknown status";
   }
 }

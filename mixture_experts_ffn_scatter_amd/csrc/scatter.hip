@@ -29,6 +29,8 @@
 // rows kernel reads them instead of scanning.
 #include "common.h"
 
+#include <mutex>
+
 namespace moe {
 
 constexpr int kTokBlock = 64;       // smallest token block
@@ -398,10 +400,10 @@ extern "C" size_t moe_scatter_workspace_bytes(int T, int k, int E_local) {
 }
 
 namespace moe {
-static int scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_start, int E_local,
-                             int A, int M_cap, const uint16_t* x, int H, int32_t* expert_ends,
-                             int32_t* route_row, uint8_t* xq, int32_t* xs, void* workspace,
-                             size_t workspace_bytes, void* stream, bool g128) {
+// Host-side checks of the scatter's sizes and pointers (no side effects).
+static int scatter_validate(const int32_t* topk_ids, int T, int k, int E_local, int A, int M_cap,
+                            const uint16_t* x, int H, int32_t* expert_ends, int32_t* route_row,
+                            uint8_t* xq, int32_t* xs) {
   if (T < 0 || k < 1 || k > kScatterMaxK || E_local < 0 || E_local > kScatterMaxE || A < 1 ||
       M_cap < 0 || H <= 0 || (long long)T * k > INT_MAX)
     return MOE_ERR_SHAPE;
@@ -409,11 +411,22 @@ static int scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_s
   if ((long long)M_cap < (long long)T * k + (long long)E_local * A) return MOE_ERR_CAPACITY;
   if (E_local == 0 && T == 0) return MOE_OK;
   if (!expert_ends && E_local > 0) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_ids || !x || !route_row || !xq || !xs)) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+static int scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_start, int E_local,
+                             int A, int M_cap, const uint16_t* x, int H, int32_t* expert_ends,
+                             int32_t* route_row, uint8_t* xq, int32_t* xs, void* workspace,
+                             size_t workspace_bytes, void* stream, bool g128) {
+  const int bad = scatter_validate(topk_ids, T, k, E_local, A, M_cap, x, H, expert_ends, route_row,
+                                   xq, xs);
+  if (bad != MOE_OK) return bad;
+  if (E_local == 0 && T == 0) return MOE_OK;
   if (T == 0) {
     // no routes: every expert is empty, ends are all zero
     return fill_i32(expert_ends, E_local, 0, (hipStream_t)stream);
   }
-  if (!topk_ids || !x || !route_row || !xq || !xs) return MOE_ERR_NULL;
   if (E_local == 0) return fill_i32(route_row, T * k, -1, (hipStream_t)stream);
   const size_t need = moe_scatter_workspace_bytes(T, k, E_local);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
@@ -454,6 +467,57 @@ extern "C" int moe_scatter_endpoints(const int32_t* topk_ids, int T, int k, int 
                                      void* stream) {
   return moe::scatter_endpoints(topk_ids, T, k, expert_start, E_local, A, M_cap, x, H, expert_ends,
                                 route_row, xq, xs, workspace, workspace_bytes, stream, false);
+}
+
+namespace moe {
+// Device scratch of moe_scatter_endpoints_noalloc, in place of the caller's
+// workspace. The largest workspace a valid call needs is the counter table
+// (at most kCountLds (token block, expert) entries: scatter_token_block grows
+// the block until they fit) plus one start per expert.
+constexpr size_t kScatterScratchBytes = (size_t)(kCountLds + kScatterMaxE) * sizeof(int32_t);
+static __device__ __align__(256) uint8_t scratch[kScatterScratchBytes];
+
+// The array's address on each device, looked up once per device (each GPU
+// holds its own copy at its own address). Host code uses these addresses,
+// never the symbol itself.
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" int moe_scatter_endpoints_noalloc(const int32_t* topk_ids, int T, int k,
+                                             int expert_start, int E_local, int A, int M_cap,
+                                             const uint16_t* x, int H, int32_t* expert_ends,
+                                             int32_t* route_row, uint8_t* xq, int32_t* xs,
+                                             void* stream) {
+  // the argument checks, then the scratch size, before anything else
+  const int bad = moe::scatter_validate(topk_ids, T, k, E_local, A, M_cap, x, H, expert_ends,
+                                        route_row, xq, xs);
+  if (bad != MOE_OK) return bad;
+  if (T > 0 && E_local > 0 && moe_scatter_workspace_bytes(T, k, E_local) > moe::kScatterScratchBytes)
+    return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (T > 0 && E_local > 0) {
+    const int st = moe::scratch_on_current_device(&ws);
+    if (st != MOE_OK) return st;
+  }
+  // the counters and offsets in the scratch are written in full before they
+  // are read, so nothing carried over from an earlier call is ever used
+  return moe::scatter_endpoints(topk_ids, T, k, expert_start, E_local, A, M_cap, x, H, expert_ends,
+                                route_row, xq, xs, ws, moe::kScatterScratchBytes, stream, false);
 }
 
 extern "C" int moe_scatter_endpoints_g128(const int32_t* topk_ids, int T, int k, int expert_start,

@@ -152,6 +152,26 @@ def moe_scatter_endpoints(topk_ids, expert_start: int, E_local: int, A: int, x,
     check(st, "moe_scatter_endpoints" + ("" if group == 32 else "_g128"))
 
 
+def moe_scatter_endpoints_noalloc(topk_ids, expert_start: int, E_local: int, A: int, x,
+                                  expert_ends, route_row, xq, xs):
+    """moe_scatter_endpoints (group-32 recipe) with the library's static
+    per-GPU scratch in place of a workspace: allocates nothing."""
+    _req(topk_ids, "topk_ids", (torch.int32,))
+    T, k = topk_ids.shape
+    _req(x, "x", _BF16)
+    H = x.shape[1]
+    M_cap = xq.shape[0]
+    _req(x, "x", _BF16, (T, H))
+    _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
+    _req(route_row, "route_row", (torch.int32,), (T * k,))
+    _req(xq, "xq", (torch.uint8,), (M_cap, H))
+    _req(xs, "xs", (torch.int32,), (scale_words(H), M_cap))
+    st = lib().moe_scatter_endpoints_noalloc(_ptr(topk_ids), T, k, expert_start, E_local, A, M_cap,
+                                             _ptr(x), H, _ptr(expert_ends), _ptr(route_row),
+                                             _ptr(xq), _ptr(xs), _stream())
+    check(st, "moe_scatter_endpoints_noalloc")
+
+
 # ------------------------------------------------------------------ GEMMs
 
 def packed_scale_shape(E: int, N: int, K: int):

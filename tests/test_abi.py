@@ -44,8 +44,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 8
-    for s in range(0, -8, -1):
+    assert lib.moe_abi_version() == 9
+    for s in range(0, -10, -1):
         assert lib.moe_status_string(s).decode()
     assert lib.moe_status_string(5).decode() == "unknown status"
 
@@ -77,6 +77,17 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
     assert lib.moe_scatter_endpoints(*args) == -4
     args[6] = 1152
     assert lib.moe_scatter_endpoints(*args) == -1                                 # NULL pointers
+    # the no-alloc form: the same checks, in the same order, before any
+    # device query (there is no workspace argument)
+    na = args[:14] + [NULL]
+    na[8], na[6] = 200, 1152
+    assert lib.moe_scatter_endpoints_noalloc(*na) == -3
+    na[8], na[6] = 256, 1024
+    assert lib.moe_scatter_endpoints_noalloc(*na) == -4
+    na[6] = 1152
+    assert lib.moe_scatter_endpoints_noalloc(*na) == -1
+    assert lib.moe_scatter_endpoints_noalloc(NULL, 64, 2, 0, 1025, 128, 1 << 20, NULL, 256, NULL,
+                                             NULL, NULL, NULL, NULL) == -2        # E_local > 1024
     # act-quant: clamp limit that is not a bf16 value
     assert lib.moe_act_quant_liverows(NULL, NULL, 8, 128, 1152, 128, ctypes.c_float(7.3),
                                       NULL, NULL, NULL) == -5
