@@ -6,20 +6,26 @@ tokens per GPU -- one GPU's share of an EP8 DeepSeek-V4-style layer
 combine for the 8x512-token group's routes to this GPU's 32 experts).
 Inputs are seeded synthetic data already resident in HBM when the timed
 region starts. A step is one pass of route -> scatter -> GEMM1 -> act-quant
--> GEMM2 -> combine. The headline times the six launches captured once into
-a HIP graph and replayed; an eager loop with HIP events around every launch
-gives the per-kernel durations (and its own ms/step, eager_ms_per_step).
+-> GEMM2 -> combine. The headline is cold: the six launches are captured
+once into a HIP graph, and each of the K timed replays follows a 512 MB read
+that evicts the L2s and the Infinity Cache (HIP events bracket the replay
+alone; the median is reported, the warm back-to-back rate beside it). Eager
+steps, each after the same read, give the per-kernel durations from HIP
+events around every launch.
 
 The same line carries:
-  roofline      the dominant kernel (GEMM1) against HBM peak, with its
-                duration measured by HIP events around it in the timed loop
+  roofline      the dominant kernel (GEMM1 with the fused act-quant) against
+                HBM peak: duration by HIP events, and by the committed kernel
+                trace while the kernel's sources match it
   kernels       per-kernel durations, algorithmic bytes / FLOP, GB/s, TFLOP/s
   layers        the same chain on the tiny and the large-expert-count layers
   actquant      the standalone live-row act-quant benchmark (3,072 live of
                 28,672 rows, width 2,048; SiLU and SiTU) and its full-buffer
                 control, cold
-  decode        the sparse decode path at 1 and 8 tokens (FP8 and MXFP4)
-  cpu_baseline  the CPU oracle timed on the host on the same layer
+  decode        the sparse decode layer at 1 and 8 tokens (FP8 and MXFP4):
+                per-kernel cold durations and the graph-replayed layer
+  cpu_baseline  the CPU oracle on the host: the headline layer on all threads
+                (the value) and, per workload, on one thread and on all
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
                        [--no-cpu-baseline] [--copy-calibration]
@@ -47,6 +53,7 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix peak
 # committed rocprofv3 summary; it is reported only while the kernel's sources
 # still hash to the value recorded when the counters were read.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_mx_gemm1_act_quant_prefill_ep_share_hbm_traffic.txt")
+TRACE_FILE = os.path.join(ROOT, "profiles", "prefill_ep_share_layer_kernel_trace.txt")
 GEMM_SOURCES = ("mixture_experts_ffn_scatter_amd/csrc/gemm.hip",
                 "mixture_experts_ffn_scatter_amd/csrc/common.h",
                 "mixture_experts_ffn_scatter_amd/csrc/sigmoid_lookup.h")
@@ -70,6 +77,22 @@ def counter_traffic():
                     rec = json.loads(line[len("TRAFFIC "):])
                     if rec.get("source_sha256") == gemm_source_hash():
                         return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+    except OSError:
+        pass
+    return None
+
+
+def trace_avg_launch_us():
+    """GEMM1's mean duration per launch from the committed rocprofv3 kernel
+    trace of the headline command (its eager-cold window), or None when the
+    kernel's sources changed since that trace was taken."""
+    try:
+        with open(TRACE_FILE) as fh:
+            for line in fh:
+                if line.startswith("TRACE "):
+                    rec = json.loads(line[len("TRACE "):])
+                    if rec.get("source_sha256") == gemm_source_hash():
+                        return float(rec["avg_launch_us"])
     except OSError:
         pass
     return None
@@ -196,19 +219,28 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # eager, warm: K steps back to back, host-timed
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    eager_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-kernel durations, cold: K eager steps, each after a 512 MB read that
+    # evicts the L2s and the 256 MB Infinity Cache. The read also keeps the
+    # GPU behind the host, so every launch is queued before its start event
+    # is reached and no window holds a host-side launch gap.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
+        _flush_caches(torch, scratch)
         step(events[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
     dur_us = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in
                                 range(args.steps)])) * 1e3 for j, n in enumerate(names)}
-    log(f"eager ms/step {ms_per_step:.4f}", {k: round(v, 2) for k, v in dur_us.items()})
-    eager_ms_per_step = ms_per_step
+    log(f"eager ms/step {eager_ms_per_step:.4f}; per kernel, cold",
+        {k: round(v, 2) for k, v in dur_us.items()})
 
     # the headline: the same six launches captured once into a HIP graph and
     # replayed (the chain never reads a count back, so the graph is valid for
@@ -217,13 +249,32 @@ def main():
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
+    # warm: K replays back to back (weights partly left in the caches by the
+    # previous replay)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    log(f"graph ms/step {ms_per_step:.4f}")
+    warm_ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # cold (the headline): before each of the K timed replays a 512 MB read
+    # evicts the L2s and the 256 MB Infinity Cache, outside the HIP events
+    # that bracket the replay, so every input comes from HBM
+    cold = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        _flush_caches(torch, scratch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    torch.cuda.synchronize()
+    del scratch
+    ms_per_step = float(np.median(cold))
+    log(f"graph ms/step cold {ms_per_step:.4f} (p10 {np.percentile(cold, 10):.4f}, p90 "
+        f"{np.percentile(cold, 90):.4f}), warm {warm_ms_per_step:.4f}")
     del graph
 
     # algorithmic work per launch, from the routed counts of this input
@@ -262,6 +313,12 @@ def main():
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
                 "alg_bytes_per_launch": int(bytes_[dom]), "avg_launch_us": round(dur_us[dom], 3)}
+    tr = trace_avg_launch_us() if fused else None
+    if tr is not None:
+        # the same launches by the committed kernel trace (no event packets
+        # or dispatch in the window)
+        roofline["avg_launch_us_trace"] = tr
+        roofline["frac_trace"] = round(bytes_[dom] / (tr * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
 
     result = {
         "metric": "MoE FFN us/layer @512 tok; live-row act-quant GB/s; % of HBM/MFMA roofline",
@@ -269,6 +326,11 @@ def main():
         "unit": "us/layer",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "timing": "cold: median of K graph replays, each after a 512 MB read that evicts the "
+                  "caches (HIP events around the replay only)",
+        "warm_ms_per_step": round(warm_ms_per_step, 5),
+        "cold_ms_p10_p90": [round(float(np.percentile(cold, 10)), 5),
+                            round(float(np.percentile(cold, 90)), 5)],
         "eager_ms_per_step": round(eager_ms_per_step, 5),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8e4m3 x mxfp4 (fp32 accum), bf16 io",
@@ -502,6 +564,11 @@ def bench_actquant(ops, torch, up, up_bf16, log, iters=20):
 
 
 def bench_decode(ops, torch, up, up_bf16, log, iters=20):
+    """The sparse decode layer (32 resident experts, H = 2,880, top-4) at 1
+    and 8 tokens, FP8 and MXFP4: per-kernel HIP-event durations of an eager
+    cold call (gate_up GEMV with the GLU, down GEMV, combine), and the three
+    launches captured into a HIP graph, replayed cold (after a cache-evicting
+    read) and warm."""
     import workloads as W
     out = {}
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -519,37 +586,67 @@ def bench_decode(ops, torch, up, up_bf16, log, iters=20):
             logits = up(rng.standard_normal((T, base.E), dtype=np.float32))
             ids, wts = ops.moe_route(logits, base.k, "softmax")
             dbuf = ops.alloc_decode(T, base.k, base.H)
+
+            def chain(ev=None):
+                def mark(i):
+                    if ev is not None:
+                        ev[i].record()
+                mark(0)
+                ops.moe_sparse_gemv(x, False, ids, 0, base.E, wfmt, dw[0], dw[1], dw[2], dbuf.act,
+                                    dbuf.slot_row, glu=True)
+                mark(1)
+                ops.moe_sparse_gemv(dbuf.act, True, ids, 0, base.E, wfmt, dw[3], dw[4], dw[5],
+                                    dbuf.down, None, glu=False)
+                mark(2)
+                ops.moe_combine(dbuf.down, dbuf.slot_row, wts, 1.0, dbuf.out)
+                mark(3)
+
             for _ in range(3):
-                ops.moe_ffn_decode(x, ids, wts, 0, base.E, wfmt, *dw, dbuf)
-            ts, tg = [], []
+                chain()
+            per = [[], [], []]
             for i in range(iters):
                 _flush_caches(torch, scratch)
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-                ev[0].record()
-                ops.moe_sparse_gemv(x, False, ids, 0, base.E, wfmt, dw[0], dw[1], dw[2], dbuf.act,
-                                    dbuf.slot_row, glu=True)
-                ev[1].record()
-                ops.moe_sparse_gemv(dbuf.act, True, ids, 0, base.E, wfmt, dw[3], dw[4], dw[5],
-                                    dbuf.down, None, glu=False)
-                ev[2].record()
-                ops.moe_combine(dbuf.down, dbuf.slot_row, wts, 1.0, dbuf.out)
-                ev[3].record()
+                chain(ev)
                 torch.cuda.synchronize()
-                ts.append(ev[0].elapsed_time(ev[3]) * 1e3)
-                tg.append(ev[0].elapsed_time(ev[2]) * 1e3)
+                for j in range(3):
+                    per[j].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+            graph = ops.capture_graph(lambda: chain(None))
+            for _ in range(3):
+                graph.replay()
+            cold, warm = [], []
+            for i in range(iters):
+                _flush_caches(torch, scratch)
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record()
+                graph.replay()
+                e1.record()
+                graph.replay()
+                e2.record()
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1) * 1e3)
+                warm.append(e1.elapsed_time(e2) * 1e3)
+            del graph
             U = int(np.unique(ids.cpu().numpy()).size)
             H, N = base.H, base.N_gu
             if wfmt == "fp8":
-                per_expert = N * H + H * H + 4 * 2
+                bpe_gu, bpe_d = N * H + 4, H * H + 4
             else:
-                per_expert = N * H // 2 + N * H // 32 + H * H // 2 + H * H // 32
-            B = U * (per_expert + (N + H) * 2) + T * base.k * H * 2 * 2 + T * H * 2
-            tgm = float(np.median(tg))
+                bpe_gu, bpe_d = N * H // 2 + N * H // 32, H * H // 2 + H * H // 32
+            B_gu = U * (bpe_gu + N * 2) + T * H * 2 + T * base.k * H * 2
+            B_d = U * (bpe_d + H * 2) + 2 * T * base.k * H * 2
+            d_gu, d_d, d_c = (float(np.median(v)) for v in per)
             key = f"{wfmt}_T{T}"
-            out[key] = {"us_layer_cold_median": round(float(np.median(ts)), 3),
-                        "us_gemvs_cold_median": round(tgm, 3), "distinct_experts": U,
-                        "alg_bytes": int(B), "GBps": round(B / (tgm * 1e-6) / 1e9, 1),
-                        "hbm_frac": round(B / (tgm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            out[key] = {"distinct_experts": U,
+                        "gate_up_us_cold": round(d_gu, 3), "down_us_cold": round(d_d, 3),
+                        "combine_us_cold": round(d_c, 3),
+                        "gate_up_hbm_frac": round(B_gu / (d_gu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "down_hbm_frac": round(B_d / (d_d * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "gemvs_alg_bytes": int(B_gu + B_d),
+                        "gemvs_hbm_frac": round((B_gu + B_d) / ((d_gu + d_d) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "kernel_sum_us": round(d_gu + d_d + d_c, 3),
+                        "layer_graph_us_cold": round(float(np.median(cold)), 3),
+                        "layer_graph_us_warm": round(float(np.median(warm)), 3)}
             log("decode", key, out[key])
         del dw, base
         torch.cuda.empty_cache()
@@ -558,23 +655,117 @@ def bench_decode(ops, torch, up, up_bf16, log, iters=20):
     return out
 
 
+def _host_cpu():
+    """The host CPU's model name and the threads this process may use (the
+    scheduler affinity, capped by OMP_NUM_THREADS when that is set)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return model, max(n, 1)
+
+
 def cpu_baseline(c, log):
-    """The CPU oracle as it stands, on this GPU's whole layer (4096-token
-    group, 32 local experts), once, on the host cores."""
+    """The CPU oracle as it stands, timed on the host cores.
+
+    The headline value is this GPU's whole EP-share layer (route of the 512
+    own tokens, then the 4,096-token group's scatter, both MX GEMMs in fp64,
+    act-quant and combine) on all the threads this process may use (the
+    oracle's per-expert thread pool, one BLAS thread per worker), once.
+    ``per_config`` adds, for every workload, the oracle on one thread and on
+    all of them; where the oracle has no parallel loop (act-quant, the decode
+    chain) one run is reported with threads = 1. Multi-threaded results are
+    checked equal to the single-threaded ones."""
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
     from oracle import moe as M
-    threads = os.cpu_count()
-    log(f"cpu baseline: oracle on the full layer ({threads} host threads)")
-    t0 = time.perf_counter()
-    ids, wts = M.route_softmax(c.logits[: c.own_tokens], c.k)
-    gids, gw = M.route_softmax(c.logits, c.k)
-    w = c.weights
-    M.prefill_expert_major(c.x, gids, gw, 0, c.E_local, c.A, c.I, w.w13, w.s13, w.w2, w.s2)
-    dt = time.perf_counter() - t0
-    log(f"cpu baseline {dt:.1f} s")
-    return {"value": round(dt * 1e6, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
-            "sample": "the whole layer once: route of 512 own tokens + the 4096-token group's "
-                      "scatter, both MX GEMMs (fp64), act-quant and combine; numpy with its BLAS "
-                      "thread pool"}
+    model, threads = _host_cpu()
+    log(f"cpu baseline: {model}, {threads} threads")
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return (time.perf_counter() - t0) * 1e6, r
+
+    def layer(case, workers, ids=None, wts=None):
+        w = case.weights
+        def run():
+            if ids is not None:
+                gi, gw = ids, wts
+            elif case.score == "softmax":
+                own = M.route_softmax(case.logits[: case.own_tokens], case.k)
+                gi, gw = (own if case.own_tokens == case.T else M.route_softmax(case.logits, case.k))
+            else:
+                gi, gw = M.route_sigmoid_bias(case.logits, case.bias, case.k)
+            return M.prefill_expert_major(case.x, gi, gw, case.expert_start, case.E_local, case.A,
+                                          case.I, w.w13, w.s13, w.w2, w.s2, clamp=case.clamp,
+                                          routed_scale=case.routed_scale, workers=workers)
+        with threadpool_limits(1):
+            return timed(run)
+
+    per = {}
+    # prefill EP share: all threads (the headline) and one thread
+    us_all, r_all = layer(c, threads)
+    us_one, r_one = layer(c, 1)
+    same = bool(np.array_equal(r_all.out, r_one.out) and np.array_equal(r_all.hq, r_one.hq))
+    per["prefill_ep_share"] = {"us_all_threads": round(us_all, 1), "us_one_thread": round(us_one, 1),
+                               "threads": threads, "same_result": same}
+    log("cpu prefill_ep_share", per["prefill_ep_share"])
+    # tiny layer (64 tokens, 8 experts)
+    t = W.tiny()
+    a_us, ra = layer(t, threads)
+    o_us, ro = layer(t, 1)
+    per["tiny"] = {"us_all_threads": round(a_us, 1), "us_one_thread": round(o_us, 1),
+                   "threads": threads, "same_result": bool(np.array_equal(ra.out, ro.out))}
+    # standalone act-quant, the 3,072 live rows of width 2 x 2,048 (SiLU)
+    aq = W.actquant()
+    with threadpool_limits(1):
+        us, _ = timed(lambda: M.act_quant_rows(aq.live, aq.I))
+    per["actquant_live_rows"] = {"us_one_thread": round(us, 1), "threads": 1,
+                                 "rows": int(aq.live.shape[0])}
+    # sparse decode layer, 32 experts, H = 2,880, top-4
+    for wfmt in ("fp8", "mxfp4"):
+        for T in (1, 8):
+            d = W.decode(T=T, wfmt=wfmt)
+            with threadpool_limits(1):
+                us, _ = timed(lambda: M.decode_chain(d))
+            per[f"decode_{wfmt}_T{T}"] = {"us_one_thread": round(us, 1), "threads": 1}
+            del d
+    log("cpu small configs", {k: v for k, v in per.items() if k != "prefill_ep_share"})
+    # large-expert-count layer (2,048 tokens, 896 experts, top-16): the routes
+    # to the first 28 experts (with their weights only), routed outside the
+    # timing, on all threads and on one; the whole layer is estimated as 32
+    # such slices
+    big = W.large(experts_with_weights=28)
+    ids_l, wts_l = M.route_sigmoid_bias(big.logits, big.bias, big.k)
+    keep = ids_l < 28
+    ids_s = np.where(keep, ids_l, -1).astype(ids_l.dtype)
+    big.E_local = 28
+    a_us, ra = layer(big, threads, ids_s, wts_l)
+    o_us, ro = layer(big, 1, ids_s, wts_l)
+    per["large_e_slice28"] = {"us_all_threads": round(a_us, 1), "us_one_thread": round(o_us, 1),
+                              "threads": threads, "routes": int(keep.sum()),
+                              "same_result": bool(np.array_equal(ra.out, ro.out)),
+                              "layer_estimate_us_one_thread": round(o_us * 32, 1),
+                              "layer_estimate_us_all_threads": round(a_us * 32, 1)}
+    log("cpu large_e slice", per["large_e_slice28"])
+    del big
+    return {"value": round(us_all, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "cpu_model": model,
+            "sample": "the prefill EP-share layer once: route of 512 own tokens, then the "
+                      "4096-token group's scatter, both MX GEMMs (fp64), act-quant and combine; "
+                      "per-expert thread pool with one BLAS thread per worker",
+            "per_config": per}
 
 
 if __name__ == "__main__":
