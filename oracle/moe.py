@@ -21,7 +21,12 @@ Parity pins (see ``tests/test_oracle_*.py``):
   activation's special cases and an fp64 evaluation of the formula.
 * ``mx_gemm`` - an independent pure-Python nibble/byte triple loop, one-hot
   rows and scale doubling.
-* ``combine`` - identity and skip cases; the token-major chain.
+* ``combine`` - identity and skip cases, slot order and rounding order;
+  the token-major chain.
+* ``scatter_masked`` / ``scales_slab`` / ``prefill_masked`` - a worked
+  example by hand (golden fixture), agreement with the aligned layout's
+  rows expert by expert, overflow keeps the earliest routes, and the
+  per-expert MN-major word layout against an element loop.
 * ``gemv`` / ``glu`` - a dense per-expert evaluation and special cases.
   ``glu`` follows a reading of the pages (the GPT-OSS gated-SiLU form with
   alpha, beta, limit), so its formula itself is parity unpinned beyond the
@@ -415,23 +420,14 @@ class PrefillResult:
     out: np.ndarray         # bf16 [T, H]
 
 
-def prefill_expert_major(x_bits, ids, weights, expert_start, E_local, A, I,
-                         w13, s13, w2, s2, clamp=0.0, routed_scale=1.0,
-                         check_exact=True, workers: int = 1) -> PrefillResult:
-    """The six-step chain in expert-major order ("Blackwell DeepGEMM
-    FusedMoE (sglang)", section 1.1 stages 2-6; "Blackwell FP4 MoE: live-row
-    boundary", section 2: scatter -> FC1(endpoint) -> SiLU+mul+quant(endpoint)
-    -> FC2(endpoint)): scatter, quantise x per route row, GEMM1 per expert,
-    act-quant, GEMM2 per expert, combine by route row.
-
-    Experts touch disjoint rows, so ``workers`` > 1 runs the per-expert
-    steps on a thread pool; the results are the same arrays."""
-    T, k = np.asarray(ids).shape
+def _expert_major_rows(x_bits, tok, le, E_local, I, w13, s13, w2, s2, clamp, check_exact,
+                       workers):
+    """The per-row steps of the chain for the placed routes, expert by
+    expert: quantise the routed token row, GEMM1, act-quant, GEMM2. ``tok``
+    and ``le`` give each placed route's token and local expert, in ascending
+    route order (which is ascending row order inside every expert)."""
+    n = tok.shape[0]
     H = x_bits.shape[1]
-    sc = scatter_routes(ids, expert_start, E_local, A)
-    lr, le = sc.local_routes, sc.local_expert
-    n = lr.shape[0]
-    tok = lr // k
     xq, xb = quant_rows(x_bits[tok]) if n else (np.zeros((0, H), np.uint8),
                                                 np.zeros((0, H // GROUP), np.uint8))
     gateup = np.zeros((n, 2 * I), np.uint16)
@@ -457,11 +453,121 @@ def prefill_expert_major(x_bits, ids, weights, expert_start, E_local, A, I,
     else:
         for e in range(E_local):
             one_expert(e)
+    return xq, xb, gateup, gex, gts, hq, hb, down, dex, dts
+
+
+def prefill_expert_major(x_bits, ids, weights, expert_start, E_local, A, I,
+                         w13, s13, w2, s2, clamp=0.0, routed_scale=1.0,
+                         check_exact=True, workers: int = 1) -> PrefillResult:
+    """The six-step chain in expert-major order ("Blackwell DeepGEMM
+    FusedMoE (sglang)", section 1.1 stages 2-6; "Blackwell FP4 MoE: live-row
+    boundary", section 2: scatter -> FC1(endpoint) -> SiLU+mul+quant(endpoint)
+    -> FC2(endpoint)): scatter, quantise x per route row, GEMM1 per expert,
+    act-quant, GEMM2 per expert, combine by route row.
+
+    Experts touch disjoint rows, so ``workers`` > 1 runs the per-expert
+    steps on a thread pool; the results are the same arrays."""
+    T, k = np.asarray(ids).shape
+    H = x_bits.shape[1]
+    sc = scatter_routes(ids, expert_start, E_local, A)
+    lr, le = sc.local_routes, sc.local_expert
+    xq, xb, gateup, gex, gts, hq, hb, down, dex, dts = _expert_major_rows(
+        x_bits, lr // k, le, E_local, I, w13, s13, w2, s2, clamp, check_exact, workers)
     # combine reads down rows by their layout row index
     rows = np.zeros((max(int(sc.end.max()) if E_local else 0, 1), H), np.float32)
     rows[sc.route_row[lr]] = bf16_to_f32(down)
     out = combine(rows, sc.route_row, np.asarray(weights, np.float32), routed_scale)
     return PrefillResult(sc, xq, xb, gateup, gex, gts, hq, hb, down, dex, dts, out)
+
+
+# ------------------------------------------------- masked (E, m_pad, K) slab
+
+@dataclass
+class MaskedScatter:
+    counts: np.ndarray        # int64 [E_local]: local routes per expert
+    masked_m: np.ndarray      # int32 [E_local]: rows present in expert e's slab
+    route_row: np.ndarray     # int32 [T*k]: e*m_pad + j, or -1 (not local, or not placed)
+    local_routes: np.ndarray  # placed routes t*k+s, ascending
+    local_expert: np.ndarray  # local expert of each of them
+
+
+def scatter_masked(ids: np.ndarray, expert_start: int, E_local: int, m_pad: int) -> MaskedScatter:
+    """The masked slab layout ("DeepGEMM FusedMoE on Blackwell (sglang)",
+    section 2.2.4, the standard masked pre-permute, and section 3.2, the
+    masked grouped GEMM's masked_m): local expert e owns the fixed block of
+    m_pad rows [e*m_pad, (e+1)*m_pad) of an [E_local, m_pad, K] buffer. Its
+    routes, in flattened route order t*k+s, take rows 0, 1, ... of its block,
+    and masked_m[e] is the number of rows taken; the rest of the block is
+    padding that no consumer reads.
+
+    The pages size m_pad so that no expert can overflow it (the rank's
+    token count rounded up, or the largest masked_m rounded up). Here a
+    route whose rank inside its expert reaches m_pad is not placed: its row
+    is -1 and masked_m[e] = min(count_e, m_pad)."""
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    e = ids - expert_start
+    local = (e >= 0) & (e < E_local)
+    counts = np.bincount(e[local], minlength=E_local).astype(np.int64)
+    route_row = np.full(ids.shape[0], -1, dtype=np.int32)
+    taken = np.zeros(E_local, dtype=np.int64)
+    for r in range(ids.shape[0]):
+        if local[r] and taken[e[r]] < m_pad:
+            route_row[r] = e[r] * m_pad + taken[e[r]]
+            taken[e[r]] += 1
+    placed = np.flatnonzero(route_row >= 0)
+    return MaskedScatter(counts, taken.astype(np.int32), route_row, placed, e[placed])
+
+
+def scales_slab(bytes_rows: np.ndarray, rows: np.ndarray, E_local: int, m_pad: int, fill=None):
+    """Packed UE8M0 words of slab rows, MN-major inside each expert: word c
+    of slab row j of expert e at [e][c][j] ("DeepGEMM FusedMoE on Blackwell
+    (sglang)", section 3.2: the masked GEMM's activation scales are
+    (E, m, G/4) int32 words in MN-major memory; section 2.4.2: the varlen
+    act-quant allocates (E, G/4, m) and transposes the view). ``rows`` are
+    slab row indices e*m_pad + j; rows not listed keep ``fill``."""
+    words = pack_ue8m0_words(bytes_rows)           # [R, G/4]
+    out = np.full((E_local, words.shape[1], m_pad), 0 if fill is None else fill, dtype=np.int32)
+    e, j = np.divmod(np.asarray(rows, dtype=np.int64), m_pad)
+    out[e, :, j] = words
+    return out
+
+
+@dataclass
+class MaskedResult:
+    scatter: MaskedScatter
+    xq: np.ndarray          # u8 [n_placed, H]  indexed like scatter.local_routes
+    xb: np.ndarray          # u8 [n_placed, H/32]
+    gateup: np.ndarray      # bf16 [n_placed, 2I]
+    gateup_exact: np.ndarray
+    gateup_tsum: np.ndarray
+    hq: np.ndarray          # u8 [n_placed, I]
+    hb: np.ndarray          # u8 [n_placed, I/32]
+    down: np.ndarray        # bf16 [n_placed, H]
+    down_exact: np.ndarray
+    down_tsum: np.ndarray
+    out: np.ndarray         # bf16 [T, H]
+
+
+def prefill_masked(x_bits, ids, weights, expert_start, E_local, m_pad, I, w13, s13, w2, s2,
+                   clamp=0.0, routed_scale=1.0, check_exact=True,
+                   workers: int = 1) -> MaskedResult:
+    """The chain on the masked slab layout ("DeepGEMM FusedMoE on Blackwell
+    (sglang)": section 2.2.4 masked pre-permute with quantisation, section
+    2.3.2 masked GEMM1 over the first masked_m[e] rows of each slab, section
+    2.4.2 varlen act-quant bounded by masked_m, section 2.5.2 masked GEMM2,
+    then the combine reading each route's row of the (E*m_pad, H) down
+    buffer). Per row the steps are those of the aligned layout; only where
+    the rows sit differs."""
+    T, k = np.asarray(ids).shape
+    H = x_bits.shape[1]
+    sc = scatter_masked(ids, expert_start, E_local, m_pad)
+    lr, le = sc.local_routes, sc.local_expert
+    xq, xb, gateup, gex, gts, hq, hb, down, dex, dts = _expert_major_rows(
+        x_bits, lr // k, le, E_local, I, w13, s13, w2, s2, clamp, check_exact, workers)
+    rows = np.zeros((max(E_local * m_pad, 1), H), np.float32)
+    rows[sc.route_row[lr]] = bf16_to_f32(down)
+    out = combine(rows, sc.route_row, np.asarray(weights, np.float32), routed_scale)
+    return MaskedResult(sc, xq, xb, gateup, gex, gts, hq, hb, down, dex, dts, out)
 
 
 def prefill_token_major(x_bits, ids, weights, expert_start, E_local, I, w13, s13, w2, s2,
