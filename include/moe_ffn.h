@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 
 enum moe_status {
     MOE_OK = 0,
@@ -285,7 +285,7 @@ int moe_grouped_gemm1(const uint8_t* xq, const int32_t* xs, const int32_t* exper
  *   hs           int32 [I/128][M_cap] out: packed UE8M0 scales, live rows only
  * Per element: s = sigmoid(g) rounded to fp32; h = fl32(fl32(g*s) * u); then
  * the per-32 quantisation of moe_scatter_endpoints on h.
- * Requires I % 128 == 0, M_cap % 4 == 0, E_local <= 1024, M_cap <= 524288,
+ * Requires I % 128 == 0, M_cap % 4 == 0, E_local <= 1024, M_cap <= 3,145,728,
  * M_cap * I * 4 < 2^31 (else MOE_ERR_SHAPE).
  * ------------------------------------------------------------------------ */
 int moe_act_quant_liverows(const uint16_t* gateup, const int32_t* expert_ends, int E_local,
@@ -367,6 +367,70 @@ int moe_grouped_gemm2_g128(const uint8_t* hq, const int32_t* hs, const int32_t* 
                            int E_local, int A, int M_cap, int I, int H,
                            const uint8_t* w2_packed, const uint8_t* w2_scale_packed,
                            uint16_t* down, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Masked slab layout: the five entry points below run the chain on an
+ * [E_local, m_pad, K] buffer in which every local expert owns a fixed block
+ * of m_pad rows, in place of the aligned layout.
+ * [SGL] section 2.2.4 (standard masked pre-permute: bucket the routes per
+ * expert into fixed slabs and quantise them in one step, producing masked_m,
+ * the real row count of each expert), section 2.3.2 and section 3.2 (masked
+ * grouped GEMM: lhs (E, m, K) fp8 with (E, m, G/4) int32 UE8M0 scales in
+ * MN-major memory, only the first masked_m[e] rows of expert e computed,
+ * out (E, m, N) bf16), section 2.4.2 (varlen act-quant bounded by masked_m)
+ * and section 2.5.2 (masked GEMM2 into (E, m, K)).
+ *
+ * Layout: expert e's rows are [e*m_pad, e*m_pad + masked_m[e]); the rest of
+ * its block is padding that no call reads or writes. A route's row inside
+ * its block is its rank among the expert's local routes in flattened route
+ * order t*k+s (as in the aligned layout). Scale words are MN-major per
+ * expert: word c of row j of expert e at scales[(e*W + c)*m_pad + j], with
+ * W = K/128 words per row (shape [E_local][K/128][m_pad] int32, bytes as in
+ * the aligned layout). m_pad must be a multiple of 4 and E_local*m_pad <
+ * 2^31; every other requirement is that of the aligned form.
+ *
+ * Capacity: the pages size m_pad so that no expert overflows (m_pad >= the
+ * token count T always suffices, since a token's k ids are distinct). A
+ * route whose rank inside its expert reaches m_pad is not placed: its
+ * route_row is -1 and masked_m[e] = min(count_e, m_pad), so the combine
+ * leaves it out. masked_m values are clamped into [0, m_pad] by every
+ * consumer. The pages' expected_m (a kernel-selection hint) has no
+ * counterpart: the GEMMs schedule from masked_m on the device.
+ *
+ * moe_scatter_masked: moe_scatter_endpoints into the slab (same quantisation,
+ *   same workspace: moe_scatter_workspace_bytes(T, k, E_local));
+ *   masked_m int32 [E_local] out; route_row int32 [T*k] out (e*m_pad + rank,
+ *   or -1); xq u8 [E_local*m_pad, H] out; xs int32 [E_local][H/128][m_pad] out.
+ *   m_pad >= 4 when E_local > 0.
+ * moe_grouped_gemm1_masked: moe_grouped_gemm1 on the slab; gateup bf16
+ *   [E_local*m_pad, 2I] out.
+ * moe_act_quant_masked: moe_act_quant_liverows (SiLU, optional clamp) on the
+ *   slab; hq u8 [E_local*m_pad, I] out; hs int32 [E_local][I/128][m_pad] out.
+ *   E_local*m_pad <= 3,145,728 as for moe_act_quant_liverows.
+ * moe_grouped_gemm1_act_quant_masked: moe_grouped_gemm1_act_quant on the
+ *   slab (hq, hs as moe_act_quant_masked writes them).
+ * moe_grouped_gemm2_masked: moe_grouped_gemm2 on the slab; down bf16
+ *   [E_local*m_pad, H] out. moe_combine then takes rows = down, n_rows =
+ *   E_local*m_pad and row_of_slot = route_row.
+ * Group-32 activation recipe only.
+ * ------------------------------------------------------------------------ */
+int moe_scatter_masked(const int32_t* topk_ids, int T, int k, int expert_start, int E_local,
+                       int m_pad, const uint16_t* x, int H, int32_t* masked_m,
+                       int32_t* route_row, uint8_t* xq, int32_t* xs, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int moe_grouped_gemm1_masked(const uint8_t* xq, const int32_t* xs, const int32_t* masked_m,
+                             int E_local, int m_pad, int H, int I, const uint8_t* w13_packed,
+                             const uint8_t* w13_scale_packed, uint16_t* gateup, void* stream);
+int moe_act_quant_masked(const uint16_t* gateup, const int32_t* masked_m, int E_local, int m_pad,
+                         int I, float clamp_limit, uint8_t* hq, int32_t* hs, void* stream);
+int moe_grouped_gemm1_act_quant_masked(const uint8_t* xq, const int32_t* xs,
+                                       const int32_t* masked_m, int E_local, int m_pad, int H,
+                                       int I, const uint8_t* w13_gateup_packed,
+                                       const uint8_t* w13_gateup_scale_packed, float clamp_limit,
+                                       uint8_t* hq, int32_t* hs, void* stream);
+int moe_grouped_gemm2_masked(const uint8_t* hq, const int32_t* hs, const int32_t* masked_m,
+                             int E_local, int m_pad, int I, int H, const uint8_t* w2_packed,
+                             const uint8_t* w2_scale_packed, uint16_t* down, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine - unpermute and weighted top-k sum.

@@ -95,10 +95,16 @@ __device__ int act_block_scan(int v, int* tmp) {
 // G128: one UE8M0 byte per 128 columns of h instead of per 32, packed four to
 // a word over 512 columns ([ceil(I/512)][M_cap] words; bytes of groups past I
 // are 0)
-template <bool CLAMP, bool SITU, bool G128>
+// SLAB: the masked slab layout ("DeepGEMM FusedMoE on Blackwell (sglang)",
+// section 2.4.2: the varlen act-quant over an (E, m_pad, 2I) slab): expert_ends
+// holds masked_m, expert e's live rows are [e slab, e slab + masked_m[e]),
+// M_cap = E_local * slab, and the scale words are MN-major per expert
+// ([e][word][row - e slab]).
+template <bool CLAMP, bool SITU, bool G128, bool SLAB>
 __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
     const uint16_t* __restrict__ gateup, const int32_t* __restrict__ expert_ends, int E_local,
-    int A, int M_cap, int I, float L, uint8_t* __restrict__ hq, int32_t* __restrict__ hs) {
+    int A, int M_cap, int slab, int I, float L, uint8_t* __restrict__ hq,
+    int32_t* __restrict__ hs) {
   __shared__ __attribute__((aligned(16))) float s_tab[MOE_SIGMOID_TABLE_SIZE];
   __shared__ __attribute__((aligned(16))) float s_t4[SITU ? MOE_TANH4_TABLE_SIZE : 4];
   __shared__ __attribute__((aligned(16))) float s_t25[SITU ? MOE_TANH25_TABLE_SIZE : 4];
@@ -151,11 +157,16 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int e = 2 * tid + j;
-    const int prev = e == 0 ? 0 : min(max(prevv[j], 0), M_cap);
-    const int s0 = min(align_up_dev(prev, A), M_cap);
-    const int en = min(max(endv[j], s0), M_cap);
-    st[j] = s0;
-    cnt[j] = e < E_local ? en - s0 : 0;
+    if constexpr (SLAB) {
+      st[j] = e * slab;
+      cnt[j] = e < E_local ? min(max(endv[j], 0), slab) : 0;
+    } else {
+      const int prev = e == 0 ? 0 : min(max(prevv[j], 0), M_cap);
+      const int s0 = min(align_up_dev(prev, A), M_cap);
+      const int en = min(max(endv[j], s0), M_cap);
+      st[j] = s0;
+      cnt[j] = e < E_local ? en - s0 : 0;
+    }
     sum += cnt[j];
   }
   int run = act_block_scan(sum, s_tmp);
@@ -289,10 +300,19 @@ __global__ __launch_bounds__(kActThreads, 1) void act_quant_kernel(
       }
       if (act) {
         *reinterpret_cast<uint2*>(hq + (size_t)row * I + col) = make_uint2(lo, hi);
+        // scale word w of the row: [w][row] over the whole buffer, or
+        // [e][w][row - e slab] inside expert e's slab
+        size_t hs0 = row;
+        int hss = M_cap;
+        if constexpr (SLAB) {
+          const int WN = G128 ? (I + 511) >> 9 : I >> 7;
+          hs0 = (size_t)(row / slab) * (size_t)(WN - 1) * (size_t)slab + row;
+          hss = slab;
+        }
         if constexpr (G128) {
-          if (lane == 0) hs[(size_t)ch * M_cap + row] = (int32_t)word;
+          if (lane == 0) hs[hs0 + (size_t)ch * hss] = (int32_t)word;
         } else {
-          if ((lane & 15) == 0) hs[(size_t)(col >> 7) * M_cap + row] = (int32_t)word;
+          if ((lane & 15) == 0) hs[hs0 + (size_t)(col >> 7) * hss] = (int32_t)word;
         }
       }
     }
@@ -348,9 +368,11 @@ int act_quant_check(const uint16_t* gateup, const int32_t* expert_ends, int E_lo
 }  // namespace
 
 namespace moe {
+// slab > 0: the masked slab layout (expert_ends = masked_m, M_cap = E_local
+// * slab; group 32 only)
 static int act_quant_silu(const uint16_t* gateup, const int32_t* expert_ends, int E_local, int A,
                           int M_cap, int I, float clamp_limit, uint8_t* hq, int32_t* hs,
-                          void* stream, bool g128) {
+                          void* stream, bool g128, int slab = 0) {
   bool clamp = false;
   if (clamp_limit > 0.f && clamp_limit < __builtin_inff()) {
     uint32_t bits;
@@ -364,10 +386,14 @@ static int act_quant_silu(const uint16_t* gateup, const int32_t* expert_ends, in
   if (rc <= 0) return rc;
   hipStream_t st = (hipStream_t)stream;
   const int grid = 256;         // one block per CU; each takes 1/256 of the live rows
-  auto kernel = clamp ? (g128 ? act_quant_kernel<true, false, true> : act_quant_kernel<true, false, false>)
-                     : (g128 ? act_quant_kernel<false, false, true> : act_quant_kernel<false, false, false>);
+  auto kernel = clamp ? (g128 ? act_quant_kernel<true, false, true, false>
+                             : act_quant_kernel<true, false, false, false>)
+                     : (g128 ? act_quant_kernel<false, false, true, false>
+                             : act_quant_kernel<false, false, false, false>);
+  if (slab > 0)
+    kernel = clamp ? act_quant_kernel<true, false, false, true> : act_quant_kernel<false, false, false, true>;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kActThreads), 0, st, gateup, expert_ends, E_local, A,
-                     M_cap, I, clamp ? clamp_limit : 0.f, hq, hs);
+                     M_cap, slab, I, clamp ? clamp_limit : 0.f, hq, hs);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -397,8 +423,18 @@ extern "C" int moe_act_quant_liverows_situ(const uint16_t* gateup, const int32_t
   if (situ_beta != 4.0f || situ_linear_beta != 25.0f) return MOE_ERR_UNSUPPORTED;
   const int rc = act_quant_check(gateup, expert_ends, E_local, A, M_cap, I, hq, hs);
   if (rc <= 0) return rc;
-  hipLaunchKernelGGL((act_quant_kernel<false, true, false>), dim3(256), dim3(kActThreads), 0,
-                     (hipStream_t)stream, gateup, expert_ends, E_local, A, M_cap, I, 0.f, hq, hs);
+  hipLaunchKernelGGL((act_quant_kernel<false, true, false, false>), dim3(256), dim3(kActThreads), 0,
+                     (hipStream_t)stream, gateup, expert_ends, E_local, A, M_cap, 0, I, 0.f, hq, hs);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+
+extern "C" int moe_act_quant_masked(const uint16_t* gateup, const int32_t* masked_m, int E_local,
+                                    int m_pad, int I, float clamp_limit, uint8_t* hq, int32_t* hs,
+                                    void* stream) {
+  if (E_local < 0 || m_pad < 0) return MOE_ERR_SHAPE;
+  if (m_pad % 4 != 0) return MOE_ERR_ALIGN;
+  if ((long long)E_local * m_pad >= (1LL << 31)) return MOE_ERR_SHAPE;
+  return moe::act_quant_silu(gateup, masked_m, E_local, 1, E_local * m_pad, I, clamp_limit, hq, hs,
+                             stream, false, m_pad);
 }

@@ -134,6 +134,21 @@ __device__ __forceinline__ void expert_range(const int32_t* __restrict__ ends, i
   end = en;
 }
 
+// Expert e's live rows in either layout. slab == 0: the aligned layout,
+// meta = expert_ends (expert_range above). slab = m_pad > 0: the masked slab
+// layout, meta = masked_m; expert e owns rows [e*m_pad, (e+1)*m_pad) and
+// its live rows are the first masked_m[e] of them (clamped into [0, m_pad]
+// so that a corrupt count cannot leave the slab).
+__device__ __forceinline__ void layout_range(const int32_t* __restrict__ meta, int e, int A,
+                                             int M_cap, int slab, int& start, int& end) {
+  if (slab > 0) {
+    start = e * slab;
+    end = start + min(max(meta[e], 0), slab);
+  } else {
+    expert_range(meta, e, A, M_cap, start, end);
+  }
+}
+
 }  // namespace moe
 
 // Host-side launch check shared by the entry points.

@@ -198,7 +198,7 @@ static_assert(kGemmBN == 256 && kGemmCB == 4, "the fused epilogue pairs 2 gate a
 template <bool ACT, bool XG128>
 __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gemm_kernel(
     const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
-    const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int K, int N,
+    const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int slab, int K, int N,
     const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out,
     GemmActOut act) {
   __shared__ GemmStage stage[kGemmStages];
@@ -218,6 +218,12 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   const int g = lane >> 4;
   const int KS = K / 128;                // k-steps
   const int NB = N / 16;                 // column blocks
+  // activation scale words per row, and the distance between a row's
+  // consecutive words: the whole buffer's rows (aligned layout) or one
+  // expert's slab (masked layout, where expert e's words start at
+  // e * XW * slab)
+  const int XW = XG128 ? (KS + 3) / 4 : KS;
+  const int ss = slab > 0 ? slab : M_cap;
   if constexpr (ACT) {
     // published by the barriers of the chunk scan below
     const float* tab = reinterpret_cast<const float*>(gemm_act::g_sigmoid_table);
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     pblk[j] = 0;
     if (e < E_local) {
       int st, en;
-      expert_range(expert_ends, e, A, M_cap, st, en);
+      layout_range(expert_ends, e, A, M_cap, slab, st, en);
       fcnt[j] = (en - st) / kGemmBM;
       pblk[j] = ((en - st) % kGemmBM + 15) >> 4;
     }
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
           (__builtin_amdgcn_readfirstlane(s_pre[e]) & 0xFFFF);        // e's full chunks
     }
     int start, end;
-    expert_range(expert_ends, e, A, M_cap, start, end);
+    layout_range(expert_ends, e, A, M_cap, slab, start, end);
     start = __builtin_amdgcn_readfirstlane(start);
     end = __builtin_amdgcn_readfirstlane(end);
     T.e = e;
@@ -357,7 +363,9 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     q.wr = make_rsrc(Wp + ((size_t)T.e * NB + T.cb0) * KS * 1024, (uint32_t)(T.ncb * KS) * 1024u);
     q.sr = make_rsrc(Sp + (size_t)T.e * KS * NB * 64, (uint32_t)(KS * NB) * 64u);
     q.xr = make_rsrc(X + (size_t)T.r0 * K, (uint32_t)T.rows * (uint32_t)K);
-    q.xsr = make_rsrc(Xs + T.r0, (uint32_t)(((XG128 ? (KS + 3) / 4 : KS) - 1) * M_cap + T.rows) * 4u);
+    // scale word w of row r: [w][r] (aligned layout), [e][w][r - e slab] (slab)
+    const size_t xs0 = (slab > 0 ? (size_t)T.e * (size_t)(XW - 1) * (size_t)slab : 0) + T.r0;
+    q.xsr = make_rsrc(Xs + xs0, (uint32_t)((XW - 1) * ss + T.rows) * 4u);
 #pragma unroll
     for (int c = 0; c < kDmaCB; ++c) {
       const int cb = kDmaCB * wid + c;
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
             base + (kDmaXR * wid + r) * 2048 + h * 1024);
     } else {
       if (wid < 2) {
-        dma4(q.xsr, q.xso + (uint32_t)((XG128 ? st >> 2 : st) * M_cap) * 4u, base + kOffXs + wid * 256);
+        dma4(q.xsr, q.xso + (uint32_t)((XG128 ? st >> 2 : st) * ss) * 4u, base + kOffXs + wid * 256);
       } else if (wid == 2) {
         // the tile's weight-scale line: 64 bytes per column block
         if (kGemmBN / 16 * 4 >= 64 || lane < kGemmBN / 16 * 4)
@@ -622,8 +630,10 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
             *reinterpret_cast<uint32_t*>(act.hq + row * act.I + 128 * nt + 32 * cg + 16 * c + 4 * g) = w;
           }
           // byte cg of the row's scale word of slice nt (group 4 nt + cg)
-          if (g == 0)
-            reinterpret_cast<uint8_t*>(act.hs)[((size_t)nt * M_cap + row) * 4 + cg] = (uint8_t)bsc;
+          if (g == 0) {
+            const size_t hs0 = slab > 0 ? (size_t)T.e * (size_t)(act.I / 128 - 1) * (size_t)slab : 0;
+            reinterpret_cast<uint8_t*>(act.hs)[(hs0 + (size_t)nt * ss + row) * 4 + cg] = (uint8_t)bsc;
+          }
         }
       }
     }
@@ -686,10 +696,13 @@ __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __re
       s[((size_t)e * N + 16 * src_cb(cb, half) + (l & 15)) * (size_t)(K / 32) + 4 * ks + (l >> 4)];
 }
 
+// slab == 0: the aligned layout (ends = expert_ends, M_cap rows); slab =
+// m_pad > 0: the masked slab layout (ends = masked_m, M_cap = E_local * m_pad)
 static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_t* ends,
                                int E_local, int A, int M_cap, int K, int N, const uint8_t* Wp,
                                const uint8_t* Sp, uint16_t* out, void* stream,
-                               const GemmActOut* act = nullptr, bool xg128 = false) {
+                               const GemmActOut* act = nullptr, bool xg128 = false,
+                               int slab = 0) {
   if (E_local < 0 || E_local > kGemmMaxE || A < 1 || M_cap < 0 || K <= 0 || N <= 0)
     return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
@@ -711,11 +724,12 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
   if (act) {
     if (xg128) return MOE_ERR_UNSUPPORTED;   // the fused epilogue quantises per 32 columns
     hipLaunchKernelGGL((grouped_mx_gemm_kernel<true, false>), dim3(grid), dim3(kGemmThreads), 0,
-                       (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, K, N, Wp, Sp, out, *act);
+                       (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out,
+                       *act);
   } else {
     auto kernel = xg128 ? grouped_mx_gemm_kernel<false, true> : grouped_mx_gemm_kernel<false, false>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kGemmThreads), 0, (hipStream_t)stream, X, Xs,
-                       ends, E_local, A, M_cap, K, N, Wp, Sp, out,
+                       ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out,
                        GemmActOut{nullptr, nullptr, 0, 0.f});
   }
   MOE_CHECK_LAUNCH();
@@ -791,17 +805,11 @@ extern "C" int moe_grouped_gemm2_g128(const uint8_t* hq, const int32_t* hs,
                                   w2_scale_packed, down, stream, nullptr, true);
 }
 
-extern "C" int moe_grouped_gemm1_act_quant(const uint8_t* xq, const int32_t* xs,
-                                           const int32_t* expert_ends, int E_local, int A,
-                                           int M_cap, int H, int I,
-                                           const uint8_t* w13_gateup_packed,
-                                           const uint8_t* w13_gateup_scale_packed,
-                                           float clamp_limit, uint8_t* hq, int32_t* hs,
-                                           void* stream) {
-  if (I <= 0 || I % 128 != 0) return MOE_ERR_ALIGN;
-  // the clamp rule of moe_act_quant_liverows: L <= 0 or +inf: none; a finite
-  // L > 0 must be exactly representable in bf16; NaN is rejected
-  float L = 0.f;
+namespace {
+// The clamp rule of moe_act_quant_liverows: L <= 0 or +inf: none; a finite
+// L > 0 must be exactly representable in bf16; NaN is rejected.
+int fused_clamp(float clamp_limit, float& L) {
+  L = 0.f;
   if (clamp_limit > 0.f && clamp_limit < __builtin_inff()) {
     uint32_t bits;
     std::memcpy(&bits, &clamp_limit, 4);
@@ -810,10 +818,80 @@ extern "C" int moe_grouped_gemm1_act_quant(const uint8_t* xq, const int32_t* xs,
   } else if (!(clamp_limit <= 0.f) && !(clamp_limit == __builtin_inff())) {
     return MOE_ERR_UNSUPPORTED;
   }
+  return MOE_OK;
+}
+
+// Masked slab sizes: m_pad a multiple of 4 (the scale words' MN direction),
+// E_local * m_pad rows addressable with 32-bit row indices.
+int masked_rows(int E_local, int m_pad, int& M_cap) {
+  if (E_local < 0 || m_pad < 0) return MOE_ERR_SHAPE;
+  if (m_pad % 4 != 0) return MOE_ERR_ALIGN;
+  if ((long long)E_local * m_pad >= (1LL << 31)) return MOE_ERR_SHAPE;
+  M_cap = E_local * m_pad;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" int moe_grouped_gemm1_act_quant(const uint8_t* xq, const int32_t* xs,
+                                           const int32_t* expert_ends, int E_local, int A,
+                                           int M_cap, int H, int I,
+                                           const uint8_t* w13_gateup_packed,
+                                           const uint8_t* w13_gateup_scale_packed,
+                                           float clamp_limit, uint8_t* hq, int32_t* hs,
+                                           void* stream) {
+  if (I <= 0 || I % 128 != 0) return MOE_ERR_ALIGN;
+  float L;
+  if (fused_clamp(clamp_limit, L) != MOE_OK) return MOE_ERR_UNSUPPORTED;
   if ((long long)M_cap * I >= (1LL << 31)) return MOE_ERR_SHAPE;
   if (E_local > 0 && M_cap > 0 && (!hq || !hs)) return MOE_ERR_NULL;
   const moe::GemmActOut act{hq, hs, I, L};
   return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I,
                                   w13_gateup_packed, w13_gateup_scale_packed, nullptr, stream,
                                   &act);
+}
+
+extern "C" int moe_grouped_gemm1_masked(const uint8_t* xq, const int32_t* xs,
+                                        const int32_t* masked_m, int E_local, int m_pad, int H,
+                                        int I, const uint8_t* w13_packed,
+                                        const uint8_t* w13_scale_packed, uint16_t* gateup,
+                                        void* stream) {
+  if (I <= 0 || I % 64 != 0) return MOE_ERR_ALIGN;
+  int M_cap = 0;
+  const int rc = masked_rows(E_local, m_pad, M_cap);
+  if (rc != MOE_OK) return rc;
+  return moe::launch_grouped_gemm(xq, xs, masked_m, E_local, 1, M_cap, H, 2 * I, w13_packed,
+                                  w13_scale_packed, gateup, stream, nullptr, false, m_pad);
+}
+
+extern "C" int moe_grouped_gemm2_masked(const uint8_t* hq, const int32_t* hs,
+                                        const int32_t* masked_m, int E_local, int m_pad, int I,
+                                        int H, const uint8_t* w2_packed,
+                                        const uint8_t* w2_scale_packed, uint16_t* down,
+                                        void* stream) {
+  int M_cap = 0;
+  const int rc = masked_rows(E_local, m_pad, M_cap);
+  if (rc != MOE_OK) return rc;
+  return moe::launch_grouped_gemm(hq, hs, masked_m, E_local, 1, M_cap, I, H, w2_packed,
+                                  w2_scale_packed, down, stream, nullptr, false, m_pad);
+}
+
+extern "C" int moe_grouped_gemm1_act_quant_masked(const uint8_t* xq, const int32_t* xs,
+                                                  const int32_t* masked_m, int E_local, int m_pad,
+                                                  int H, int I,
+                                                  const uint8_t* w13_gateup_packed,
+                                                  const uint8_t* w13_gateup_scale_packed,
+                                                  float clamp_limit, uint8_t* hq, int32_t* hs,
+                                                  void* stream) {
+  if (I <= 0 || I % 128 != 0) return MOE_ERR_ALIGN;
+  float L;
+  if (fused_clamp(clamp_limit, L) != MOE_OK) return MOE_ERR_UNSUPPORTED;
+  int M_cap = 0;
+  const int rc = masked_rows(E_local, m_pad, M_cap);
+  if (rc != MOE_OK) return rc;
+  if ((long long)M_cap * I >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (E_local > 0 && M_cap > 0 && (!hq || !hs)) return MOE_ERR_NULL;
+  const moe::GemmActOut act{hq, hs, I, L};
+  return moe::launch_grouped_gemm(xq, xs, masked_m, E_local, 1, M_cap, H, 2 * I,
+                                  w13_gateup_packed, w13_gateup_scale_packed, nullptr, stream,
+                                  &act, false, m_pad);
 }

@@ -73,9 +73,11 @@ __device__ int block_exclusive_scan_1024(int v, int* wave_tot) {
 
 constexpr int kCountBatch = 32;     // ids in flight per lane
 
+// slab > 0: the masked slab layout (starts e * slab, and expert_ends receives
+// masked_m = min(count, slab))
 __global__ __launch_bounds__(1024) void scatter_count_scan_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int A, int TB,
-    int W, int32_t* __restrict__ offsets, int32_t* __restrict__ starts,
+    const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int A, int slab,
+    int TB, int W, int32_t* __restrict__ offsets, int32_t* __restrict__ starts,
     int32_t* __restrict__ expert_ends) {
   __shared__ int s_cnt[kCountLds];
   __shared__ int s_tot[kScatterMaxE];
@@ -143,8 +145,8 @@ __global__ __launch_bounds__(1024) void scatter_count_scan_kernel(
   const int aligned = e < E_local ? align_up_dev(total, A) : 0;
   const int start = block_exclusive_scan_1024(aligned, wave_tot);
   if (e < E_local) {
-    starts[e] = start;
-    expert_ends[e] = start + total;
+    starts[e] = slab > 0 ? e * slab : start;
+    expert_ends[e] = slab > 0 ? min(total, slab) : start + total;
   }
 }
 
@@ -196,10 +198,15 @@ constexpr int kScanMaxE = 256;   // rows-kernel scan: local experts
 // G128: one UE8M0 byte per 128 columns instead of per 32, packed four to a
 // word over 512 columns ([ceil(H/512)][M_cap] words; bytes of groups past H
 // are 0).
-template <bool SCAN, bool G128>
+// SLAB: the masked slab layout ("DeepGEMM FusedMoE on Blackwell (sglang)",
+// section 2.2.4): expert e's rows start at e * slab, a route whose rank in
+// its expert reaches slab is not placed (row -1), expert_ends receives
+// masked_m = min(count, slab), M_cap = E_local * slab, and the scale words
+// are MN-major per expert ([e][word][row - e slab]).
+template <bool SCAN, bool G128, bool SLAB>
 __global__ __launch_bounds__(64 * kRowsWaves) void scatter_rows_kernel(
     const int32_t* __restrict__ ids, int T, int k, int expert_start, int E_local, int A,
-    int M_cap, int TB, int W, const uint16_t* __restrict__ x, int H,
+    int M_cap, int slab, int TB, int W, const uint16_t* __restrict__ x, int H,
     const int32_t* __restrict__ meta, const int32_t* __restrict__ starts,
     int32_t* __restrict__ expert_ends, int32_t* __restrict__ route_row,
     uint8_t* __restrict__ xq, int32_t* __restrict__ xs) {
@@ -255,8 +262,13 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scatter_rows_kernel(
     int start = incl - aligned;
     for (int v = 0; v < wid; ++v) start += s_wsum[v];
     if (e < E_local) {
-      s_base[e] = start + before;
-      if (blockIdx.x == 0) expert_ends[e] = start + total;
+      if constexpr (SLAB) {
+        s_base[e] = e * slab + before;
+        if (blockIdx.x == 0) expert_ends[e] = min(total, slab);
+      } else {
+        s_base[e] = start + before;
+        if (blockIdx.x == 0) expert_ends[e] = start + total;
+      }
     }
     __syncthreads();
   }
@@ -316,6 +328,9 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scatter_rows_kernel(
   int row = -1;
   if (local) {
     row = base + rank;
+    if constexpr (SLAB) {
+      if (row - ev * slab >= slab) row = -1;   // the expert's slab is full: not placed
+    }
     if (row >= M_cap) row = -1;           // corrupt metadata: never write past the buffer
   }
   const uint64_t live = __ballot(row >= 0);
@@ -362,12 +377,21 @@ __global__ __launch_bounds__(64 * kRowsWaves) void scatter_rows_kernel(
       for (uint64_t m = live; m; m &= m - 1) {   // wave-uniform loop over destination rows
         const int s = __ffsll((unsigned long long)m) - 1;
         const int r = __builtin_amdgcn_readlane(row, s);
+        // scale word w of row r: [w][r] over the whole buffer, or
+        // [e][w][r - e slab] inside expert e's slab
+        size_t xs0 = r;
+        int xss = M_cap;
+        if constexpr (SLAB) {
+          const int WN = G128 ? (H + 511) >> 9 : H >> 7;
+          xs0 = (size_t)__builtin_amdgcn_readlane(ev, s) * (size_t)(WN - 1) * (size_t)slab + r;
+          xss = slab;
+        }
         if (col < H) {
           *reinterpret_cast<uint2*>(xq + (size_t)r * H + col) = make_uint2(lo, hi);
           if constexpr (G128) {
-            if (lane == 0) xs[(size_t)(c0 + j) * M_cap + r] = (int32_t)wd;
+            if (lane == 0) xs[xs0 + (size_t)(c0 + j) * xss] = (int32_t)wd;
           } else {
-            if ((lane & 15) == 0) xs[(size_t)(col >> 7) * M_cap + r] = (int32_t)wd;
+            if ((lane & 15) == 0) xs[xs0 + (size_t)(col >> 7) * xss] = (int32_t)wd;
           }
         }
       }
@@ -401,14 +425,17 @@ extern "C" size_t moe_scatter_workspace_bytes(int T, int k, int E_local) {
 
 namespace moe {
 // Host-side checks of the scatter's sizes and pointers (no side effects).
+// slab > 0 (the masked slab layout): M_cap = E_local * slab, and any slab
+// size is valid (routes past a full slab are not placed).
 static int scatter_validate(const int32_t* topk_ids, int T, int k, int E_local, int A, int M_cap,
                             const uint16_t* x, int H, int32_t* expert_ends, int32_t* route_row,
-                            uint8_t* xq, int32_t* xs) {
+                            uint8_t* xq, int32_t* xs, int slab = 0) {
   if (T < 0 || k < 1 || k > kScatterMaxK || E_local < 0 || E_local > kScatterMaxE || A < 1 ||
       M_cap < 0 || H <= 0 || (long long)T * k > INT_MAX)
     return MOE_ERR_SHAPE;
   if (H % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
-  if ((long long)M_cap < (long long)T * k + (long long)E_local * A) return MOE_ERR_CAPACITY;
+  if (slab == 0 && (long long)M_cap < (long long)T * k + (long long)E_local * A)
+    return MOE_ERR_CAPACITY;
   if (E_local == 0 && T == 0) return MOE_OK;
   if (!expert_ends && E_local > 0) return MOE_ERR_NULL;
   if (T > 0 && (!topk_ids || !x || !route_row || !xq || !xs)) return MOE_ERR_NULL;
@@ -418,9 +445,9 @@ static int scatter_validate(const int32_t* topk_ids, int T, int k, int E_local, 
 static int scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_start, int E_local,
                              int A, int M_cap, const uint16_t* x, int H, int32_t* expert_ends,
                              int32_t* route_row, uint8_t* xq, int32_t* xs, void* workspace,
-                             size_t workspace_bytes, void* stream, bool g128) {
+                             size_t workspace_bytes, void* stream, bool g128, int slab = 0) {
   const int bad = scatter_validate(topk_ids, T, k, E_local, A, M_cap, x, H, expert_ends, route_row,
-                                   xq, xs);
+                                   xq, xs, slab);
   if (bad != MOE_OK) return bad;
   if (E_local == 0 && T == 0) return MOE_OK;
   if (T == 0) {
@@ -441,19 +468,23 @@ static int scatter_endpoints(const int32_t* topk_ids, int T, int k, int expert_s
     hipLaunchKernelGGL(scatter_count_kernel, dim3(W), dim3(256), 0, st, topk_ids, T * k,
                        expert_start, E_local, TB * k, meta);
     MOE_CHECK_LAUNCH();
-    auto rows_kernel = g128 ? scatter_rows_kernel<true, true> : scatter_rows_kernel<true, false>;
+    auto rows_kernel = slab > 0 ? scatter_rows_kernel<true, false, true>
+                       : g128 ? scatter_rows_kernel<true, true, false>
+                              : scatter_rows_kernel<true, false, false>;
     hipLaunchKernelGGL(rows_kernel, rows_grid, dim3(64 * kRowsWaves), 0, st, topk_ids, T, k, expert_start,
-                       E_local, A, M_cap, TB, W, x, H, meta, starts, expert_ends, route_row, xq,
-                       xs);
+                       E_local, A, M_cap, slab, TB, W, x, H, meta, starts, expert_ends, route_row,
+                       xq, xs);
     MOE_CHECK_LAUNCH();
   } else {
     hipLaunchKernelGGL(scatter_count_scan_kernel, dim3(1), dim3(1024), 0, st, topk_ids, T, k,
-                       expert_start, E_local, A, TB, W, meta, starts, expert_ends);
+                       expert_start, E_local, A, slab, TB, W, meta, starts, expert_ends);
     MOE_CHECK_LAUNCH();
-    auto rows_kernel = g128 ? scatter_rows_kernel<false, true> : scatter_rows_kernel<false, false>;
+    auto rows_kernel = slab > 0 ? scatter_rows_kernel<false, false, true>
+                       : g128 ? scatter_rows_kernel<false, true, false>
+                              : scatter_rows_kernel<false, false, false>;
     hipLaunchKernelGGL(rows_kernel, rows_grid, dim3(64 * kRowsWaves), 0, st, topk_ids, T, k, expert_start,
-                       E_local, A, M_cap, TB, W, x, H, meta, starts, expert_ends, route_row, xq,
-                       xs);
+                       E_local, A, M_cap, slab, TB, W, x, H, meta, starts, expert_ends, route_row,
+                       xq, xs);
     MOE_CHECK_LAUNCH();
   }
   return MOE_OK;
@@ -527,4 +558,17 @@ extern "C" int moe_scatter_endpoints_g128(const int32_t* topk_ids, int T, int k,
                                           void* stream) {
   return moe::scatter_endpoints(topk_ids, T, k, expert_start, E_local, A, M_cap, x, H, expert_ends,
                                 route_row, xq, xs, workspace, workspace_bytes, stream, true);
+}
+
+extern "C" int moe_scatter_masked(const int32_t* topk_ids, int T, int k, int expert_start,
+                                  int E_local, int m_pad, const uint16_t* x, int H,
+                                  int32_t* masked_m, int32_t* route_row, uint8_t* xq, int32_t* xs,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (E_local < 0 || m_pad < 0) return MOE_ERR_SHAPE;
+  if (m_pad % 4 != 0) return MOE_ERR_ALIGN;
+  if ((long long)E_local * m_pad >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (E_local > 0 && m_pad == 0) return MOE_ERR_SHAPE;
+  return moe::scatter_endpoints(topk_ids, T, k, expert_start, E_local, 1, E_local * m_pad, x, H,
+                                masked_m, route_row, xq, xs, workspace, workspace_bytes, stream,
+                                false, m_pad);
 }

@@ -292,6 +292,136 @@ def moe_grouped_gemm2(hq, hs, expert_ends, A: int, w2_packed, w2_scale_packed, d
     check(st, "moe_grouped_gemm2" + ("" if group == 32 else "_g128"))
 
 
+# ------------------------------------------------- masked (E, m_pad, K) slab
+
+@dataclass
+class MaskedBuffers:
+    masked_m: torch.Tensor      # int32 [E_local]
+    route_row: torch.Tensor     # int32 [T*k]
+    xq: torch.Tensor            # u8 [E_local, m_pad, H]
+    xs: torch.Tensor            # int32 [E_local, H/128, m_pad]
+    workspace: torch.Tensor     # u8
+    gateup: torch.Tensor        # bf16 [E_local, m_pad, 2I]
+    hq: torch.Tensor            # u8 [E_local, m_pad, I]
+    hs: torch.Tensor            # int32 [E_local, I/128, m_pad]
+    down: torch.Tensor          # bf16 [E_local, m_pad, H]
+    out: torch.Tensor           # bf16 [T, H]
+
+
+def alloc_masked(T, k, E_local, m_pad, H, I, device="cuda", fill: bool = False) -> MaskedBuffers:
+    """Allocate every buffer of the chain on the masked slab layout
+    (``fill=True`` plants the same padding sentinels as alloc_grouped)."""
+    def u8(*s):
+        t = torch.empty(s, dtype=torch.uint8, device=device)
+        if fill:
+            t.fill_(0xA5)
+        return t
+
+    def i32(*s):
+        t = torch.empty(s, dtype=torch.int32, device=device)
+        if fill:
+            t.fill_(-1515870811)  # 0xA5A5A5A5
+        return t
+
+    def bf(*s):
+        t = torch.empty(s, dtype=torch.int16, device=device)
+        if fill:
+            t.fill_(0x7FC1)
+        return t.view(torch.bfloat16)
+
+    ws = max(moe_scatter_workspace_bytes(T, k, E_local), 1)
+    return MaskedBuffers(
+        masked_m=torch.empty(E_local, dtype=torch.int32, device=device),
+        route_row=torch.empty(T * k, dtype=torch.int32, device=device),
+        xq=u8(E_local, m_pad, H), xs=i32(E_local, H // 128, m_pad),
+        workspace=torch.empty(ws, dtype=torch.uint8, device=device),
+        gateup=bf(E_local, m_pad, 2 * I), hq=u8(E_local, m_pad, I), hs=i32(E_local, I // 128, m_pad),
+        down=bf(E_local, m_pad, H), out=bf(T, H))
+
+
+def moe_scatter_masked(topk_ids, expert_start: int, x, masked_m, route_row, xq, xs, workspace):
+    _req(topk_ids, "topk_ids", (torch.int32,))
+    T, k = topk_ids.shape
+    _req(x, "x", _BF16)
+    H = x.shape[1]
+    _req(xq, "xq", (torch.uint8,))
+    E_local, m_pad, _ = xq.shape
+    _req(x, "x", _BF16, (T, H))
+    _req(xq, "xq", (torch.uint8,), (E_local, m_pad, H))
+    _req(masked_m, "masked_m", (torch.int32,), (E_local,))
+    _req(route_row, "route_row", (torch.int32,), (T * k,))
+    _req(xs, "xs", (torch.int32,), (E_local, H // 128, m_pad))
+    _req(workspace, "workspace", (torch.uint8,))
+    st = lib().moe_scatter_masked(_ptr(topk_ids), T, k, expert_start, E_local, m_pad, _ptr(x), H,
+                                  _ptr(masked_m), _ptr(route_row), _ptr(xq), _ptr(xs),
+                                  _ptr(workspace), workspace.numel(), _stream())
+    check(st, "moe_scatter_masked")
+
+
+def moe_grouped_gemm1_masked(xq, xs, masked_m, w13_packed, w13_scale_packed, gateup):
+    _req(xq, "xq", (torch.uint8,))
+    E_local, m_pad, H = xq.shape
+    _, twoI, _ = w13_packed.shape
+    I = twoI // 2
+    _req(xs, "xs", (torch.int32,), (E_local, H // 128, m_pad))
+    _req(masked_m, "masked_m", (torch.int32,), (E_local,))
+    _req(w13_packed, "w13_packed", (torch.uint8,), (E_local, 2 * I, H // 2))
+    _req(w13_scale_packed, "w13_scale_packed", (torch.uint8,), packed_scale_shape(E_local, 2 * I, H))
+    _req(gateup, "gateup", _BF16, (E_local, m_pad, 2 * I))
+    st = lib().moe_grouped_gemm1_masked(_ptr(xq), _ptr(xs), _ptr(masked_m), E_local, m_pad, H, I,
+                                        _ptr(w13_packed), _ptr(w13_scale_packed), _ptr(gateup),
+                                        _stream())
+    check(st, "moe_grouped_gemm1_masked")
+
+
+def moe_act_quant_masked(gateup, masked_m, clamp_limit: float, hq, hs):
+    _req(gateup, "gateup", _BF16)
+    E_local, m_pad, twoI = gateup.shape
+    I = twoI // 2
+    _req(masked_m, "masked_m", (torch.int32,), (E_local,))
+    _req(hq, "hq", (torch.uint8,), (E_local, m_pad, I))
+    _req(hs, "hs", (torch.int32,), (E_local, I // 128, m_pad))
+    st = lib().moe_act_quant_masked(_ptr(gateup), _ptr(masked_m), E_local, m_pad, I,
+                                    float(clamp_limit), _ptr(hq), _ptr(hs), _stream())
+    check(st, "moe_act_quant_masked")
+
+
+def moe_grouped_gemm1_act_quant_masked(xq, xs, masked_m, w13_gateup_packed,
+                                       w13_gateup_scale_packed, clamp_limit: float, hq, hs):
+    _req(xq, "xq", (torch.uint8,))
+    E_local, m_pad, H = xq.shape
+    _, twoI, _ = w13_gateup_packed.shape
+    I = twoI // 2
+    _req(xs, "xs", (torch.int32,), (E_local, H // 128, m_pad))
+    _req(masked_m, "masked_m", (torch.int32,), (E_local,))
+    _req(w13_gateup_packed, "w13_gateup_packed", (torch.uint8,), (E_local, 2 * I, H // 2))
+    _req(w13_gateup_scale_packed, "w13_gateup_scale_packed", (torch.uint8,),
+         packed_scale_shape(E_local, 2 * I, H))
+    _req(hq, "hq", (torch.uint8,), (E_local, m_pad, I))
+    _req(hs, "hs", (torch.int32,), (E_local, I // 128, m_pad))
+    st = lib().moe_grouped_gemm1_act_quant_masked(_ptr(xq), _ptr(xs), _ptr(masked_m), E_local,
+                                                  m_pad, H, I, _ptr(w13_gateup_packed),
+                                                  _ptr(w13_gateup_scale_packed),
+                                                  float(clamp_limit), _ptr(hq), _ptr(hs),
+                                                  _stream())
+    check(st, "moe_grouped_gemm1_act_quant_masked")
+
+
+def moe_grouped_gemm2_masked(hq, hs, masked_m, w2_packed, w2_scale_packed, down):
+    _req(hq, "hq", (torch.uint8,))
+    E_local, m_pad, I = hq.shape
+    _, H, _ = w2_packed.shape
+    _req(hs, "hs", (torch.int32,), (E_local, I // 128, m_pad))
+    _req(masked_m, "masked_m", (torch.int32,), (E_local,))
+    _req(w2_packed, "w2_packed", (torch.uint8,), (E_local, H, I // 2))
+    _req(w2_scale_packed, "w2_scale_packed", (torch.uint8,), packed_scale_shape(E_local, H, I))
+    _req(down, "down", _BF16, (E_local, m_pad, H))
+    st = lib().moe_grouped_gemm2_masked(_ptr(hq), _ptr(hs), _ptr(masked_m), E_local, m_pad, I, H,
+                                        _ptr(w2_packed), _ptr(w2_scale_packed), _ptr(down),
+                                        _stream())
+    check(st, "moe_grouped_gemm2_masked")
+
+
 # ---------------------------------------------------------------- combine
 
 def moe_combine(rows, row_of_slot, topk_weights, routed_scale: float, out):
@@ -369,6 +499,30 @@ def moe_ffn_prefill_fused(x, topk_ids, topk_weights, expert_start: int, A: int,
                                 w13_gateup_scale_packed, clamp_limit, buf.hq, buf.hs)
     moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, A, w2_packed, w2_scale_packed, buf.down)
     moe_combine(buf.down, buf.route_row, topk_weights, routed_scale, buf.out)
+    return buf.out
+
+
+def moe_ffn_prefill_masked(x, topk_ids, topk_weights, expert_start: int, w13_packed,
+                           w13_scale_packed, w2_packed, w2_scale_packed, buf: MaskedBuffers,
+                           clamp_limit: float = 0.0, routed_scale: float = 1.0,
+                           fused: bool = False):
+    """The chain on the masked slab layout: masked scatter -> GEMM1 ->
+    varlen act-quant -> GEMM2 -> combine over the slab's rows. ``fused``:
+    GEMM1 and the act-quant in one kernel (w13 from
+    moe_pack_mx_weights_gateup)."""
+    moe_scatter_masked(topk_ids, expert_start, x, buf.masked_m, buf.route_row, buf.xq, buf.xs,
+                       buf.workspace)
+    if fused:
+        moe_grouped_gemm1_act_quant_masked(buf.xq, buf.xs, buf.masked_m, w13_packed,
+                                           w13_scale_packed, clamp_limit, buf.hq, buf.hs)
+    else:
+        moe_grouped_gemm1_masked(buf.xq, buf.xs, buf.masked_m, w13_packed, w13_scale_packed,
+                                 buf.gateup)
+        moe_act_quant_masked(buf.gateup, buf.masked_m, clamp_limit, buf.hq, buf.hs)
+    moe_grouped_gemm2_masked(buf.hq, buf.hs, buf.masked_m, w2_packed, w2_scale_packed, buf.down)
+    E_local, m_pad, H = buf.down.shape
+    moe_combine(buf.down.view(E_local * m_pad, H), buf.route_row, topk_weights, routed_scale,
+                buf.out)
     return buf.out
 
 

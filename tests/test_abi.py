@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 9
+    assert lib.moe_abi_version() == 10
     for s in range(0, -10, -1):
         assert lib.moe_status_string(s).decode()
     assert lib.moe_status_string(5).decode() == "unknown status"
@@ -125,6 +125,38 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 200, 128, NULL, NULL, NULL) == -3
     assert lib.moe_pack_mx_weights(NULL, NULL, 0, 256, 128, NULL, NULL, NULL) == 0
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 256, 128, NULL, NULL, NULL) == -1
+    # masked slab forms: m_pad not a multiple of 4, E_local * m_pad too
+    # large, m_pad 0 with experts (scatter), then the aligned forms' checks
+    ms = [NULL, 64, 2, 0, 8, 130, NULL, 256, NULL, NULL, NULL, NULL, NULL, 0, NULL]
+    assert lib.moe_scatter_masked(*ms) == -3
+    ms[5] = 1 << 28
+    assert lib.moe_scatter_masked(*ms) == -2
+    ms[5] = 0
+    assert lib.moe_scatter_masked(*ms) == -2
+    ms[5], ms[7] = 128, 200
+    assert lib.moe_scatter_masked(*ms) == -3                                      # H % 128
+    ms[7] = 256
+    assert lib.moe_scatter_masked(*ms) == -1                                      # NULL pointers
+    assert lib.moe_grouped_gemm1_masked(NULL, NULL, NULL, 8, 130, 256, 128, NULL, NULL, NULL,
+                                        NULL) == -3
+    assert lib.moe_grouped_gemm1_masked(NULL, NULL, NULL, 8, 128, 192, 128, NULL, NULL, NULL,
+                                        NULL) == -3
+    assert lib.moe_grouped_gemm1_masked(NULL, NULL, NULL, 8, 128, 256, 128, NULL, NULL, NULL,
+                                        NULL) == -1
+    assert lib.moe_grouped_gemm2_masked(NULL, NULL, NULL, 8, 128, 100, 256, NULL, NULL, NULL,
+                                        NULL) == -3
+    assert lib.moe_act_quant_masked(NULL, NULL, 8, 130, 128, ctypes.c_float(0.0), NULL, NULL,
+                                    NULL) == -3
+    assert lib.moe_act_quant_masked(NULL, NULL, 8, 128, 128, ctypes.c_float(7.3), NULL, NULL,
+                                    NULL) == -5
+    assert lib.moe_act_quant_masked(NULL, NULL, 8, 128, 128, ctypes.c_float(0.0), NULL, NULL,
+                                    NULL) == -1
+    assert lib.moe_grouped_gemm1_act_quant_masked(NULL, NULL, NULL, 8, 128, 256, 128, NULL, NULL,
+                                                  ctypes.c_float(7.3), NULL, NULL, NULL) == -5
+    assert lib.moe_grouped_gemm1_act_quant_masked(NULL, NULL, NULL, 8, 128, 256, 64, NULL, NULL,
+                                                  ctypes.c_float(0.0), NULL, NULL, NULL) == -3
+    assert lib.moe_grouped_gemm1_act_quant_masked(NULL, NULL, NULL, 8, 0, 256, 128, NULL, NULL,
+                                                  ctypes.c_float(0.0), NULL, NULL, NULL) == 0
     # combine: H not a multiple of 8
     assert lib.moe_combine(NULL, 0, NULL, NULL, 4, 2, 12, ctypes.c_float(1.0), NULL, NULL) == -3
     # sparse GEMV: too many slots, unsupported format
