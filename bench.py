@@ -24,6 +24,7 @@ The same line carries:
                 control, cold
   decode        the sparse decode layer at 1 and 8 tokens (FP8 and MXFP4):
                 per-kernel cold durations and the graph-replayed layer
+  masked        the headline layer on the masked (E, m_pad, K) slab layout
   cpu_baseline  the CPU oracle on the host: the headline layer on all threads
                 (the value) and, per workload, on one thread and on all
 
@@ -351,6 +352,8 @@ def main():
         result["layers"] = bench_other_layers(ops, torch, up, up_bf16, log)
         result["actquant"] = bench_actquant(ops, torch, up, up_bf16, log)
         result["decode"] = bench_decode(ops, torch, up, up_bf16, log)
+        result["masked"] = bench_masked(ops, torch, up, up_bf16, log, c, ids, wts, logits_own,
+                                        own_ids, own_w, fused)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c, log)
     print(json.dumps(result), flush=True)
@@ -410,6 +413,88 @@ def bench_g128(ops, torch, up, c, ids, wts, logits_own, own_ids, own_w, log, ste
     log("recipe g128", round(us, 2), dur)
     return {"us_per_layer_graph": round(us, 2), "kernels_us": dur,
             "note": "two-call GEMM1 + act-quant (no fused form for group 128)"}
+
+
+def bench_masked(ops, torch, up, up_bf16, log, c, ids, wts, logits_own, own_ids, own_w, fused,
+                 steps=20, warmup=5):
+    """The same EP-share layer on the masked slab layout: every local expert
+    owns a fixed block of m_pad rows. Two capacities: the group's token count
+    (4,096; no expert can overflow it) and the busiest expert's count
+    rounded up to 256 (known here from the routing; a caller would need a
+    device-to-host read for it). Per-kernel durations of cold eager steps
+    and the cold graph-replayed layer."""
+    w = c.weights
+    pack13 = ops.moe_pack_mx_weights_gateup if fused else ops.moe_pack_mx_weights
+    w13, s13 = pack13(up(w.w13), up(w.s13))
+    w2, s2 = ops.moe_pack_mx_weights(up(w.w2), up(w.s2))
+    x = up_bf16(c.x)
+    counts = local_counts(ids.cpu().numpy(), 0, c.E_local)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for label, m_pad in (("m_pad_tokens", c.T), ("m_pad_max_count", (int(counts.max()) + 255) // 256 * 256)):
+        buf = ops.alloc_masked(c.T, c.k, c.E_local, m_pad, c.H, c.I)
+        names = (["route", "scatter", "gemm1_act", "gemm2", "combine"] if fused else
+                 ["route", "scatter", "gemm1", "act_quant", "gemm2", "combine"])
+
+        def step(ev=None):
+            def mark(i):
+                if ev is not None:
+                    ev[i].record()
+            mark(0)
+            ops.moe_route(logits_own, c.k, "softmax", None, own_ids, own_w)
+            mark(1)
+            ops.moe_scatter_masked(ids, 0, x, buf.masked_m, buf.route_row, buf.xq, buf.xs,
+                                   buf.workspace)
+            mark(2)
+            if fused:
+                ops.moe_grouped_gemm1_act_quant_masked(buf.xq, buf.xs, buf.masked_m, w13, s13, 0.0,
+                                                       buf.hq, buf.hs)
+            else:
+                ops.moe_grouped_gemm1_masked(buf.xq, buf.xs, buf.masked_m, w13, s13, buf.gateup)
+                mark(3)
+                ops.moe_act_quant_masked(buf.gateup, buf.masked_m, 0.0, buf.hq, buf.hs)
+            mark(len(names) - 2)
+            ops.moe_grouped_gemm2_masked(buf.hq, buf.hs, buf.masked_m, w2, s2, buf.down)
+            mark(len(names) - 1)
+            ops.moe_combine(buf.down.view(c.E_local * m_pad, c.H), buf.route_row, wts,
+                            c.routed_scale, buf.out)
+            mark(len(names))
+
+        for _ in range(warmup):
+            step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            _flush_caches(torch, scratch)
+            step(evs[i])
+        torch.cuda.synchronize()
+        dur = {n: round(float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                       for i in range(steps)])) * 1e3, 3)
+               for j, n in enumerate(names)}
+        graph = ops.capture_graph(lambda: step(None))
+        for _ in range(warmup):
+            graph.replay()
+        cold = []
+        for _ in range(steps):
+            _flush_caches(torch, scratch)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            e1.synchronize()
+            cold.append(e0.elapsed_time(e1) * 1e3)
+        del graph
+        used = [buf.xq, buf.xs, buf.hq, buf.hs, buf.down] + ([] if fused else [buf.gateup])
+        slab_bytes = sum(t.numel() * t.element_size() for t in used)
+        out[label] = {"m_pad": m_pad, "us_per_layer_graph_cold": round(float(np.median(cold)), 2),
+                      "kernels_us_cold": dur, "slab_buffer_bytes": int(slab_bytes)}
+        log(f"masked {label}", out[label])
+        del buf
+        torch.cuda.empty_cache()
+    del scratch, w13, s13, w2, s2, x
+    torch.cuda.empty_cache()
+    return out
 
 
 def _flush_caches(torch, scratch):

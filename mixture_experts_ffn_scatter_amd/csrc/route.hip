@@ -7,12 +7,126 @@
 // DeepGEMM FusedMoE (sglang)", section 1; "Phase 20: Sparse MoE Decode",
 // section 1). Sigmoid routing selects on sigmoid(logit) + correction bias and
 // weights the unbiased sigmoid, renormalised ("Kimi-K3 on SM120 FlashInfer
-// MXFP4", Phase 1 call chain). The sigmoid used for selection is the fp32
-// rounding of a fp64 evaluation, i.e. the correctly rounded value except
-// where an fp64 result falls within a few fp64 ulps of an fp32 midpoint.
+// MXFP4", Phase 1 call chain). The sigmoid used for selection is the
+// correctly rounded fp32 value of 1/(1+e^-x): an fp64 evaluation decides it
+// unless it lies within 2^-47 (relative) of an fp32 rounding midpoint, and
+// there a double-double evaluation decides.
 #include "common.h"
 
 namespace moe {
+
+// ---------------------------------------------- correctly rounded sigmoid
+//
+// Double-double arithmetic (a value is hi + lo with |lo| <= ulp(hi)/2):
+// the error-free sum of Knuth and the error-free product by fused
+// multiply-add, and the usual dd add / multiply / divide built on them.
+// (The library compiles with floating-point contraction off, so no
+// expression below is fused behind its back.)
+struct dd {
+  double hi, lo;
+};
+__device__ __forceinline__ dd dd_two_sum(double a, double b) {
+  const double s = a + b;
+  const double bb = s - a;
+  return {s, (a - (s - bb)) + (b - bb)};
+}
+__device__ __forceinline__ dd dd_fast_two_sum(double a, double b) {   // |a| >= |b|
+  const double s = a + b;
+  return {s, b - (s - a)};
+}
+__device__ __forceinline__ dd dd_add(dd a, dd b) {
+  dd s = dd_two_sum(a.hi, b.hi);
+  const dd t = dd_two_sum(a.lo, b.lo);
+  s.lo += t.hi;
+  s = dd_fast_two_sum(s.hi, s.lo);
+  s.lo += t.lo;
+  return dd_fast_two_sum(s.hi, s.lo);
+}
+__device__ __forceinline__ dd dd_mul(dd a, dd b) {
+  const double p = a.hi * b.hi;
+  double e = __builtin_fma(a.hi, b.hi, -p);
+  e += a.hi * b.lo + a.lo * b.hi;
+  return dd_fast_two_sum(p, e);
+}
+__device__ __forceinline__ dd dd_mul_d(dd a, double b) {
+  const double p = a.hi * b;
+  double e = __builtin_fma(a.hi, b, -p);
+  e += a.lo * b;
+  return dd_fast_two_sum(p, e);
+}
+// a / b by long division: three quotient digits
+__device__ __forceinline__ dd dd_div(dd a, dd b) {
+  const double q1 = a.hi / b.hi;
+  dd r = dd_add(a, dd_mul_d(b, -q1));
+  const double q2 = r.hi / b.hi;
+  r = dd_add(r, dd_mul_d(b, -q2));
+  const double q3 = r.hi / b.hi;
+  return dd_add(dd_fast_two_sum(q1, q2), dd{q3, 0.0});
+}
+
+// e^x in double-double for |x| <= 110: x = n ln2 + r with |r| <= ln2/2
+// (ln2 as a double-double), e^(r/1024) - 1 by its Taylor series through
+// degree 9 (Horner; the first dropped term is below 2^-120 of the sum),
+// then ten squarings of 1 + t in the form t <- t (t + 2), and the power of
+// two. Relative error well below 2^-90.
+__device__ dd dd_exp(double x) {
+  const dd ln2{0x1.62e42fefa39efp-1, 0x1.abc9e3b39803fp-56};
+  const double n = __builtin_rint(x * 0x1.71547652b82fep0);   // nearest integer to x / ln2
+  dd r = dd_add(dd{x, 0.0}, dd_mul_d(ln2, -n));
+  r.hi = __builtin_ldexp(r.hi, -10);
+  r.lo = __builtin_ldexp(r.lo, -10);
+  // 1/j! as a double-double (j! is exact in fp64 for j <= 9)
+  auto inv_fact = [](int j) {
+    double f = 1.0;
+    for (int i = 2; i <= j; ++i) f *= (double)i;
+    return dd_div(dd{1.0, 0.0}, dd{f, 0.0});
+  };
+  // p = 1/1! + r/2! + r^2/3! + ... + r^8/9!
+  dd p = inv_fact(9);
+  for (int j = 8; j >= 1; --j) p = dd_add(inv_fact(j), dd_mul(r, p));
+  dd t = dd_mul(r, p);                                         // e^(r/1024) - 1
+  for (int i = 0; i < 10; ++i) t = dd_mul(t, dd_add(t, dd{2.0, 0.0}));
+  const dd e = dd_add(dd{1.0, 0.0}, t);
+  const int ni = (int)n;
+  return {__builtin_ldexp(e.hi, ni), __builtin_ldexp(e.lo, ni)};
+}
+
+// neighbours of a non-negative finite fp32 value
+__device__ __forceinline__ float f32_up(float f) { return __uint_as_float(__float_as_uint(f) + 1u); }
+__device__ __forceinline__ float f32_down(float f) {
+  return f > 0.f ? __uint_as_float(__float_as_uint(f) - 1u) : -__uint_as_float(1u);
+}
+
+// The fp32 value nearest 1/(1+e^-v), ties to even.
+__device__ float sigmoid_f32_rn(float v) {
+  const double x = (double)v;
+  const double s64 = 1.0 / (1.0 + exp(-x));
+  const float f = (float)s64;                 // in [0, 1]
+  // the two rounding midpoints around f (exact in fp64, also for subnormal f)
+  const double fd = (double)f;
+  const double m_lo = 0.5 * (fd + (double)f32_down(f));
+  const double m_hi = 0.5 * (fd + (double)f32_up(f));
+  const double tol = 0x1p-47 * s64;
+  const bool near_lo = __builtin_fabs(s64 - m_lo) <= tol;
+  const bool near_hi = __builtin_fabs(s64 - m_hi) <= tol;
+  if (!(near_lo || near_hi)) return f;
+  if (!(x > -110.0 && x < 110.0)) return f;   // beyond: never near a midpoint
+  // double-double: for v >= 0, 1 / (1 + e^-v); for v < 0, e^v / (1 + e^v)
+  dd sig;
+  if (x >= 0.0) {
+    const dd e = dd_exp(-x);
+    sig = dd_div(dd{1.0, 0.0}, dd_add(dd{1.0, 0.0}, e));
+  } else {
+    const dd e = dd_exp(x);
+    sig = dd_div(e, dd_add(dd{1.0, 0.0}, e));
+  }
+  // which side of the midpoint: sig.hi - m is exact near m (Sterbenz)
+  const double m = near_hi ? m_hi : m_lo;
+  const double side = (sig.hi - m) + sig.lo;
+  const bool odd = (__float_as_uint(f) & 1u) != 0;
+  if (near_hi) return (side > 0.0 || (side == 0.0 && odd)) ? f32_up(f) : f;
+  return (side < 0.0 || (side == 0.0 && odd)) ? f32_down(f) : f;
+}
 
 constexpr int kRouteTokensPerBlock = 4;
 constexpr int kRouteMaxE = 1024;
@@ -70,8 +184,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
       const float v = row[e];
       float key = v;
       if (SIGMOID) {
-        const double s64 = 1.0 / (1.0 + exp(-(double)v));
-        aux[j] = (float)s64;
+        aux[j] = sigmoid_f32_rn(v);
         key = __fadd_rn(aux[j], bias[e]);
       } else {
         aux[j] = v;
