@@ -712,6 +712,29 @@ def bench_decode(ops, torch, up, up_bf16, log, iters=20):
                 cold.append(e0.elapsed_time(e1) * 1e3)
                 warm.append(e1.elapsed_time(e2) * 1e3)
             del graph
+            # the same layer with the GLU applied on load by the down GEMV
+            gu_buf = torch.empty((T * base.k, base.N_gu), dtype=torch.bfloat16, device="cuda")
+
+            def chain_on_load():
+                ops.moe_sparse_gemv(x, False, ids, 0, base.E, wfmt, dw[0], dw[1], dw[2], gu_buf,
+                                    dbuf.slot_row, glu=False)
+                ops.moe_sparse_gemv(gu_buf, True, ids, 0, base.E, wfmt, dw[3], dw[4], dw[5],
+                                    dbuf.down, None, glu_on_load=True)
+                ops.moe_combine(dbuf.down, dbuf.slot_row, wts, 1.0, dbuf.out)
+
+            graph = ops.capture_graph(chain_on_load)
+            for _ in range(3):
+                graph.replay()
+            cold_ol = []
+            for i in range(iters):
+                _flush_caches(torch, scratch)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                cold_ol.append(e0.elapsed_time(e1) * 1e3)
+            del graph, gu_buf
             U = int(np.unique(ids.cpu().numpy()).size)
             H, N = base.H, base.N_gu
             if wfmt == "fp8":
@@ -731,7 +754,8 @@ def bench_decode(ops, torch, up, up_bf16, log, iters=20):
                         "gemvs_hbm_frac": round((B_gu + B_d) / ((d_gu + d_d) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                         "kernel_sum_us": round(d_gu + d_d + d_c, 3),
                         "layer_graph_us_cold": round(float(np.median(cold)), 3),
-                        "layer_graph_us_warm": round(float(np.median(warm)), 3)}
+                        "layer_graph_us_warm": round(float(np.median(warm)), 3),
+                        "layer_graph_us_cold_glu_on_load": round(float(np.median(cold_ol)), 3)}
             log("decode", key, out[key])
         del dw, base
         torch.cuda.empty_cache()

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 10
+#define MOE_ABI_VERSION 11
 
 enum moe_status {
     MOE_OK = 0,
@@ -476,10 +476,18 @@ int moe_combine(const uint16_t* rows, int64_t n_rows, const int32_t* row_of_slot
  *                   g = y[j], u = y[j+N/2] (already rounded to bf16),
  *                   g' = min(g, glu_limit), u' = clamp(u, -glu_limit, glu_limit)
  *                   (glu_limit <= 0: no clamp).
+ *                2: the GLU on load: act is the per-slot gate/up output of
+ *                   a glu = 0 call, bf16 [T*k, 2K] (act_per_slot must be 1),
+ *                   and the activation element j of slot q is the bf16 value
+ *                   of the formula above with g = act[q, j], u = act[q, K+j];
+ *                   out bf16 [T*k, N] holds y. A glu = 1 gate_up call
+ *                   followed by a glu = 0 down call gives the same bytes as
+ *                   a glu = 0 gate_up call followed by a glu = 2 down call.
  *   out          row t*k+s is written only when slot (t,s) is local
  *   slot_row     int32 [T*k] out or NULL: t*k+s when local, else -1
  * Requires K % 32 == 0 (FP8: K % 16 == 0 suffices), K <= 8192, N % 2 == 0
- * when glu, 1 <= T*k <= 64, E_local <= 1024.
+ * when glu == 1, 1 <= T*k <= 64, E_local <= 1024; glu outside 0..2, or
+ * glu == 2 with act_per_slot == 0, is MOE_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 int moe_sparse_gemv(const uint16_t* act, int act_per_slot, const int32_t* topk_ids, int T, int k,
                     int expert_start, int E_local, int N, int K, int wfmt, const uint8_t* w,

@@ -22,7 +22,12 @@
 // converted to exact bf16 pairs and dotted in fp32; the partial sums are
 // folded inside each wave with DPP adds and across the waves of a row group
 // through LDS in a fixed order. With the GLU fused, the GLU is applied to the
-// bf16-rounded gate and up results before the single bf16 store.
+// bf16-rounded gate and up results before the single bf16 store. With the
+// GLU applied on load instead (GLU_LOAD), the activation rows are the
+// per-slot gate/up outputs of the first GEMV ([T*k, 2K]: gate then up) and
+// each activation element is the bf16 rounding of the GLU of its gate and
+// up values, formed as the chunk is read; the results equal those of the
+// fused form, whose stored activation is that same bf16 value.
 #include <cmath>
 #include <type_traits>
 
@@ -92,7 +97,7 @@ __device__ __forceinline__ void fp4x32_to_bf16(const v4i raw, v2bf* wp) {
 // (one E8M0 scale group). A row group of threads covers K: all 256 threads
 // for FP8; 128 for MXFP4, whose rows are half as long, so that a block
 // holds 2 row groups of 8 rows (16 rows, about the bytes of FP8's 8).
-template <bool MXFP4, bool GLU, int CH>
+template <bool MXFP4, bool GLU, int CH, bool GLU_LOAD>
 __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
     const uint16_t* __restrict__ act, int act_per_slot, const int32_t* __restrict__ ids, int T,
     int k, int expert_start, int E_local, int N, int K, const uint8_t* __restrict__ W,
@@ -194,15 +199,37 @@ __global__ __launch_bounds__(kGemvThreads) void sparse_gemv_kernel(
 #pragma unroll
       for (int b = 0; b < kGemvSlotBatch; ++b) {
         const int arow = p[b] < 0 ? 0 : (act_per_slot ? p[b] : p[b] / k);
-        const v4i* ap = reinterpret_cast<const v4i*>(act + (size_t)arow * K + (size_t)chc * kWpc);
+        if constexpr (GLU_LOAD) {
+          // gate at [arow, chunk], up K columns later; each pair -> bf16(glu)
+          const uint16_t* gp = act + (size_t)arow * (2 * (size_t)K) + (size_t)chc * kWpc;
+          const v4i* g4p = reinterpret_cast<const v4i*>(gp);
+          const v4i* u4p = reinterpret_cast<const v4i*>(gp + K);
 #pragma unroll
-        for (int v = 0; v < kWpc / 8; ++v) {
-          const v4i a4 = ap[v];
-          // components copied out first: a bit cast of a vector component
-          // expression reads the vector's first component
-          const int w4[4] = {a4.x, a4.y, a4.z, a4.w};
+          for (int v = 0; v < kWpc / 8; ++v) {
+            const v4i g4 = g4p[v], u4 = u4p[v];
+            const uint32_t gw[4] = {(uint32_t)g4.x, (uint32_t)g4.y, (uint32_t)g4.z, (uint32_t)g4.w};
+            const uint32_t uw[4] = {(uint32_t)u4.x, (uint32_t)u4.y, (uint32_t)u4.z, (uint32_t)u4.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) av[b][4 * v + i] = __builtin_bit_cast(v2bf, w4[i]);
+            for (int i = 0; i < 4; ++i) {
+              const float lo = glu_apply(bf16_to_f32((uint16_t)(gw[i] & 0xFFFFu)),
+                                         bf16_to_f32((uint16_t)(uw[i] & 0xFFFFu)), alpha, beta, limit);
+              const float hi = glu_apply(bf16_to_f32((uint16_t)(gw[i] >> 16)),
+                                         bf16_to_f32((uint16_t)(uw[i] >> 16)), alpha, beta, limit);
+              const uint32_t packed = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+              av[b][4 * v + i] = __builtin_bit_cast(v2bf, packed);
+            }
+          }
+        } else {
+          const v4i* ap = reinterpret_cast<const v4i*>(act + (size_t)arow * K + (size_t)chc * kWpc);
+#pragma unroll
+          for (int v = 0; v < kWpc / 8; ++v) {
+            const v4i a4 = ap[v];
+            // components copied out first: a bit cast of a vector component
+            // expression reads the vector's first component
+            const int w4[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[b][4 * v + i] = __builtin_bit_cast(v2bf, w4[i]);
+          }
         }
       }
       if (valid) {
@@ -271,9 +298,12 @@ extern "C" int moe_sparse_gemv(const uint16_t* act, int act_per_slot, const int3
   if (T < 0 || k < 1 || E_local < 0 || E_local > 1024 || N <= 0 || K <= 0) return MOE_ERR_SHAPE;
   if ((long long)T * k > kGemvMaxSlots) return MOE_ERR_SHAPE;
   if (wfmt != MOE_W_FP8_PER_EXPERT && wfmt != MOE_W_MXFP4_G32) return MOE_ERR_UNSUPPORTED;
+  if (glu < 0 || glu > 2) return MOE_ERR_UNSUPPORTED;
+  // GLU on load: the activation is the per-slot gate/up rows [T*k, 2K]
+  if (glu == 2 && act_per_slot != 1) return MOE_ERR_UNSUPPORTED;
   if (K % (wfmt == MOE_W_MXFP4_G32 ? 32 : 16) != 0) return MOE_ERR_ALIGN;
   if (K % 8 != 0) return MOE_ERR_ALIGN;
-  if (glu && N % 2 != 0) return MOE_ERR_ALIGN;
+  if (glu == 1 && N % 2 != 0) return MOE_ERR_ALIGN;
   if (act_per_slot != 0 && act_per_slot != 1) return MOE_ERR_UNSUPPORTED;
   const bool mx = wfmt == MOE_W_MXFP4_G32;
   // FP8: 16 weights per thread chunk over 256 threads; MXFP4: 32 over 128
@@ -281,24 +311,26 @@ extern "C" int moe_sparse_gemv(const uint16_t* act, int act_per_slot, const int3
   if (chunks_per_thread > kGemvMaxCh) return MOE_ERR_SHAPE;  // K <= 8192
   if (T == 0) return MOE_OK;
   if (!act || !topk_ids || !w || !w_scale || !out) return MOE_ERR_NULL;
-  const int n_out = glu ? N / 2 : N;
+  const int n_out = glu == 1 ? N / 2 : N;
   const int rows_per_block = mx ? 2 * kGemvRows : kGemvRows;
-  const int outs_per_block = glu ? rows_per_block / 2 : rows_per_block;
+  const int outs_per_block = glu == 1 ? rows_per_block / 2 : rows_per_block;
   dim3 grid((n_out + outs_per_block - 1) / outs_per_block, T * k);
   hipStream_t st = (hipStream_t)stream;
-#define MOE_GEMV_LAUNCH(MX, G, CHN)                                                            \
-  hipLaunchKernelGGL((sparse_gemv_kernel<MX, G, CHN>), grid, dim3(kGemvThreads), 0, st, act,  \
+#define MOE_GEMV_LAUNCH(MX, G, CHN, GL)                                                        \
+  hipLaunchKernelGGL((sparse_gemv_kernel<MX, G, CHN, GL>), grid, dim3(kGemvThreads), 0, st, act, \
                      act_per_slot, topk_ids, T, k, expert_start, E_local, N, K, w, w_scale, bias, \
                      glu_alpha, glu_beta, glu_limit, out, slot_row)
-#define MOE_GEMV_CH(MX, G)                       \
-  switch (chunks_per_thread) {                   \
-    case 1: MOE_GEMV_LAUNCH(MX, G, 1); break;    \
-    default: MOE_GEMV_LAUNCH(MX, G, 2); break;   \
+#define MOE_GEMV_CH(MX, G, GL)                       \
+  switch (chunks_per_thread) {                       \
+    case 1: MOE_GEMV_LAUNCH(MX, G, 1, GL); break;    \
+    default: MOE_GEMV_LAUNCH(MX, G, 2, GL); break;   \
   }
-  if (mx && glu) MOE_GEMV_CH(true, true)
-  else if (mx) MOE_GEMV_CH(true, false)
-  else if (glu) MOE_GEMV_CH(false, true)
-  else MOE_GEMV_CH(false, false)
+  if (mx && glu == 1) MOE_GEMV_CH(true, true, false)
+  else if (mx && glu == 2) MOE_GEMV_CH(true, false, true)
+  else if (mx) MOE_GEMV_CH(true, false, false)
+  else if (glu == 1) MOE_GEMV_CH(false, true, false)
+  else if (glu == 2) MOE_GEMV_CH(false, false, true)
+  else MOE_GEMV_CH(false, false, false)
 #undef MOE_GEMV_CH
 #undef MOE_GEMV_LAUNCH
   MOE_CHECK_LAUNCH();

@@ -440,12 +440,24 @@ def moe_combine(rows, row_of_slot, topk_weights, routed_scale: float, out):
 
 def moe_sparse_gemv(act, act_per_slot: bool, topk_ids, expert_start: int, E_local: int,
                     wfmt: str, w, w_scale, bias, out, slot_row=None, glu: bool = False,
-                    glu_alpha: float = 1.702, glu_beta: float = 1.0, glu_limit: float = 7.0):
+                    glu_alpha: float = 1.702, glu_beta: float = 1.0, glu_limit: float = 7.0,
+                    glu_on_load: bool = False):
+    """``glu``: the GLU in the epilogue (out [T*k, N/2]). ``glu_on_load``: the
+    GLU applied to the activation as it is read (act = the per-slot gate/up
+    rows [T*k, 2K] of the first GEMV; out [T*k, N])."""
     _req(topk_ids, "topk_ids", (torch.int32,))
     T, k = topk_ids.shape
     _req(act, "act", _BF16)
-    K = act.shape[1]
-    _req(act, "act", _BF16, ((T * k) if act_per_slot else T, K))
+    if glu and glu_on_load:
+        raise ValueError("glu and glu_on_load are exclusive")
+    if glu_on_load:
+        if not act_per_slot:
+            raise ValueError("glu_on_load takes per-slot gate/up rows")
+        K = act.shape[1] // 2
+        _req(act, "act", _BF16, (T * k, 2 * K))
+    else:
+        K = act.shape[1]
+        _req(act, "act", _BF16, ((T * k) if act_per_slot else T, K))
     _req(w, "w", (torch.uint8,))
     N = w.shape[1]
     if wfmt == "fp8":
@@ -459,9 +471,10 @@ def moe_sparse_gemv(act, act_per_slot: bool, topk_ids, expert_start: int, E_loca
     _req(out, "out", _BF16, (T * k, N // 2 if glu else N))
     if slot_row is not None:
         _req(slot_row, "slot_row", (torch.int32,), (T * k,))
+    mode = 2 if glu_on_load else int(bool(glu))
     st = lib().moe_sparse_gemv(_ptr(act), int(bool(act_per_slot)), _ptr(topk_ids), T, k,
                                expert_start, E_local, N, K, WFMT[wfmt], _ptr(w), _ptr(w_scale),
-                               _ptr(bias), int(bool(glu)), float(glu_alpha), float(glu_beta),
+                               _ptr(bias), mode, float(glu_alpha), float(glu_beta),
                                float(glu_limit), _ptr(out), _ptr(slot_row), _stream())
     check(st, "moe_sparse_gemv")
 

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 10
+    assert lib.moe_abi_version() == 11
     for s in range(0, -10, -1):
         assert lib.moe_status_string(s).decode()
     assert lib.moe_status_string(5).decode() == "unknown status"
@@ -166,6 +166,16 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
     assert lib.moe_sparse_gemv(NULL, 0, NULL, 1, 4, 0, 32, 5760, 2880, 3, NULL, NULL, NULL, 1,
                                ctypes.c_float(1.702), ctypes.c_float(1.0), ctypes.c_float(7.0),
                                NULL, NULL, NULL) == -5
+    # GLU mode outside 0..2; GLU on load needs per-slot activation rows
+    assert lib.moe_sparse_gemv(NULL, 1, NULL, 1, 4, 0, 32, 2880, 2880, 0, NULL, NULL, NULL, 3,
+                               ctypes.c_float(1.702), ctypes.c_float(1.0), ctypes.c_float(7.0),
+                               NULL, NULL, NULL) == -5
+    assert lib.moe_sparse_gemv(NULL, 0, NULL, 1, 4, 0, 32, 2880, 2880, 0, NULL, NULL, NULL, 2,
+                               ctypes.c_float(1.702), ctypes.c_float(1.0), ctypes.c_float(7.0),
+                               NULL, NULL, NULL) == -5
+    assert lib.moe_sparse_gemv(NULL, 1, NULL, 1, 4, 0, 32, 2880, 2880, 0, NULL, NULL, NULL, 2,
+                               ctypes.c_float(1.702), ctypes.c_float(1.0), ctypes.c_float(7.0),
+                               NULL, NULL, NULL) == -1
 
 
 def test_hip_side_sigmoid_table_equals_oracle(tmp_path):

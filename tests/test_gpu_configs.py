@@ -205,6 +205,13 @@ def test_decode_exact_config(ops, wfmt, T):
         a_got = F.bf16_to_f32(act[q]).astype(np.float64)
         assert np.all(np.abs(a_got - a_ref) <= _bf16_step(a_ref))
 
+    say("  GLU on load: down over the gate_up rows equals down over the fused GLU's rows")
+    dn2 = torch.full((T * c.k, H), BF16_SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    gu_d = torch.from_numpy(gu.view(np.int16)).cuda().view(torch.bfloat16)
+    ops.moe_sparse_gemv(gu_d, True, ids_d, 0, 32, wfmt, dw[3], dw[4], dw[5], dn2, None,
+                        glu_on_load=True)
+    assert np.array_equal(host(dn2), down)
+
     say("  down GEMV from the GPU's activations within the derived bound")
     for (t, s) in ref.down:
         e, q = int(ids[t, s]), t * c.k + s
