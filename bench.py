@@ -25,6 +25,7 @@ The same line carries:
   decode        the sparse decode layer at 1 and 8 tokens (FP8 and MXFP4):
                 per-kernel cold durations and the graph-replayed layer
   masked        the headline layer on the masked (E, m_pad, K) slab layout
+  natural_weights  GEMM1 + act-quant and GEMM2 on checkpoint-layout weights
   cpu_baseline  the CPU oracle on the host: the headline layer on all threads
                 (the value) and, per workload, on one thread and on all
 
@@ -354,6 +355,7 @@ def main():
         result["decode"] = bench_decode(ops, torch, up, up_bf16, log)
         result["masked"] = bench_masked(ops, torch, up, up_bf16, log, c, ids, wts, logits_own,
                                         own_ids, own_w, fused)
+        result["natural_weights"] = bench_natural(ops, torch, up, up_bf16, log, c, ids)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c, log)
     print(json.dumps(result), flush=True)
@@ -495,6 +497,49 @@ def bench_masked(ops, torch, up, up_bf16, log, c, ids, wts, logits_own, own_ids,
     del scratch, w13, s13, w2, s2, x
     torch.cuda.empty_cache()
     return out
+
+
+def bench_natural(ops, torch, up, up_bf16, log, c, ids, steps=20):
+    """The EP-share layer's GEMM1 + act-quant and GEMM2 on checkpoint-layout
+    weights (no load-time packing), cold, beside the packed forms in the
+    same loop: per-kernel HIP-event durations."""
+    w = c.weights
+    x = up_bf16(c.x)
+    buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I)
+    ops.moe_scatter_endpoints(ids, 0, c.E_local, c.A, x, buf.expert_ends, buf.route_row, buf.xq,
+                              buf.xs, buf.workspace)
+    w13, s13, w2, s2 = up(w.w13), up(w.s13), up(w.w2), up(w.s2)
+    g13, gs13 = ops.moe_pack_mx_weights_gateup(w13, s13)
+    p2, ps2 = ops.moe_pack_mx_weights(w2, s2)
+    calls = {
+        "gemm1_act_packed": lambda: ops.moe_grouped_gemm1_act_quant(
+            buf.xq, buf.xs, buf.expert_ends, c.A, g13, gs13, 0.0, buf.hq, buf.hs),
+        "gemm1_act_natural": lambda: ops.moe_grouped_gemm1_act_quant_natural(
+            buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13, 0.0, buf.hq, buf.hs),
+        "gemm2_packed": lambda: ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, p2,
+                                                      ps2, buf.down),
+        "gemm2_natural": lambda: ops.moe_grouped_gemm2_natural(buf.hq, buf.hs, buf.expert_ends,
+                                                               c.A, w2, s2, buf.down),
+    }
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, call in calls.items():
+        for _ in range(3):
+            call()
+        ts = []
+        for _ in range(steps):
+            _flush_caches(torch, scratch)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        out[name] = round(float(np.median(ts)), 3)
+    log("natural weights (us, cold)", out)
+    del buf, scratch, w13, s13, w2, s2, g13, gs13, p2, ps2, x
+    torch.cuda.empty_cache()
+    return {"kernels_us_cold": out}
 
 
 def _flush_caches(torch, scratch):

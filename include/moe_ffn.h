@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 11
+#define MOE_ABI_VERSION 12
 
 enum moe_status {
     MOE_OK = 0,
@@ -329,6 +329,35 @@ int moe_grouped_gemm2(const uint8_t* hq, const int32_t* hs, const int32_t* exper
                       int E_local, int A, int M_cap, int I, int H,
                       const uint8_t* w2_packed, const uint8_t* w2_scale_packed,
                       uint16_t* down, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Natural-weight forms: moe_grouped_gemm1, moe_grouped_gemm2 and
+ * moe_grouped_gemm1_act_quant taking the weights in their checkpoint layout
+ * instead of the packed one, so that no load-time preparation is needed.
+ * [SGL] sections 2.3 and 3.3 (the contiguous grouped GEMM's rhs is
+ * (E, N, K//2) packed fp4 with (E, N, K//32) E8M0 scales); [KIMI] checkpoint
+ * contract (w13 rows [gate; up]).
+ *
+ *   w13, w13_scale  u8 [E_local, 2I, H/2] (two E2M1 codes per byte, low
+ *                   nibble = even column; rows 0..I-1 gate, I..2I-1 up) and
+ *                   u8 [E_local, 2I, H/32] (E8M0)
+ *   w2, w2_scale    u8 [E_local, H, I/2] and u8 [E_local, H, I/32]
+ * Every other argument, requirement, output and error as in the packed
+ * forms, whose results these reproduce bit for bit (the same products are
+ * summed in the same order; only where the weight bytes are read from
+ * differs). The packed forms stay the faster path for repeated calls.
+ * ------------------------------------------------------------------------ */
+int moe_grouped_gemm1_natural(const uint8_t* xq, const int32_t* xs, const int32_t* expert_ends,
+                              int E_local, int A, int M_cap, int H, int I, const uint8_t* w13,
+                              const uint8_t* w13_scale, uint16_t* gateup, void* stream);
+int moe_grouped_gemm2_natural(const uint8_t* hq, const int32_t* hs, const int32_t* expert_ends,
+                              int E_local, int A, int M_cap, int I, int H, const uint8_t* w2,
+                              const uint8_t* w2_scale, uint16_t* down, void* stream);
+int moe_grouped_gemm1_act_quant_natural(const uint8_t* xq, const int32_t* xs,
+                                        const int32_t* expert_ends, int E_local, int A,
+                                        int M_cap, int H, int I, const uint8_t* w13,
+                                        const uint8_t* w13_scale, float clamp_limit,
+                                        uint8_t* hq, int32_t* hs, void* stream);
 
 /* ------------------------------------------------------------------------
  * Group-128 activation recipe: the four entry points below are the group-32

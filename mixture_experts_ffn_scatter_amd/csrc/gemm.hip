@@ -192,10 +192,28 @@ struct GemmActOut {
 
 static_assert(kGemmBN == 256 && kGemmCB == 4, "the fused epilogue pairs 2 gate and 2 up blocks per wave");
 
+// With half > 0 (the gate/up form of w13, half = I/16 gate column blocks)
+// packed column block p takes source block src_cb(p): in each group of 16
+// (one 256-column tile), position 4cg + k holds gate block 8nt + 2cg + k for
+// k < 2 and the matching up block half + 8nt + 2cg + (k - 2) for k >= 2.
+__device__ __forceinline__ int src_cb(int p, int half) {
+  if (half == 0) return p;
+  const int nt = p >> 4, l = p & 15, cg = l >> 2, k = l & 3;
+  return (k < 2 ? 0 : half) + 8 * nt + 2 * cg + (k & 1);
+}
+
 // XG128: activation scales of one UE8M0 byte per 128 columns, packed four
 // k-steps to a word ([ceil(K/512)][M_cap]); the byte of k-step ks is byte
 // ks % 4 of word ks / 4 and serves all four 32-column blocks of the step.
-template <bool ACT, bool XG128>
+// NATW: the weights in their checkpoint layout (codes [E][N][K/2], scales
+// [E][N][K/32]) instead of the packed one. Each lane's 16 code bytes of a
+// k-step are then the 64-byte run [64 ks + 16 (l/16), +16) of row
+// 16 cb + l%16 (the packed chunk is exactly these bytes, so the LDS stage is
+// the same), and the tile's scales of a k-step are one dword per weight row
+// (its 4 groups), moved by waves 2-5 and gathered into the MFMA's scale word
+// by 4 byte reads. With ACT the gate/up interleaving of the packed form is
+// an address mapping (src_cb).
+template <bool ACT, bool XG128, bool NATW>
 __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gemm_kernel(
     const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
     const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int slab, int K, int N,
@@ -358,10 +376,18 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     T.cb0 = nt * (kGemmBN / 16);
     T.ncb = min(kGemmBN / 16, NB - T.cb0);
   };
+  // weight column block of packed position p (the gate/up interleave of the
+  // fused form; identity otherwise)
+  const int half = ACT ? act.I / 16 : 0;
   auto sources = [&](const GemmTile& T, bool live) {
     GemmSrc q;
-    q.wr = make_rsrc(Wp + ((size_t)T.e * NB + T.cb0) * KS * 1024, (uint32_t)(T.ncb * KS) * 1024u);
-    q.sr = make_rsrc(Sp + (size_t)T.e * KS * NB * 64, (uint32_t)(KS * NB) * 64u);
+    if constexpr (NATW) {
+      q.wr = make_rsrc(Wp + (size_t)T.e * N * (K / 2), (uint32_t)N * (uint32_t)(K / 2));
+      q.sr = make_rsrc(Sp + (size_t)T.e * N * (K / 32), (uint32_t)N * (uint32_t)(K / 32));
+    } else {
+      q.wr = make_rsrc(Wp + ((size_t)T.e * NB + T.cb0) * KS * 1024, (uint32_t)(T.ncb * KS) * 1024u);
+      q.sr = make_rsrc(Sp + (size_t)T.e * KS * NB * 64, (uint32_t)(KS * NB) * 64u);
+    }
     q.xr = make_rsrc(X + (size_t)T.r0 * K, (uint32_t)T.rows * (uint32_t)K);
     // scale word w of row r: [w][r] (aligned layout), [e][w][r - e slab] (slab)
     const size_t xs0 = (slab > 0 ? (size_t)T.e * (size_t)(XW - 1) * (size_t)slab : 0) + T.r0;
@@ -369,12 +395,25 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
 #pragma unroll
     for (int c = 0; c < kDmaCB; ++c) {
       const int cb = kDmaCB * wid + c;
-      q.wo[c] = (live && cb < T.ncb) ? (uint32_t)(cb * KS) * 1024u + lane * 16 : kOob;
+      if constexpr (NATW) {
+        const int src = src_cb(T.cb0 + cb, half);
+        q.wo[c] = (live && cb < T.ncb) ? (uint32_t)(16 * src + l16) * (uint32_t)(K / 2) + 16 * g : kOob;
+      } else {
+        q.wo[c] = (live && cb < T.ncb) ? (uint32_t)(cb * KS) * 1024u + lane * 16 : kOob;
+      }
     }
     q.xo = (live && 16 * kDmaXR * wid < T.rows)
                ? (uint32_t)(16 * kDmaXR * wid + l16) * (uint32_t)K + 16 * g : kOob;
     q.xso = (live && 64 * wid < T.rows) ? (uint32_t)(64 * wid + lane) * 4u : kOob;
-    q.so = live ? (uint32_t)(lane * NB + T.cb0) : kOob;
+    if constexpr (NATW) {
+      // waves 2-5: tile weight row n = 64 (wid - 2) + lane, its 4 groups of the step
+      const int n = 64 * (wid - 2) + lane, cbt = n >> 4;
+      q.so = (live && wid >= 2 && wid < 6 && cbt < T.ncb)
+                 ? (uint32_t)(16 * src_cb(T.cb0 + cbt, half) + (n & 15)) * (uint32_t)(K / 32)
+                 : kOob;
+    } else {
+      q.so = live ? (uint32_t)(lane * NB + T.cb0) : kOob;
+    }
     return q;
   };
 
@@ -386,7 +425,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     constexpr int k = decltype(kk)::value;
     const uint32_t base = lds0 + (uint32_t)sg * (uint32_t)sizeof(GemmStage);
     if constexpr (k < kDmaCB) {
-      dma16(q.wr, q.wo[k] + (uint32_t)st * 1024u, base + kOffW + (kDmaCB * wid + k) * 1024);
+      dma16(q.wr, q.wo[k] + (uint32_t)st * (NATW ? 64u : 1024u), base + kOffW + (kDmaCB * wid + k) * 1024);
     } else if constexpr (k < kDmaOps) {
       constexpr int r = (k - kDmaCB) / 2, h = (k - kDmaCB) % 2;
       dma16(q.xr, q.xo + (uint32_t)(16 * r) * (uint32_t)K + (uint32_t)st * 128u + 64 * h,
@@ -394,6 +433,8 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     } else {
       if (wid < 2) {
         dma4(q.xsr, q.xso + (uint32_t)((XG128 ? st >> 2 : st) * ss) * 4u, base + kOffXs + wid * 256);
+      } else if constexpr (NATW) {
+        if (wid < 6) dma4(q.sr, q.so + (uint32_t)st * 4u, base + kOffWs + (wid - 2) * 256);
       } else if (wid == 2) {
         // the tile's weight-scale line: 64 bytes per column block
         if (kGemmBN / 16 * 4 >= 64 || lane < kGemmBN / 16 * 4)
@@ -417,8 +458,10 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   constexpr int kWaitA = (kGemmStages - 2) * (kDmaOps + 1);
   constexpr int kWaitB = (kGemmStages - 2) * kDmaOps;
   static_assert(kWaitA < 64, "vmcnt field");
+  constexpr int kScaleWaves = NATW ? 6 : 3;   // waves issuing a scale transfer per step
+  static_assert(kGemmWaves >= kScaleWaves, "scale transfers need their waves");
   auto wait_stage = [&]() {
-    if (wid < 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitA) : "memory");
+    if (wid < kScaleWaves) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitA) : "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitB) : "memory");
   };
 
@@ -476,7 +519,18 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       for (int c = 0; c < kGemmCB; ++c)
         af[c] = *reinterpret_cast<const v4i*>(&S.w[kGemmCB * cg + c][lane * 16]);
       static_assert(kGemmCB == 4, "one scale word covers the wave's 4 column blocks");
-      const int sa = (int)*reinterpret_cast<const uint32_t*>(&S.ws[lane][kGemmCB * cg]);
+      int sa;
+      if constexpr (NATW) {
+        // byte g of tile row 16 (4 cg + c) + l16's dword, for c = 0..3
+        const uint8_t* wsb = &S.ws[0][0];
+        uint32_t v = 0;
+#pragma unroll
+        for (int c = 0; c < kGemmCB; ++c)
+          v |= (uint32_t)wsb[(16 * (kGemmCB * cg + c) + l16) * 4 + g] << (8 * c);
+        sa = (int)v;
+      } else {
+        sa = (int)*reinterpret_cast<const uint32_t*>(&S.ws[lane][kGemmCB * cg]);
+      }
       // the scale words of the lane's row in every row block (two per LDS
       // read); k-block g is byte g, moved to byte 0 for the MFMA
       uint32_t xw[kGemmMB];
@@ -655,16 +709,6 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
 //          byte cb of lane row (e, ks, l) = group 4ks + l/16 of row 16cb + l%16
 // One wave per 1 KB code chunk; one thread per scale byte.
 //
-// With half > 0 (the gate/up form of w13, half = I/16 gate column blocks)
-// packed column block p takes source block src_cb(p): in each group of 16
-// (one 256-column tile), position 4cg + k holds gate block 8nt + 2cg + k for
-// k < 2 and the matching up block half + 8nt + 2cg + (k - 2) for k >= 2.
-__device__ __forceinline__ int src_cb(int p, int half) {
-  if (half == 0) return p;
-  const int nt = p >> 4, l = p & 15, cg = l >> 2, k = l & 3;
-  return (k < 2 ? 0 : half) + 8 * nt + 2 * cg + (k & 1);
-}
-
 __global__ __launch_bounds__(256) void pack_mx_codes_kernel(const uint8_t* __restrict__ w, int N,
                                                             int K, int half, uint8_t* __restrict__ wp) {
   const int KS = K / 128;
@@ -702,7 +746,7 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
                                int E_local, int A, int M_cap, int K, int N, const uint8_t* Wp,
                                const uint8_t* Sp, uint16_t* out, void* stream,
                                const GemmActOut* act = nullptr, bool xg128 = false,
-                               int slab = 0) {
+                               int slab = 0, bool natw = false) {
   if (E_local < 0 || E_local > kGemmMaxE || A < 1 || M_cap < 0 || K <= 0 || N <= 0)
     return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 128 != 0 || M_cap % 4 != 0) return MOE_ERR_ALIGN;
@@ -721,13 +765,17 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
   const int resident = 256 * kGemmBlocksPerCU;
   int grid = max_items < resident ? (int)max_items : resident;
   grid = (grid + 7) & ~7;
+  if (natw && xg128) return MOE_ERR_UNSUPPORTED;   // natural weights with group-32 activations only
   if (act) {
     if (xg128) return MOE_ERR_UNSUPPORTED;   // the fused epilogue quantises per 32 columns
-    hipLaunchKernelGGL((grouped_mx_gemm_kernel<true, false>), dim3(grid), dim3(kGemmThreads), 0,
+    auto kernel = natw ? grouped_mx_gemm_kernel<true, false, true> : grouped_mx_gemm_kernel<true, false, false>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kGemmThreads), 0,
                        (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out,
                        *act);
   } else {
-    auto kernel = xg128 ? grouped_mx_gemm_kernel<false, true> : grouped_mx_gemm_kernel<false, false>;
+    auto kernel = natw ? grouped_mx_gemm_kernel<false, false, true>
+                  : xg128 ? grouped_mx_gemm_kernel<false, true, false>
+                          : grouped_mx_gemm_kernel<false, false, false>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kGemmThreads), 0, (hipStream_t)stream, X, Xs,
                        ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out,
                        GemmActOut{nullptr, nullptr, 0, 0.f});
@@ -894,4 +942,37 @@ extern "C" int moe_grouped_gemm1_act_quant_masked(const uint8_t* xq, const int32
   return moe::launch_grouped_gemm(xq, xs, masked_m, E_local, 1, M_cap, H, 2 * I,
                                   w13_gateup_packed, w13_gateup_scale_packed, nullptr, stream,
                                   &act, false, m_pad);
+}
+
+extern "C" int moe_grouped_gemm1_natural(const uint8_t* xq, const int32_t* xs,
+                                         const int32_t* expert_ends, int E_local, int A,
+                                         int M_cap, int H, int I, const uint8_t* w13,
+                                         const uint8_t* w13_scale, uint16_t* gateup,
+                                         void* stream) {
+  if (I <= 0 || I % 64 != 0) return MOE_ERR_ALIGN;
+  return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I, w13,
+                                  w13_scale, gateup, stream, nullptr, false, 0, true);
+}
+
+extern "C" int moe_grouped_gemm2_natural(const uint8_t* hq, const int32_t* hs,
+                                         const int32_t* expert_ends, int E_local, int A,
+                                         int M_cap, int I, int H, const uint8_t* w2,
+                                         const uint8_t* w2_scale, uint16_t* down, void* stream) {
+  return moe::launch_grouped_gemm(hq, hs, expert_ends, E_local, A, M_cap, I, H, w2, w2_scale,
+                                  down, stream, nullptr, false, 0, true);
+}
+
+extern "C" int moe_grouped_gemm1_act_quant_natural(const uint8_t* xq, const int32_t* xs,
+                                                   const int32_t* expert_ends, int E_local, int A,
+                                                   int M_cap, int H, int I, const uint8_t* w13,
+                                                   const uint8_t* w13_scale, float clamp_limit,
+                                                   uint8_t* hq, int32_t* hs, void* stream) {
+  if (I <= 0 || I % 128 != 0) return MOE_ERR_ALIGN;
+  float L;
+  if (fused_clamp(clamp_limit, L) != MOE_OK) return MOE_ERR_UNSUPPORTED;
+  if ((long long)M_cap * I >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (E_local > 0 && M_cap > 0 && (!hq || !hs)) return MOE_ERR_NULL;
+  const moe::GemmActOut act{hq, hs, I, L};
+  return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I, w13,
+                                  w13_scale, nullptr, stream, &act, false, 0, true);
 }

@@ -292,6 +292,60 @@ def moe_grouped_gemm2(hq, hs, expert_ends, A: int, w2_packed, w2_scale_packed, d
     check(st, "moe_grouped_gemm2" + ("" if group == 32 else "_g128"))
 
 
+# ------------------------------------------- GEMMs on the checkpoint layout
+
+def moe_grouped_gemm1_natural(xq, xs, expert_ends, A: int, w13, w13_scale, gateup):
+    """moe_grouped_gemm1 with w13 u8 [E, 2I, H/2] and its scales u8
+    [E, 2I, H/32] as stored in the checkpoint (no packing)."""
+    M_cap, H = xq.shape
+    E_local, twoI, _ = w13.shape
+    I = twoI // 2
+    _req(xq, "xq", (torch.uint8,))
+    _req(xs, "xs", (torch.int32,), (H // 128, M_cap))
+    _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
+    _req(w13, "w13", (torch.uint8,), (E_local, 2 * I, H // 2))
+    _req(w13_scale, "w13_scale", (torch.uint8,), (E_local, 2 * I, H // 32))
+    _req(gateup, "gateup", _BF16, (M_cap, 2 * I))
+    st = lib().moe_grouped_gemm1_natural(_ptr(xq), _ptr(xs), _ptr(expert_ends), E_local, A, M_cap,
+                                         H, I, _ptr(w13), _ptr(w13_scale), _ptr(gateup), _stream())
+    check(st, "moe_grouped_gemm1_natural")
+
+
+def moe_grouped_gemm2_natural(hq, hs, expert_ends, A: int, w2, w2_scale, down):
+    """moe_grouped_gemm2 with w2 u8 [E, H, I/2] and its scales u8 [E, H, I/32]."""
+    M_cap, I = hq.shape
+    E_local, H, _ = w2.shape
+    _req(hq, "hq", (torch.uint8,))
+    _req(hs, "hs", (torch.int32,), (I // 128, M_cap))
+    _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
+    _req(w2, "w2", (torch.uint8,), (E_local, H, I // 2))
+    _req(w2_scale, "w2_scale", (torch.uint8,), (E_local, H, I // 32))
+    _req(down, "down", _BF16, (M_cap, H))
+    st = lib().moe_grouped_gemm2_natural(_ptr(hq), _ptr(hs), _ptr(expert_ends), E_local, A, M_cap,
+                                         I, H, _ptr(w2), _ptr(w2_scale), _ptr(down), _stream())
+    check(st, "moe_grouped_gemm2_natural")
+
+
+def moe_grouped_gemm1_act_quant_natural(xq, xs, expert_ends, A: int, w13, w13_scale,
+                                        clamp_limit: float, hq, hs):
+    """moe_grouped_gemm1_act_quant with the checkpoint-layout w13 and scales."""
+    M_cap, H = xq.shape
+    E_local, twoI, _ = w13.shape
+    I = twoI // 2
+    _req(xq, "xq", (torch.uint8,))
+    _req(xs, "xs", (torch.int32,), (H // 128, M_cap))
+    _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
+    _req(w13, "w13", (torch.uint8,), (E_local, 2 * I, H // 2))
+    _req(w13_scale, "w13_scale", (torch.uint8,), (E_local, 2 * I, H // 32))
+    _req(hq, "hq", (torch.uint8,), (M_cap, I))
+    _req(hs, "hs", (torch.int32,), (I // 128, M_cap))
+    st = lib().moe_grouped_gemm1_act_quant_natural(_ptr(xq), _ptr(xs), _ptr(expert_ends), E_local,
+                                                   A, M_cap, H, I, _ptr(w13), _ptr(w13_scale),
+                                                   float(clamp_limit), _ptr(hq), _ptr(hs),
+                                                   _stream())
+    check(st, "moe_grouped_gemm1_act_quant_natural")
+
+
 # ------------------------------------------------- masked (E, m_pad, K) slab
 
 @dataclass

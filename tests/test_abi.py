@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 11
+    assert lib.moe_abi_version() == 12
     for s in range(0, -10, -1):
         assert lib.moe_status_string(s).decode()
     assert lib.moe_status_string(5).decode() == "unknown status"
@@ -125,6 +125,14 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 200, 128, NULL, NULL, NULL) == -3
     assert lib.moe_pack_mx_weights(NULL, NULL, 0, 256, 128, NULL, NULL, NULL) == 0
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 256, 128, NULL, NULL, NULL) == -1
+    # natural-weight GEMMs: the packed forms' checks
+    assert lib.moe_grouped_gemm1_natural(NULL, NULL, NULL, 8, 128, 1152, 192, 128, NULL, NULL,
+                                         NULL, NULL) == -3
+    assert lib.moe_grouped_gemm2_natural(NULL, NULL, NULL, 8, 128, 1152, 256, 256, NULL, NULL,
+                                         NULL, NULL) == -1
+    assert lib.moe_grouped_gemm1_act_quant_natural(NULL, NULL, NULL, 8, 128, 1152, 256, 128,
+                                                   NULL, NULL, ctypes.c_float(7.3), NULL, NULL,
+                                                   NULL) == -5
     # masked slab forms: m_pad not a multiple of 4, E_local * m_pad too
     # large, m_pad 0 with experts (scatter), then the aligned forms' checks
     ms = [NULL, 64, 2, 0, 8, 130, NULL, 256, NULL, NULL, NULL, NULL, NULL, 0, NULL]
