@@ -310,8 +310,8 @@ def main():
     dom = "gemm1_act" if fused else "gemm1"
     ach = bytes_[dom] / (dur_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm",
-                "kernel": ("grouped_mx_gemm_kernel<true, false> (moe_grouped_gemm1_act_quant)" if fused
-                           else "grouped_mx_gemm_kernel<false, false> (moe_grouped_gemm1)"),
+                "kernel": ("grouped_mx_gemm_kernel<true, false, false> (moe_grouped_gemm1_act_quant)" if fused
+                           else "grouped_mx_gemm_kernel<false, false, false> (moe_grouped_gemm1)"),
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
                 "alg_bytes_per_launch": int(bytes_[dom]), "avg_launch_us": round(dur_us[dom], 3)}
