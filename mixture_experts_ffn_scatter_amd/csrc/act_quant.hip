@@ -10,10 +10,12 @@
 // Work decomposition: the live rows are numbered 0..R-1 in layout order
 // (expert by expert, from the endpoints) and split evenly over one block of
 // 8 waves per CU, so padding rows are never visited. A block's rows are cut
-// into (row, 512-column chunk) items, taken 64 at a time (8 per wave); the
+// into (row, 512-column chunk) items, taken 16 at a time (2 per wave); the
 // next batch's loads are issued before the current batch is computed
-// (registers double-buffered), and the sigmoid table's loads go out before
-// any of them. A lane owns 8 consecutive columns of a chunk (16-byte loads
+// (registers double-buffered), so the math of one batch overlaps the loads
+// of the next (a block's 48 items at the EP-share shapes are 3 batches per
+// wave, where 8-item batches made one batch and no overlap), and the
+// sigmoid table's loads go out before any of them. A lane owns 8 consecutive columns of a chunk (16-byte loads
 // of gate and up, 8-byte stores of codes), a 32-column group spans 4 lanes
 // (amax by two shuffles), a packed scale word spans 16 lanes and is stored
 // by its first lane (MN-major).
@@ -64,7 +66,8 @@ __device__ __forceinline__ float scaled_tanh_lookup(const float* tab, float x, f
 
 constexpr int kActThreads = 512;   // 8 waves
 constexpr int kActWaves = kActThreads / 64;
-constexpr int kActBatch = 8;       // items per wave per batch
+constexpr int kActBatch = 2;       // items per wave per batch (double-buffered: small batches
+                                   // let one batch's math overlap the next one's loads)
 constexpr int kActMaxE = 1024;
 constexpr int kActMaxWordsPerRow = 64;  // I <= 8192
 // live rows per block (M_cap <= 256 * 12288); the 48 KB this takes also keeps
