@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 12
+#define MOE_ABI_VERSION 13
 
 enum moe_status {
     MOE_OK = 0,
@@ -192,11 +192,13 @@ int moe_scatter_endpoints_noalloc(const int32_t* topk_ids, int T, int k, int exp
  *                   k-step ks = k/128 a 1 KB chunk at ((e*N/16 + cb)*K/128 + ks)*1024
  *                   whose 16 bytes at lane*16 are bytes [64ks + 16(lane/16), +16)
  *                   of row 16cb + lane%16
- *   w_scale_packed  u8, E*(K/128)*64*(N/16) bytes (= E*N*K/32), out: for k-step
- *                   ks and lane l (0..63) a row of N/16 bytes at
- *                   ((e*K/128 + ks)*64 + l)*N/16 whose byte cb is the E8M0
- *                   byte of group 4ks + l/16 of row 16cb + l%16
- * Pure data movement (bit-exact). Requires K % 128 == 0, N % 16 == 0,
+ *   w_scale_packed  u8, E*(K/128)*(N/64)*256 bytes (= E*N*K/32), out: for
+ *                   k-step ks, group q of 4 column blocks and lane l (0..63)
+ *                   a 4-byte word at (((e*K/128 + ks)*N/64 + q)*64 + l)*4
+ *                   whose byte b is the E8M0 byte of group 4ks + l/16 of row
+ *                   16(4q + b) + l%16 (a wave's 4 column blocks of one step
+ *                   are 256 contiguous bytes)
+ * Pure data movement (bit-exact). Requires K % 128 == 0, N % 64 == 0,
  * E <= 65535. The caller owns all four buffers; the packed buffers are what
  * moe_grouped_gemm1 / moe_grouped_gemm2 take.
  * ------------------------------------------------------------------------ */

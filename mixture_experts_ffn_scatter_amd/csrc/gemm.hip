@@ -27,10 +27,11 @@
 // (sglang)", section 2.1: weights are rearranged into the layout the GEMM
 // consumes, so that the run-time GEMM never touches the checkpoint layout):
 // codes are stored in MFMA fragment order, one contiguous 1 KB chunk per
-// (16-column block, 128-wide k-step), and scales per (k-step, lane) as one
-// row of N/16 bytes (the byte lane l of the MFMA needs for each column
-// block), so that one k-step of a 256-column tile's scales is 16 contiguous
-// bytes per lane and a wave reads its 4 column blocks' scales as one word.
+// (16-column block, 128-wide k-step), and scales per (k-step, group of 4
+// column blocks) as 64 lane words (byte c of lane l's word: the byte lane l
+// of the MFMA needs for column block 4q + c), so that one k-step of a
+// 256-column tile's scales is one contiguous 1 KB block and a wave reads
+// its 4 column blocks' scales as one word.
 //
 // Work decomposition. An item is (expert, n-tile of 256 columns, m-chunk of
 // up to 128 live rows); its cost grows with its live row blocks (a full
@@ -112,7 +113,8 @@ constexpr int kDmaOps = kDmaCB + 2 * kDmaXR;
 //             of row 16mb + l%16 at k 64h + 16(l/16))
 //   w[cb]:    weight codes of column block cb in A-fragment order
 //   xs[row]:  the row's 4 UE8M0 bytes (k-blocks 0..3 of the step)
-//   ws[l]:    lane l's E8M0 bytes of the tile's 16 column blocks
+//   ws:       the tile's weight scales: for column-block group q (4 blocks)
+//             lane l's 4 E8M0 bytes at 256 q + 4 l (byte c: block 4q + c)
 struct __attribute__((aligned(16))) GemmStage {
   uint8_t x[kGemmBM / 16][2][1024];
   uint8_t w[kGemmBN / 16][1024];
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
                  ? (uint32_t)(16 * src_cb(T.cb0 + cbt, half) + (n & 15)) * (uint32_t)(K / 32)
                  : kOob;
     } else {
-      q.so = live ? (uint32_t)(lane * NB + T.cb0) : kOob;
+      q.so = live ? (uint32_t)((T.cb0 >> 2) * 256 + lane * 16) : kOob;   // the tile's 4 groups
     }
     return q;
   };
@@ -436,9 +438,10 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       } else if constexpr (NATW) {
         if (wid < 6) dma4(q.sr, q.so + (uint32_t)st * 4u, base + kOffWs + (wid - 2) * 256);
       } else if (wid == 2) {
-        // the tile's weight-scale line: 64 bytes per column block
-        if (kGemmBN / 16 * 4 >= 64 || lane < kGemmBN / 16 * 4)
-          dma16(q.sr, q.so + (uint32_t)(st * 64 * NB), base + kOffWs);
+        // the tile's weight scales of the step: 4 groups of 256 bytes, one
+        // contiguous 1 KB block
+        static_assert(kGemmBN / 16 == 16, "one 16-byte transfer per lane covers the tile");
+        dma16(q.sr, q.so + (uint32_t)(st * 64 * NB), base + kOffWs);
       }
     }
   };
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
           v |= (uint32_t)wsb[(16 * (kGemmCB * cg + c) + l16) * 4 + g] << (8 * c);
         sa = (int)v;
       } else {
-        sa = (int)*reinterpret_cast<const uint32_t*>(&S.ws[lane][kGemmCB * cg]);
+        sa = (int)*reinterpret_cast<const uint32_t*>(&S.ws[0][0] + 256 * cg + 4 * lane);
       }
       // the scale words of the lane's row in every row block (two per LDS
       // read); k-block g is byte g, moved to byte 0 for the MFMA
@@ -705,8 +708,9 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
 // Load-time weight preparation (bit-exact data movement):
 //   codes  w [E][N][K/2] -> wp [E][N/16][K/128][64 lanes][16 B]
 //          lane l of chunk (e, cb, ks) = bytes [64ks + 16(l/16), +16) of row 16cb + l%16
-//   scales s [E][N][K/32] -> sp [E][K/128][64 lanes][N/16]
-//          byte cb of lane row (e, ks, l) = group 4ks + l/16 of row 16cb + l%16
+//   scales s [E][N][K/32] -> sp [E][K/128][N/64][64 lanes][4 B]
+//          byte b of lane l's word of group q in (e, ks) = group 4ks + l/16 of
+//          row 16(4q + b) + l%16
 // One wave per 1 KB code chunk; one thread per scale byte.
 //
 __global__ __launch_bounds__(256) void pack_mx_codes_kernel(const uint8_t* __restrict__ w, int N,
@@ -732,10 +736,13 @@ __global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __re
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= per_e) return;
   const int e = blockIdx.y;
-  const size_t line = idx / NB;                  // ks * 64 + lane
-  const int cb = (int)(idx - line * NB);
-  const int l = (int)(line & 63);
-  const int ks = (int)(line >> 6);
+  // idx = ((ks * NB/4 + q) * 64 + l) * 4 + b: byte b of lane l's word of
+  // column-block group q (block 4q + b) in k-step ks
+  const int b = (int)(idx & 3);
+  const int l = (int)((idx >> 2) & 63);
+  const size_t gq = idx >> 8;                    // ks * NB/4 + q
+  const int ks = (int)(gq / (NB / 4));
+  const int cb = 4 * (int)(gq - (size_t)ks * (NB / 4)) + b;
   sp[(size_t)e * per_e + idx] =
       s[((size_t)e * N + 16 * src_cb(cb, half) + (l & 15)) * (size_t)(K / 32) + 4 * ks + (l >> 4)];
 }
@@ -787,7 +794,7 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
 static int pack_mx(const uint8_t* w, const uint8_t* w_scale, int E, int N, int K, int half,
                    uint8_t* w_packed, uint8_t* w_scale_packed, void* stream) {
   if (E < 0 || N < 0 || K <= 0 || E > 65535) return MOE_ERR_SHAPE;
-  if (K % 128 != 0 || N % 16 != 0) return MOE_ERR_ALIGN;
+  if (K % 128 != 0 || N % 64 != 0) return MOE_ERR_ALIGN;
   if (E == 0 || N == 0) return MOE_OK;
   if (!w || !w_scale || !w_packed || !w_scale_packed) return MOE_ERR_NULL;
   const size_t chunks = (size_t)(N / 16) * (K / 128);

@@ -175,13 +175,14 @@ def moe_scatter_endpoints_noalloc(topk_ids, expert_start: int, E_local: int, A: 
 # ------------------------------------------------------------------ GEMMs
 
 def packed_scale_shape(E: int, N: int, K: int):
-    return (E, K // 128, 64, N // 16)
+    return (E, K // 128, N // 64, 64, 4)
 
 
 def moe_pack_mx_weights(w, w_scale):
     """Load-time weight preparation: MXFP4 codes u8 [E, N, K/2] and E8M0
     scales u8 [E, N, K/32] -> (codes in fragment order, same shape [E, N, K/2];
-    scales u8 [E, K/128, 64, N/16]), the operands of the grouped GEMMs."""
+    scales u8 [E, K/128, N/64, 64, 4]: per k-step and group of 4 column
+    blocks, one 4-byte word per MFMA lane), the operands of the grouped GEMMs."""
     _req(w, "w", (torch.uint8,))
     E, N, K2 = w.shape
     K = 2 * K2

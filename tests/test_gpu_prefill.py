@@ -442,21 +442,22 @@ def _expected_packing(w, s):
     KS = K // 128
     lane = np.arange(64)
     wp = np.empty((E, N // 16, KS, 64, 16), np.uint8)
-    sp = np.empty((E, KS, 64, N // 16), np.uint8)
+    sp = np.empty((E, KS, N // 64, 64, 4), np.uint8)
     for cb in range(N // 16):
         rows = 16 * cb + lane % 16
         for ks in range(KS):
             cols = 64 * ks + 16 * (lane // 16)
             wp[:, cb, ks] = w[:, rows[:, None], cols[:, None] + np.arange(16)[None, :]]
-            sp[:, ks, :, cb] = s[:, rows, 4 * ks + lane // 16]
+            # byte cb % 4 of lane l's word of column-block group cb // 4
+            sp[:, ks, cb // 4, :, cb % 4] = s[:, rows, 4 * ks + lane // 16]
     return wp.reshape(E, N, K2), sp
 
 
 def test_pack_mx_weights_bitexact(ops):
     """Load-time weight preparation is pure data movement into the documented
-    fragment order (codes) and per-step lane lines (scales)."""
+    fragment order (codes) and per-step, per-group lane words (scales)."""
     rng = np.random.default_rng(2024)
-    for E, N, K in ((3, 48, 384), (1, 128, 128), (2, 256, 2048), (1, 64, 1152)):
+    for E, N, K in ((3, 192, 384), (1, 128, 128), (2, 256, 2048), (1, 64, 1152)):
         say(f"pack mx weights E={E} N={N} K={K}")
         w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
         s = rng.integers(0, 256, size=(E, N, K // 32), dtype=np.uint8)
