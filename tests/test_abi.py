@@ -120,9 +120,12 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
                                       NULL) == -3
     assert lib.moe_grouped_gemm2_g128(NULL, NULL, NULL, 8, 128, 1152, 256, 256, NULL, NULL, NULL,
                                       NULL) == -1
-    # weight packing: K not a multiple of 128, N not of 16; empty is a no-op
+    # weight packing: K not a multiple of 128, N not of 64 (the scale words
+    # hold 4 column blocks); empty is a no-op
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 256, 96, NULL, NULL, NULL) == -3
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 200, 128, NULL, NULL, NULL) == -3
+    assert lib.moe_pack_mx_weights(NULL, NULL, 4, 48, 128, NULL, NULL, NULL) == -3
+    assert lib.moe_pack_mx_weights(NULL, NULL, 4, 192, 128, NULL, NULL, NULL) == -1
     assert lib.moe_pack_mx_weights(NULL, NULL, 0, 256, 128, NULL, NULL, NULL) == 0
     assert lib.moe_pack_mx_weights(NULL, NULL, 4, 256, 128, NULL, NULL, NULL) == -1
     # natural-weight GEMMs: the packed forms' checks
