@@ -570,6 +570,23 @@ def moe_ffn_prefill_fused(x, topk_ids, topk_weights, expert_start: int, A: int,
     return buf.out
 
 
+def moe_ffn_prefill_natural(x, topk_ids, topk_weights, expert_start: int, A: int, w13,
+                            w13_scale, w2, w2_scale, buf: GroupedBuffers,
+                            clamp_limit: float = 0.0, routed_scale: float = 1.0):
+    """moe_ffn_prefill_fused on the weights in their checkpoint layout (w13
+    u8 [E, 2I, H/2] with rows [gate; up] and scales [E, 2I, H/32]; w2 u8
+    [E, H, I/2] and [E, H, I/32]): no load-time packing; byte-identical
+    results to the packed fused chain."""
+    E_local = w13.shape[0]
+    moe_scatter_endpoints(topk_ids, expert_start, E_local, A, x, buf.expert_ends, buf.route_row,
+                          buf.xq, buf.xs, buf.workspace)
+    moe_grouped_gemm1_act_quant_natural(buf.xq, buf.xs, buf.expert_ends, A, w13, w13_scale,
+                                        clamp_limit, buf.hq, buf.hs)
+    moe_grouped_gemm2_natural(buf.hq, buf.hs, buf.expert_ends, A, w2, w2_scale, buf.down)
+    moe_combine(buf.down, buf.route_row, topk_weights, routed_scale, buf.out)
+    return buf.out
+
+
 def moe_ffn_prefill_masked(x, topk_ids, topk_weights, expert_start: int, w13_packed,
                            w13_scale_packed, w2_packed, w2_scale_packed, buf: MaskedBuffers,
                            clamp_limit: float = 0.0, routed_scale: float = 1.0,

@@ -10,8 +10,8 @@ import torch
 import workloads as W
 from oracle import formats as F
 from oracle import moe as M
-from tests.gpu_helpers import (BF16_SENT, BYTE_SENT, WORD_SENT, dev, gemm_within_bound, host,
-                               say)
+from tests.gpu_helpers import (BF16_SENT, BYTE_SENT, WORD_SENT, dev, dev_bf16, gemm_within_bound,
+                               host, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,4 +132,31 @@ def test_natural_gemms_equal_packed_ep_share(ops):
         res.append((host(hq), host(hs), host(down)))
         torch.cuda.empty_cache()
     for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("case,clamp,scale", [("tiny", 7.0, 2.5), ("prefill", 0.0, 1.0)])
+def test_natural_chain_equals_fused_chain(ops, case, clamp, scale):
+    """moe_ffn_prefill_natural (checkpoint-layout weights, no packing) equals
+    moe_ffn_prefill_fused on the packed weights in every buffer, byte for byte."""
+    c = W.tiny() if case == "tiny" else W.prefill()
+    w = c.weights
+    ids, wts = M.route_softmax(c.logits, c.k)
+    say(f"natural chain vs fused chain: {case}")
+    outs = []
+    for natural in (False, True):
+        buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, fill=True)
+        if natural:
+            ops.moe_ffn_prefill_natural(dev_bf16(c.x), dev(ids), dev(wts), c.expert_start, c.A,
+                                        dev(w.w13), dev(w.s13), dev(w.w2), dev(w.s2), buf,
+                                        clamp_limit=clamp, routed_scale=scale)
+        else:
+            g = ops.moe_pack_mx_weights_gateup(dev(w.w13), dev(w.s13))
+            d = ops.moe_pack_mx_weights(dev(w.w2), dev(w.s2))
+            ops.moe_ffn_prefill_fused(dev_bf16(c.x), dev(ids), dev(wts), c.expert_start, c.A,
+                                      *g, *d, buf, clamp_limit=clamp, routed_scale=scale)
+        outs.append((host(buf.hq), host(buf.hs), host(buf.down), host(buf.out)))
+        del buf
+        torch.cuda.empty_cache()
+    for a, b in zip(*outs):
         assert np.array_equal(a, b)
