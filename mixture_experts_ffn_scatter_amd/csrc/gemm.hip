@@ -58,6 +58,14 @@
 // of the tile, so per step it reads 4 weight and 4 activation fragments
 // (12 KB of LDS for 16 MFMAs) and issues up to 16 MFMAs, reading the
 // activation fragments two row blocks ahead of the MFMAs that consume them.
+// Every wave issues the same 5 transfers a step (2 weight chunks, 2 halves
+// of an activation row block, one dword of scales), so the step body has no
+// per-wave branch, and they go out in pairs after each row block's MFMAs
+// (pinned by scheduling barriers) rather than queueing at the step's start
+// ahead of them. Steps are software-pipelined across the barrier: a step
+// waits, synchronises and reads the next step's weight fragments, scale
+// words and first activation fragments before its own last row block's
+// MFMAs, so the matrix cores keep working while the block synchronises.
 // Loads use buffer resources whose range ends at the last live row (or
 // column): lanes past it read zeros without touching memory, so
 // padding rows are never read.
@@ -79,9 +87,6 @@ namespace gemm_act {
 
 namespace moe {
 
-#ifndef GEMM_DMA_SPREAD
-#define GEMM_DMA_SPREAD 1
-#endif
 constexpr int kGemmThreads = 512;  // 8 waves
 constexpr int kGemmBN = 256;       // columns per item (16 blocks of 16)
 constexpr int kGemmStages = 4;     // LDS ring depth (k-steps)
@@ -94,18 +99,13 @@ constexpr int kGemmRG = kGemmBM / 16 / kGemmMB;         // row groups of waves
 constexpr int kGemmCG = kGemmBN / 16 / kGemmCB;         // column groups of waves
 constexpr int kDmaCB = kGemmBN / 16 / kGemmWaves;      // weight chunks a wave transfers per step
 constexpr int kDmaXR = kGemmBM / 16 / kGemmWaves;      // activation row blocks a wave transfers
-#ifndef GEMM_RD
-#define GEMM_RD 3
-#endif
-constexpr int kGemmRD = GEMM_RD;   // activation fragments in registers (read-ahead + 1)
 constexpr int kGemmMaxE = 1024;
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: reads zero, no traffic
 static_assert(kGemmRG * kGemmCG == kGemmThreads / 64, "wave grid");
 static_assert(kDmaCB * kGemmWaves == kGemmBN / 16 && kDmaXR * kGemmWaves == kGemmBM / 16,
               "transfers split evenly over the waves");
-static_assert(kGemmWaves >= 3, "waves 0, 1 move the scale words, wave 2 the weight scales");
-// transfers a wave issues per step: its weight chunks, 2 halves of each of
-// its row blocks, plus one scale transfer on waves 0-2
+// transfers a wave issues per step: its weight chunks and 2 halves of each
+// of its row blocks, plus one scale transfer
 constexpr int kDmaOps = kDmaCB + 2 * kDmaXR;
 
 // One LDS stage: everything one k-step of a 128 x 256 tile reads.
@@ -171,11 +171,13 @@ struct GemmTile {
 // One work item's transfer sources. With live false every offset is kOob,
 // which is how an absent item (or a step past the last) is "loaded".
 struct GemmSrc {
-  __amdgpu_buffer_rsrc_t wr, sr, xr, xsr;
+  __amdgpu_buffer_rsrc_t wr, xr;
+  __amdgpu_buffer_rsrc_t sr;   // the wave's scale source: the weight scales (waves 2-5)
+                               // or the rows' activation scale words (the others)
   uint32_t wo[kDmaCB];   // per-lane weight-code offsets of the wave's transferred blocks
   uint32_t xo;           // per-lane activation offset of this wave's first row block
-  uint32_t xso;          // per-lane scale-word offset (waves 0, 1: rows 64 w + lane)
-  uint32_t so;           // per-lane weight-scale offset (wave 2: the tile's 1 KB line)
+  uint32_t so;           // per-lane scale offset at k-step 0
+  uint32_t sstep;        // its advance per k-step (per 4 k-steps for group-128 words)
 };
 
 // The fused GEMM1 epilogue (ACT): the weights are packed with the gate and
@@ -381,19 +383,25 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   // weight column block of packed position p (the gate/up interleave of the
   // fused form; identity otherwise)
   const int half = ACT ? act.I / 16 : 0;
+  // waves 2-5 move the tile's weight scales, the others the rows' scale words
+  const bool wsw = wid >= 2 && wid < 6;
+  const uint32_t s_lds = wsw ? (uint32_t)(kOffWs + (wid - 2) * 256) : (uint32_t)(kOffXs + (wid & 1) * 256);
   auto sources = [&](const GemmTile& T, bool live) {
     GemmSrc q;
     if constexpr (NATW) {
       q.wr = make_rsrc(Wp + (size_t)T.e * N * (K / 2), (uint32_t)N * (uint32_t)(K / 2));
-      q.sr = make_rsrc(Sp + (size_t)T.e * N * (K / 32), (uint32_t)N * (uint32_t)(K / 32));
     } else {
       q.wr = make_rsrc(Wp + ((size_t)T.e * NB + T.cb0) * KS * 1024, (uint32_t)(T.ncb * KS) * 1024u);
-      q.sr = make_rsrc(Sp + (size_t)T.e * KS * NB * 64, (uint32_t)(KS * NB) * 64u);
     }
     q.xr = make_rsrc(X + (size_t)T.r0 * K, (uint32_t)T.rows * (uint32_t)K);
-    // scale word w of row r: [w][r] (aligned layout), [e][w][r - e slab] (slab)
-    const size_t xs0 = (slab > 0 ? (size_t)T.e * (size_t)(XW - 1) * (size_t)slab : 0) + T.r0;
-    q.xsr = make_rsrc(Xs + xs0, (uint32_t)((XW - 1) * ss + T.rows) * 4u);
+    if (wsw) {
+      q.sr = NATW ? make_rsrc(Sp + (size_t)T.e * N * (K / 32), (uint32_t)N * (uint32_t)(K / 32))
+                  : make_rsrc(Sp + (size_t)T.e * KS * NB * 64, (uint32_t)(KS * NB) * 64u);
+    } else {
+      // scale word w of row r: [w][r] (aligned layout), [e][w][r - e slab] (slab)
+      const size_t xs0 = (slab > 0 ? (size_t)T.e * (size_t)(XW - 1) * (size_t)slab : 0) + T.r0;
+      q.sr = make_rsrc(Xs + xs0, (uint32_t)((XW - 1) * ss + T.rows) * 4u);
+    }
 #pragma unroll
     for (int c = 0; c < kDmaCB; ++c) {
       const int cb = kDmaCB * wid + c;
@@ -406,23 +414,30 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     }
     q.xo = (live && 16 * kDmaXR * wid < T.rows)
                ? (uint32_t)(16 * kDmaXR * wid + l16) * (uint32_t)K + 16 * g : kOob;
-    q.xso = (live && 64 * wid < T.rows) ? (uint32_t)(64 * wid + lane) * 4u : kOob;
-    if constexpr (NATW) {
-      // waves 2-5: tile weight row n = 64 (wid - 2) + lane, its 4 groups of the step
+    if (!wsw) {
+      // rows 64 (wid & 1) + lane (waves 6, 7 repeat waves 0, 1)
+      q.so = (live && 64 * (wid & 1) < T.rows) ? (uint32_t)(64 * (wid & 1) + lane) * 4u : kOob;
+      q.sstep = (uint32_t)ss * 4u;
+    } else if constexpr (NATW) {
+      // tile weight row n = 64 (wid - 2) + lane, its 4 groups of the step
       const int n = 64 * (wid - 2) + lane, cbt = n >> 4;
-      q.so = (live && wid >= 2 && wid < 6 && cbt < T.ncb)
+      q.so = (live && cbt < T.ncb)
                  ? (uint32_t)(16 * src_cb(T.cb0 + cbt, half) + (n & 15)) * (uint32_t)(K / 32)
                  : kOob;
+      q.sstep = 4u;
     } else {
-      q.so = live ? (uint32_t)((T.cb0 >> 2) * 256 + lane * 16) : kOob;   // the tile's 4 groups
+      // group wid - 2 of the tile's 4 (256 bytes of one contiguous 1 KB block)
+      q.so = live ? (uint32_t)((T.cb0 >> 2) * 256 + (wid - 2) * 256 + lane * 4) : kOob;
+      q.sstep = (uint32_t)(64 * NB);
     }
     return q;
   };
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)&stage[0];
   // transfers of k-step st of a source into ring stage sg: per wave its 2
-  // weight blocks and the 2 halves of its activation row block; waves 0, 1
-  // the scale words of rows 64 w .. 64 w + 63, wave 2 the weight-scale line
+  // weight blocks, the 2 halves of its activation row block and one dword
+  // per lane of scales (waves 2-5: a quarter of the tile's weight scales;
+  // waves 0, 1: the scale words of rows 64 w .. + 63, repeated by 6, 7)
   auto issue_op = [&](const GemmSrc& q, int st, int sg, auto kk) {
     constexpr int k = decltype(kk)::value;
     const uint32_t base = lds0 + (uint32_t)sg * (uint32_t)sizeof(GemmStage);
@@ -433,16 +448,10 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       dma16(q.xr, q.xo + (uint32_t)(16 * r) * (uint32_t)K + (uint32_t)st * 128u + 64 * h,
             base + (kDmaXR * wid + r) * 2048 + h * 1024);
     } else {
-      if (wid < 2) {
-        dma4(q.xsr, q.xso + (uint32_t)((XG128 ? st >> 2 : st) * ss) * 4u, base + kOffXs + wid * 256);
-      } else if constexpr (NATW) {
-        if (wid < 6) dma4(q.sr, q.so + (uint32_t)st * 4u, base + kOffWs + (wid - 2) * 256);
-      } else if (wid == 2) {
-        // the tile's weight scales of the step: 4 groups of 256 bytes, one
-        // contiguous 1 KB block
-        static_assert(kGemmBN / 16 == 16, "one 16-byte transfer per lane covers the tile");
-        dma16(q.sr, q.so + (uint32_t)(st * 64 * NB), base + kOffWs);
-      }
+      // one dword per lane on every wave (no per-wave branch in the step)
+      static_assert(kGemmBN / 16 == 16, "4 waves of 256 bytes cover the tile's weight scales");
+      const int sk = (XG128 && !wsw) ? st >> 2 : st;
+      dma4(q.sr, q.so + (uint32_t)sk * q.sstep, base + s_lds);
     }
   };
   auto issue = [&](const GemmSrc& q, int st, int sg) {
@@ -451,22 +460,15 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     issue_op(q, st, sg, std::integral_constant<int, 2>{});
     issue_op(q, st, sg, std::integral_constant<int, 3>{});
     issue_op(q, st, sg, std::integral_constant<int, 4>{});
-    if constexpr (kDmaOps + 1 > 5) issue_op(q, st, sg, std::integral_constant<int, 5>{});
-    if constexpr (kDmaOps + 1 > 6) issue_op(q, st, sg, std::integral_constant<int, 6>{});
-    static_assert(kDmaOps + 1 <= 7, "issue covers up to 7 transfers");
+    static_assert(kDmaOps + 1 == 5, "issue covers 5 transfers");
   };
   // waits until this wave's transfers of the oldest stage in flight have
-  // landed: kGemmStages - 2 stages (kDmaOps + 1 transfers per step on waves
-  // 0-2, kDmaOps on the others) were issued after it
+  // landed: kGemmStages - 2 stages (kDmaOps + 1 transfers each) were issued
+  // after it
   constexpr int kWaitA = (kGemmStages - 2) * (kDmaOps + 1);
-  constexpr int kWaitB = (kGemmStages - 2) * kDmaOps;
   static_assert(kWaitA < 64, "vmcnt field");
-  constexpr int kScaleWaves = NATW ? 6 : 3;   // waves issuing a scale transfer per step
-  static_assert(kGemmWaves >= kScaleWaves, "scale transfers need their waves");
-  auto wait_stage = [&]() {
-    if (wid < kScaleWaves) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitA) : "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitB) : "memory");
-  };
+  static_assert(kGemmWaves == 8, "waves 0, 1, 6, 7 move scale words, waves 2-5 weight scales");
+  auto wait_stage = [&]() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitA) : "memory"); };
 
   int kc = 0;                            // the block's current item (k-th)
   int item = item_at(0);
@@ -504,25 +506,41 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
 #pragma unroll
       for (int i = 0; i < kGemmMB; ++i) acc[c][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // one k-step; FULL (all of the wave's row blocks live) runs without
-    // per-row-block branches
-    int cur_ks = 0;                      // the item's k-step (XG128 picks the scale byte by it)
-    auto step = [&](auto full) {
+    // The operands of one k-step in registers: the wave's 4 weight
+    // fragments and their scale word, the scale words of its row blocks, and
+    // the activation fragments of row block i in bf[i].
+    struct StepOps {
+      v4i af[kGemmCB];
+      int sa;
+      uint32_t xw[kGemmMB];
+      v8i bf[kGemmMB];
+    };
+    static_assert(kGemmCB == 4, "one scale word covers the wave's 4 column blocks");
+    // activation fragments of row block i of the current stage; a row block
+    // past the live ones is read as one broadcast word
+    auto read_b = [&](StepOps& o, int i, auto full) {
       constexpr bool FULL = decltype(full)::value;
-      // stage gs complete for this wave, then (barrier) for the block; the
-      // barrier also retires every read of the stage refilled below
+      const GemmStage& S = stage[gs % kGemmStages];
+      const bool live = FULL || i < mlive;
+      const uint8_t* xb = &S.x[0][0][0];
+      const int off = live ? (kGemmMB * rg + i) * 2048 + lane * 16 : 0;
+      const v4i lo4 = *reinterpret_cast<const v4i*>(xb + off);
+      const v4i hi4 = *reinterpret_cast<const v4i*>(xb + off + (live ? 1024 : 0));
+      o.bf[i] = v8i{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+    };
+    // the head of step gs: wait until its stage is complete for this wave,
+    // then (barrier) for the block, and read its weight fragments, scale
+    // words and the first two row blocks' activation fragments. The barrier
+    // also retires every read of the stage that step gs refills, provided
+    // each wave's reads of it have completed before the wave arrives.
+    auto head = [&](StepOps& o, auto full) {
       wait_stage();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       const GemmStage& S = stage[gs % kGemmStages];
-      // this wave's weight fragments, and its 4 scale bytes in one word
-      // (byte c for column block c, selected by the MFMA's op_sel)
-      v4i af[kGemmCB];
 #pragma unroll
       for (int c = 0; c < kGemmCB; ++c)
-        af[c] = *reinterpret_cast<const v4i*>(&S.w[kGemmCB * cg + c][lane * 16]);
-      static_assert(kGemmCB == 4, "one scale word covers the wave's 4 column blocks");
-      int sa;
+        o.af[c] = *reinterpret_cast<const v4i*>(&S.w[kGemmCB * cg + c][lane * 16]);
       if constexpr (NATW) {
         // byte g of tile row 16 (4 cg + c) + l16's dword, for c = 0..3
         const uint8_t* wsb = &S.ws[0][0];
@@ -530,82 +548,102 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
 #pragma unroll
         for (int c = 0; c < kGemmCB; ++c)
           v |= (uint32_t)wsb[(16 * (kGemmCB * cg + c) + l16) * 4 + g] << (8 * c);
-        sa = (int)v;
+        o.sa = (int)v;
       } else {
-        sa = (int)*reinterpret_cast<const uint32_t*>(&S.ws[0][0] + 256 * cg + 4 * lane);
+        o.sa = (int)*reinterpret_cast<const uint32_t*>(&S.ws[0][0] + 256 * cg + 4 * lane);
       }
-      // the scale words of the lane's row in every row block (two per LDS
-      // read); k-block g is byte g, moved to byte 0 for the MFMA
-      uint32_t xw[kGemmMB];
 #pragma unroll
-      for (int i = 0; i < kGemmMB; ++i) xw[i] = S.xs[16 * (kGemmMB * rg + i) + l16];
-      // activation fragments, read kGemmRD - 1 row blocks ahead of their
-      // MFMAs (LDS latency under this load spans several MFMA pairs); a row
-      // block past the live ones is read as one broadcast word
-      v8i bf[kGemmRD];
-      auto read_b = [&](int i) {
-        const bool live = FULL || i < mlive;
-        const uint8_t* xb = &S.x[0][0][0];
-        const int o = live ? (kGemmMB * rg + i) * 2048 + lane * 16 : 0;
-        const v4i lo4 = *reinterpret_cast<const v4i*>(xb + o);
-        const v4i hi4 = *reinterpret_cast<const v4i*>(xb + o + (live ? 1024 : 0));
-        bf[i % kGemmRD] = v8i{lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-      };
-#pragma unroll
-      for (int i = 0; i < kGemmRD - 1; ++i) read_b(i);
+      for (int i = 0; i < kGemmMB; ++i) o.xw[i] = S.xs[16 * (kGemmMB * rg + i) + l16];
+      read_b(o, 0, full);
+      read_b(o, 1, full);
+    };
+
+    // one k-step on operands whose head is in o. FULL (all of the wave's
+    // row blocks live) runs without per-row-block branches. PIPE: the next
+    // step's head is taken (into nx) before the last row block's MFMAs, so
+    // the matrix cores work through the barrier; nx must not be o.
+    int cur_ks = 0;                      // the item's k-step (XG128 picks the scale byte by it)
+    auto step = [&](StepOps& o, StepOps& nx, auto full, auto walk, auto pipe) {
+      constexpr bool FULL = decltype(full)::value;
+      constexpr bool WALK = decltype(walk)::value;
+      constexpr bool PIPE = decltype(pipe)::value;
       // transfers of the walker's step (3 ahead) into the stage the
       // previous step used
       const int sg = (gs + kGemmStages - 1) % kGemmStages;
-#if !GEMM_DMA_SPREAD
-      issue(ps, pst, sg);
-#endif
-#pragma unroll
-      for (int i = 0; i < kGemmMB; ++i) {
-        if (i + kGemmRD - 1 < kGemmMB) read_b(i + kGemmRD - 1);
+      const int xk = XG128 ? (cur_ks & 3) : g;    // scale byte of the step's k-block
+      auto mfmas = [&](int i) {
         if (FULL || i < mlive) {
-          const int sb = (int)(xw[i] >> (8 * (XG128 ? (cur_ks & 3) : g)));
+          const int sb = (int)(o.xw[i] >> (8 * xk));
           // op_sel must be a constant: one call per column block
           auto mfma = [&](auto cc) {
             constexpr int c = decltype(cc)::value;
             acc[c][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[c].xyzwxyzw, bf[i % kGemmRD], acc[c][i], 4, 0, c, sa, 0, sb);
+                o.af[c].xyzwxyzw, o.bf[i], acc[c][i], 4, 0, c, o.sa, 0, sb);
           };
           mfma(std::integral_constant<int, 0>{});
           mfma(std::integral_constant<int, 1>{});
           mfma(std::integral_constant<int, 2>{});
           mfma(std::integral_constant<int, 3>{});
         }
-#if GEMM_DMA_SPREAD
-        // two transfers after each row block's MFMAs, so the block's
-        // transfers spread over the step instead of queueing at its start
-        if (i == 0) {
-          issue_op(ps, pst, sg, std::integral_constant<int, 0>{});
-          issue_op(ps, pst, sg, std::integral_constant<int, 1>{});
-        } else if (i == 1) {
-          issue_op(ps, pst, sg, std::integral_constant<int, 2>{});
-          issue_op(ps, pst, sg, std::integral_constant<int, 3>{});
-        } else if (i == 2) {
-          issue_op(ps, pst, sg, std::integral_constant<int, 4>{});
-          if constexpr (kDmaOps + 1 > 5) issue_op(ps, pst, sg, std::integral_constant<int, 5>{});
-        } else if (i == 3) {
-          if constexpr (kDmaOps + 1 > 6) issue_op(ps, pst, sg, std::integral_constant<int, 6>{});
-        }
-#endif
-      }
-      advance();
+      };
+      static_assert(kGemmMB == 4 && kDmaOps + 1 == 5, "the step below spreads 5 transfers over 4 row blocks");
+      // two transfers after each of the first row blocks' MFMAs, so the
+      // block's transfers spread over the step instead of queueing at its
+      // start (the scheduling barriers keep this order)
+      read_b(o, 2, full);
+      mfmas(0);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_op(ps, pst, sg, std::integral_constant<int, 0>{});
+      issue_op(ps, pst, sg, std::integral_constant<int, 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(o, 3, full);
+      mfmas(1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_op(ps, pst, sg, std::integral_constant<int, 2>{});
+      issue_op(ps, pst, sg, std::integral_constant<int, 3>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(2);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_op(ps, pst, sg, std::integral_constant<int, 4>{});
+      __builtin_amdgcn_sched_barrier(0);
+      // the walker enters the next item only in an item's last 4 steps
+      // (it runs 3 ahead); before those the step body has no branch
+      if constexpr (WALK) advance(); else ++pst;
       ++gs;
+      if constexpr (PIPE) {
+        // this wave's reads of the stage are complete before it arrives
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        head(nx, full);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfmas(3);
+      __builtin_amdgcn_sched_barrier(0);
     };
-    if (mlive == kGemmMB) {
-      for (int ks = 0; ks < KS; ++ks) {
+    const int ks_plain = KS - 4;         // steps [0, KS - 4): no item change in the walker
+    auto run_item = [&](auto full) {
+      StepOps o[2];
+      head(o[0], full);
+      int ks = 0;
+      for (; ks + 2 <= ks_plain; ks += 2) {
         cur_ks = ks;
-        step(std::true_type{});
+        step(o[0], o[1], full, std::false_type{}, std::true_type{});
+        cur_ks = ks + 1;
+        step(o[1], o[0], full, std::false_type{}, std::true_type{});
       }
-    } else {
-      for (int ks = 0; ks < KS; ++ks) {
+      if (ks < ks_plain) {
         cur_ks = ks;
-        step(std::false_type{});
+        step(o[0], o[1], full, std::false_type{}, std::true_type{});
+        o[0] = o[1];
+        ++ks;
       }
-    }
+      for (; ks < KS; ++ks) {
+        cur_ks = ks;
+        step(o[0], o[1], full, std::true_type{}, std::false_type{});
+        if (ks + 1 < KS) head(o[0], full);
+      }
+    };
+    if (mlive == kGemmMB) run_item(std::true_type{});
+    else run_item(std::false_type{});
 
     if constexpr (!ACT) {
       // epilogue: lane holds columns 16cb + 4g .. +3 of row r0 + 16mb + l16
