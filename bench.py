@@ -314,7 +314,9 @@ def main():
                            else "grouped_mx_gemm_kernel<false, false, false> (moe_grouped_gemm1)"),
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
-                "alg_bytes_per_launch": int(bytes_[dom]), "avg_launch_us": round(dur_us[dom], 3)}
+                "alg_bytes_per_launch": int(bytes_[dom]), "avg_launch_us": round(dur_us[dom], 3),
+                # the same launch against the matrix cores (its FLOP / time / dense FP8 peak)
+                "mfma_frac_fp8_peak": kernels[dom]["mfma_frac_fp8_peak"]}
     tr = trace_avg_launch_us() if fused else None
     if tr is not None:
         # the same launches by the committed kernel trace (no event packets
