@@ -246,11 +246,6 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   // e * XW * slab)
   const int XW = XG128 ? (KS + 3) / 4 : KS;
   const int ss = slab > 0 ? slab : M_cap;
-  if constexpr (ACT) {
-    // published by the barriers of the chunk scan below
-    const float* tab = reinterpret_cast<const float*>(gemm_act::g_sigmoid_table);
-    for (int i = tid; i < kSigRows * 128; i += kGemmThreads) s_sig[i] = tab[sigmoid_compact_source(i)];
-  }
   const int NT = (N + kGemmBN - 1) / kGemmBN;
 
   // chunks per expert: full 128-row chunks and at most one partial one of
@@ -259,19 +254,44 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   // first the row blocks of e's partial chunk (0: none), then its rank among
   // all partial chunks by row blocks descending, ties by expert (0xFFFF: none)
   constexpr int kEPT = kGemmMaxE / kGemmThreads;   // experts per thread
+  // Every load of the prologue goes out before the first wait: this
+  // thread's experts' endpoints (clamped indices, unpredicated), then (the
+  // fused form) its share of the sigmoid values, which reach LDS only after
+  // the scan has used the endpoints.
+  int endv[kEPT], prevv[kEPT];
+#pragma unroll
+  for (int j = 0; j < kEPT; ++j) {
+    const int e = min(tid * kEPT + j, max(E_local - 1, 0));
+    endv[j] = expert_ends[e];
+    prevv[j] = expert_ends[max(e - 1, 0)];
+  }
+  constexpr int kSigN = ACT ? kSigRows * 128 : 1;
+  constexpr int kSigPer = (kSigN + kGemmThreads - 1) / kGemmThreads;
+  float sigv[kSigPer];
+  if constexpr (ACT) {
+    const float* tab = reinterpret_cast<const float*>(gemm_act::g_sigmoid_table);
+#pragma unroll
+    for (int j = 0; j < kSigPer; ++j) sigv[j] = tab[sigmoid_compact_source(min(tid + j * kGemmThreads, kSigN - 1))];
+  }
   int fcnt[kEPT], pblk[kEPT];
   int local_sum = 0;
 #pragma unroll
   for (int j = 0; j < kEPT; ++j) {
+    // expert e's live rows, as layout_range takes them from the endpoints
+    // (computed for every thread, kept for e < E_local: no branch between
+    // the loads and their use)
     const int e = tid * kEPT + j;
-    fcnt[j] = 0;
-    pblk[j] = 0;
-    if (e < E_local) {
-      int st, en;
-      layout_range(expert_ends, e, A, M_cap, slab, st, en);
-      fcnt[j] = (en - st) / kGemmBM;
-      pblk[j] = ((en - st) % kGemmBM + 15) >> 4;
+    int live_rows;
+    if (slab > 0) {
+      live_rows = min(max(endv[j], 0), slab);
+    } else {
+      const int prev = e == 0 ? 0 : min(max(prevv[j], 0), M_cap);
+      const int st = min(align_up_dev(prev, A), M_cap);
+      live_rows = min(max(endv[j], st), M_cap) - st;
     }
+    live_rows = e < E_local ? live_rows : 0;
+    fcnt[j] = live_rows / kGemmBM;
+    pblk[j] = (live_rows % kGemmBM + 15) >> 4;
     local_sum += fcnt[j];
   }
   int run = block_exclusive_scan(local_sum, s_tmp);
@@ -303,6 +323,12 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   for (int j = 0; j < kEPT; ++j) {
     const int e = tid * kEPT + j;
     if (e < E_local) s_pre[e] = (s_pre[e] & 0xFFFF) | ((pblk[j] > 0 ? prank[j] : 0xFFFF) << 16);
+  }
+  if constexpr (ACT) {
+    // published by the barrier below
+#pragma unroll
+    for (int j = 0; j < kSigPer; ++j)
+      if (tid + j * kGemmThreads < kSigN) s_sig[tid + j * kGemmThreads] = sigv[j];
   }
   __syncthreads();
   // LDS and global values the whole block agrees on are made scalar
@@ -369,8 +395,19 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
       c = (__builtin_amdgcn_readfirstlane(s_pre[e + 1]) & 0xFFFF) -
           (__builtin_amdgcn_readfirstlane(s_pre[e]) & 0xFFFF);        // e's full chunks
     }
+    // expert e's live rows, as layout_range takes them; both endpoint
+    // loads are issued before either is used (one round trip)
+    const int endv_e = expert_ends[e];
+    const int prevv_e = expert_ends[max(e - 1, 0)];
     int start, end;
-    layout_range(expert_ends, e, A, M_cap, slab, start, end);
+    if (slab > 0) {
+      start = e * slab;
+      end = start + min(max(endv_e, 0), slab);
+    } else {
+      const int prev = e == 0 ? 0 : min(max(prevv_e, 0), M_cap);
+      start = min(align_up_dev(prev, A), M_cap);
+      end = min(max(endv_e, start), M_cap);
+    }
     start = __builtin_amdgcn_readfirstlane(start);
     end = __builtin_amdgcn_readfirstlane(end);
     T.e = e;
