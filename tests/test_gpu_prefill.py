@@ -671,8 +671,12 @@ def _gemm_edge_case(ops, counts, A, K, N, seed):
     assert np.all(got[~live] == BF16_SENT)
 
 
-@pytest.mark.parametrize("K,N", [(128, 128), (256, 384), (384, 640), (1152, 256)])
+@pytest.mark.parametrize("K,N", [(128, 128), (256, 384), (384, 640), (512, 256), (768, 384),
+                                 (1152, 256)])
 def test_gemm_edge_layouts(ops, K, N):
+    """Edge layouts at k-step counts 1-9: the item walker changes item only in
+    an item's last 4 steps, so 4 steps (K = 512) have no step without it, 6
+    (K = 768) one pipelined pair, 5 and 9 an odd pipelined step."""
     say(f"gemm edge layouts K={K} N={N}")
     _gemm_edge_case(ops, [0, 128, 129, 1, 300, 0, 17], 128, K, N, seed=K + N)
 
@@ -726,14 +730,16 @@ def _fused_vs_two_call(ops, xq, xs, ends, A, w13, s13, clamp):
     return outs + [host(gateup)]
 
 
-@pytest.mark.parametrize("I,clamp", [(128, 0.0), (256, 6.0), (384, 0.0)])
-def test_gemm1_act_quant_fused_equals_two_calls(ops, I, clamp):
+@pytest.mark.parametrize("I,clamp,H", [(128, 0.0, 256), (256, 6.0, 640), (384, 0.0, 768)])
+def test_gemm1_act_quant_fused_equals_two_calls(ops, I, clamp, H):
     """Byte-identical hq / hs against the two-call path on the edge layouts
     (empty, exactly 128, 129, single-row and multi-chunk experts), padding
-    untouched; and the two-call path itself against the oracle's act-quant."""
-    say(f"fused gemm1+act-quant I={I} clamp={clamp}")
+    untouched; and the two-call path itself against the oracle's act-quant.
+    H = 640 and 768 put an odd and an even number of pipelined k-steps
+    before the item walker's last 4."""
+    say(f"fused gemm1+act-quant I={I} clamp={clamp} H={H}")
     rng = np.random.default_rng(I)
-    A, H = 128, 256
+    A = 128
     counts = [0, 128, 129, 1, 300, 0, 17]
     ends, prev = [], 0
     for cnt in counts:
