@@ -87,26 +87,30 @@ namespace gemm_act {
 
 namespace moe {
 
-constexpr int kGemmThreads = 512;  // 8 waves
 constexpr int kGemmBN = 256;       // columns per item (16 blocks of 16)
-constexpr int kGemmStages = 4;     // LDS ring depth (k-steps)
-constexpr int kGemmBlocksPerCU = 1;
-constexpr int kGemmWaves = kGemmThreads / 64;
 constexpr int kGemmBM = 128;       // rows per item (8 blocks of 16)
-constexpr int kGemmCB = 4;         // column blocks per wave (MFMA)
+constexpr int kGemmStages = 4;     // LDS ring depth (k-steps)
 constexpr int kGemmMB = 4;         // row blocks per wave (MFMA)
-constexpr int kGemmRG = kGemmBM / 16 / kGemmMB;         // row groups of waves
-constexpr int kGemmCG = kGemmBN / 16 / kGemmCB;         // column groups of waves
-constexpr int kDmaCB = kGemmBN / 16 / kGemmWaves;      // weight chunks a wave transfers per step
-constexpr int kDmaXR = kGemmBM / 16 / kGemmWaves;      // activation row blocks a wave transfers
 constexpr int kGemmMaxE = 1024;
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: reads zero, no traffic
-static_assert(kGemmRG * kGemmCG == kGemmThreads / 64, "wave grid");
-static_assert(kDmaCB * kGemmWaves == kGemmBN / 16 && kDmaXR * kGemmWaves == kGemmBM / 16,
-              "transfers split evenly over the waves");
-// transfers a wave issues per step: its weight chunks and 2 halves of each
-// of its row blocks, plus one scale transfer
-constexpr int kDmaOps = kDmaCB + 2 * kDmaXR;
+
+// The wave layout of a 128 x 256 tile: 8 waves in 2 row groups x 4 column
+// groups, each 64 rows x 64 columns (16 MFMAs and 12 KB of LDS reads per
+// step; accumulators in VGPRs).
+struct Gemm8 {
+  static constexpr int waves = 8;
+  static constexpr int threads = 64 * waves;
+  static constexpr int CB = 4;                             // column blocks per wave
+  static constexpr int CG = kGemmBN / 16 / CB;             // column groups of waves
+  static constexpr int RG = kGemmBM / 16 / kGemmMB;        // row groups of waves
+  static constexpr int dma_cb = kGemmBN / 16 / waves;      // weight chunks a wave moves per step
+  static constexpr int dma_xr = kGemmBM / 16 / waves;      // activation row blocks a wave moves
+  static constexpr int ops = dma_cb + 2 * dma_xr + 1;      // transfers a wave issues per step
+  static_assert(RG * CG == waves, "wave grid");
+  static_assert(dma_cb * waves == kGemmBN / 16 && dma_xr * waves == kGemmBM / 16,
+                "transfers split evenly over the waves");
+};
+constexpr int kGemmThreads = Gemm8::threads;
 
 // One LDS stage: everything one k-step of a 128 x 256 tile reads.
 //   x[mb][h]: activations of rows 16mb.. in B-fragment order (lane l: 16 bytes
@@ -174,7 +178,7 @@ struct GemmSrc {
   __amdgpu_buffer_rsrc_t wr, xr;
   __amdgpu_buffer_rsrc_t sr;   // the wave's scale source: the weight scales (waves 2-5)
                                // or the rows' activation scale words (the others)
-  uint32_t wo[kDmaCB];   // per-lane weight-code offsets of the wave's transferred blocks
+  uint32_t wo[Gemm8::dma_cb];  // per-lane weight-code offsets of the wave's transferred blocks
   uint32_t xo;           // per-lane activation offset of this wave's first row block
   uint32_t so;           // per-lane scale offset at k-step 0
   uint32_t sstep;        // its advance per k-step (per 4 k-steps for group-128 words)
@@ -182,10 +186,10 @@ struct GemmSrc {
 
 // The fused GEMM1 epilogue (ACT): the weights are packed with the gate and
 // up column blocks of each 128-column slice of h interleaved (tile nt holds
-// gate blocks 8nt..8nt+7 and the matching up blocks), so the wave of
-// column group cg holds gate blocks 2cg, 2cg+1 in acc[0..1] and their up
-// blocks in acc[2..3]. It rounds both to bf16 (what GEMM1 would store),
-// forms h = SiLU(g) * u and quantises one 32-column group per row exactly as
+// gate blocks 8nt..8nt+7 and the matching up blocks), so each group q of 4
+// packed column blocks holds gate blocks 2q, 2q+1 and their up blocks. The
+// epilogue rounds both to bf16 (what GEMM1 would store), forms h =
+// SiLU(g) * u and quantises one 32-column group per row exactly as
 // moe_act_quant_liverows does with those bf16 inputs, and writes hq / hs.
 struct GemmActOut {
   uint8_t* hq;       // [M_cap, I] E4M3
@@ -194,70 +198,33 @@ struct GemmActOut {
   float L;           // clamp limit (> 0: clamp)
 };
 
-static_assert(kGemmBN == 256 && kGemmCB == 4, "the fused epilogue pairs 2 gate and 2 up blocks per wave");
+static_assert(kGemmBN == 256, "the fused epilogue pairs 2 gate and 2 up blocks per group of 4");
 
 // With half > 0 (the gate/up form of w13, half = I/16 gate column blocks)
 // packed column block p takes source block src_cb(p): in each group of 16
-// (one 256-column tile), position 4cg + k holds gate block 8nt + 2cg + k for
-// k < 2 and the matching up block half + 8nt + 2cg + (k - 2) for k >= 2.
+// (one 256-column tile), position 4q + k holds gate block 8nt + 2q + k for
+// k < 2 and the matching up block half + 8nt + 2q + (k - 2) for k >= 2.
 __device__ __forceinline__ int src_cb(int p, int half) {
   if (half == 0) return p;
-  const int nt = p >> 4, l = p & 15, cg = l >> 2, k = l & 3;
-  return (k < 2 ? 0 : half) + 8 * nt + 2 * cg + (k & 1);
+  const int nt = p >> 4, l = p & 15, q = l >> 2, k = l & 3;
+  return (k < 2 ? 0 : half) + 8 * nt + 2 * q + (k & 1);
 }
 
-// XG128: activation scales of one UE8M0 byte per 128 columns, packed four
-// k-steps to a word ([ceil(K/512)][M_cap]); the byte of k-step ks is byte
-// ks % 4 of word ks / 4 and serves all four 32-column blocks of the step.
-// NATW: the weights in their checkpoint layout (codes [E][N][K/2], scales
-// [E][N][K/32]) instead of the packed one. Each lane's 16 code bytes of a
-// k-step are then the 64-byte run [64 ks + 16 (l/16), +16) of row
-// 16 cb + l%16 (the packed chunk is exactly these bytes, so the LDS stage is
-// the same), and the tile's scales of a k-step are one dword per weight row
-// (its 4 groups), moved by waves 2-5 and gathered into the MFMA's scale word
-// by 4 byte reads. With ACT the gate/up interleaving of the packed form is
-// an address mapping (src_cb).
-template <bool ACT, bool XG128, bool NATW>
-__global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gemm_kernel(
-    const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
-    const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int slab, int K, int N,
-    const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out,
-    GemmActOut act) {
-  __shared__ GemmStage stage[kGemmStages];
-  // per expert: full chunks before it (low 16 bits), partial chunks before
-  // it (high 16 bits)
-  __shared__ int s_pre[kGemmMaxE + 1];
-  __shared__ int s_tmp[kGemmWaves];
-  // the fused epilogue's sigmoid values (the compact subset of the table)
-  __shared__ __attribute__((aligned(16))) float s_sig[ACT ? kSigRows * 128 : 1];
-
+// The block's prologue. s_pre[e] holds, in its low
+// 16 bits, the full 128-row chunks before expert e (the host caps
+// M_cap / 128 < 2^16), and in its high 16 bits the rank of e's partial chunk
+// (1-8 row blocks) among all partial chunks, by row blocks descending, ties
+// by expert (0xFFFF: none); s_pre[E_local] is the number of full chunks F.
+// Every load goes out before the first wait: this thread's experts'
+// endpoints, then (ACT) its share of the compact sigmoid table, which
+// reaches s_sig only after the scan has used the endpoints. Returns F and
+// the number of partial chunks P, uniform over the block.
+template <int THREADS, bool ACT>
+__device__ __forceinline__ void gemm_prologue(const int32_t* __restrict__ expert_ends, int E_local,
+                                              int A, int M_cap, int slab, int* s_pre,
+                                              int* s_tmp, float* s_sig, int& F_out, int& P_out) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int rg = wid / kGemmCG;          // MFMA rows: row blocks [MB rg, MB rg + MB)
-  const int cg = wid % kGemmCG;          // MFMA columns: column blocks [CB cg, CB cg + CB)
-  const int l16 = lane & 15;
-  const int g = lane >> 4;
-  const int KS = K / 128;                // k-steps
-  const int NB = N / 16;                 // column blocks
-  // activation scale words per row, and the distance between a row's
-  // consecutive words: the whole buffer's rows (aligned layout) or one
-  // expert's slab (masked layout, where expert e's words start at
-  // e * XW * slab)
-  const int XW = XG128 ? (KS + 3) / 4 : KS;
-  const int ss = slab > 0 ? slab : M_cap;
-  const int NT = (N + kGemmBN - 1) / kGemmBN;
-
-  // chunks per expert: full 128-row chunks and at most one partial one of
-  // 1-8 row blocks. s_pre[e] holds, in its low 16 bits, the full chunks
-  // before e (the host caps M_cap / 128 < 2^16), and in its high 16 bits
-  // first the row blocks of e's partial chunk (0: none), then its rank among
-  // all partial chunks by row blocks descending, ties by expert (0xFFFF: none)
-  constexpr int kEPT = kGemmMaxE / kGemmThreads;   // experts per thread
-  // Every load of the prologue goes out before the first wait: this
-  // thread's experts' endpoints (clamped indices, unpredicated), then (the
-  // fused form) its share of the sigmoid values, which reach LDS only after
-  // the scan has used the endpoints.
+  constexpr int kEPT = kGemmMaxE / THREADS;   // experts per thread
   int endv[kEPT], prevv[kEPT];
 #pragma unroll
   for (int j = 0; j < kEPT; ++j) {
@@ -266,12 +233,12 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     prevv[j] = expert_ends[max(e - 1, 0)];
   }
   constexpr int kSigN = ACT ? kSigRows * 128 : 1;
-  constexpr int kSigPer = (kSigN + kGemmThreads - 1) / kGemmThreads;
+  constexpr int kSigPer = (kSigN + THREADS - 1) / THREADS;
   float sigv[kSigPer];
   if constexpr (ACT) {
     const float* tab = reinterpret_cast<const float*>(gemm_act::g_sigmoid_table);
 #pragma unroll
-    for (int j = 0; j < kSigPer; ++j) sigv[j] = tab[sigmoid_compact_source(min(tid + j * kGemmThreads, kSigN - 1))];
+    for (int j = 0; j < kSigPer; ++j) sigv[j] = tab[sigmoid_compact_source(min(tid + j * THREADS, kSigN - 1))];
   }
   int fcnt[kEPT], pblk[kEPT];
   int local_sum = 0;
@@ -301,7 +268,7 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     if (e < E_local) s_pre[e] = run | (pblk[j] << 16);
     run += fcnt[j];
   }
-  if (tid == kGemmThreads - 1) s_pre[E_local] = run;
+  if (tid == THREADS - 1) s_pre[E_local] = run;
   __syncthreads();
   // rank of each partial chunk (every thread walks all experts in step, so
   // each read is one broadcast); P counts the partial chunks
@@ -328,42 +295,51 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     // published by the barrier below
 #pragma unroll
     for (int j = 0; j < kSigPer; ++j)
-      if (tid + j * kGemmThreads < kSigN) s_sig[tid + j * kGemmThreads] = sigv[j];
+      if (tid + j * THREADS < kSigN) s_sig[tid + j * THREADS] = sigv[j];
   }
   __syncthreads();
-  // LDS and global values the whole block agrees on are made scalar
-  // (readfirstlane), so the buffer resources built from them stay in SGPRs
-  const int F = __builtin_amdgcn_readfirstlane(s_pre[E_local]);   // full chunks
-  P = __builtin_amdgcn_readfirstlane(P);                            // partial chunks
-  const int MT = F + P;                  // chunks of one n-tile
-  if (MT == 0) return;                   // no live rows (uniform over the block)
+  // values the whole block agrees on are made scalar (readfirstlane), so
+  // the buffer resources built from them stay in SGPRs
+  F_out = __builtin_amdgcn_readfirstlane(s_pre[E_local]);
+  P_out = __builtin_amdgcn_readfirstlane(P);
+}
 
-  // The schedule. Chunks are ranked by cost: the full ones first (expert
-  // order), then the partial ones by row blocks descending. The full chunks
-  // are cut into 8 contiguous runs, one per XCD, so the chunks of an expert
-  // with several share its weights in one L2 where they can; the partial
-  // chunks are dealt in snake order (the j-th partial of XCD x is partial
-  // 8j + x for even j, 8j + 7 - x for odd j). Every chunk goes with all its
-  // NT n-tiles, so the items of a chunk share its activations in that XCD's
-  // L2. An XCD lists its items chunk-major (costliest first), n-tile-minor,
-  // and its blocks take them in snake order over rounds of nslot items, so a
-  // block that got a costly item in one round gets a cheap one in the next.
-  // (Block b runs on XCD b % 8.)
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int nslot = gridDim.x >> 3;      // the grid is a multiple of 8
-  const int f0 = (int)(((long long)F * xcd) >> 3);          // this XCD's full chunks:
-  const int nf = (int)(((long long)F * (xcd + 1)) >> 3) - f0;   // ranks [f0, f0 + nf)
-  const int kr = P >> 3, rm = P & 7;     // full rounds of partial chunks, remainder
-  const int nx = nf + kr + (((kr & 1) ? 7 - xcd : xcd) < rm);   // chunks of this XCD
-  const int nitems = nx * NT;
+// The schedule. Chunks are ranked by cost: the full ones first (expert
+// order), then the partial ones by row blocks descending. The full chunks
+// are cut into 8 contiguous runs, one per XCD, so the chunks of an expert
+// with several share its weights in one L2 where they can; the partial
+// chunks are dealt in snake order (the j-th partial of XCD x is partial
+// 8j + x for even j, 8j + 7 - x for odd j). Every chunk goes with all its
+// NT n-tiles, so the items of a chunk share its activations in that XCD's
+// L2. An XCD lists its items chunk-major (costliest first), n-tile-minor,
+// and its blocks take them in snake order over rounds of nslot items, so a
+// block that got a costly item in one round gets a cheap one in the next.
+// (Block b runs on XCD b % 8; the grid is a multiple of 8.)
+struct GemmSchedule {
+  const int* s_pre;
+  int E_local, A, M_cap, slab, NT, NB, F, P;
+  int xcd, slot, nslot, f0, nf, nitems;
+
+  __device__ __forceinline__ void init(const int* pre, int E, int A_, int Mc, int sl, int nt, int nb,
+                                       int F_, int P_) {
+    s_pre = pre; E_local = E; A = A_; M_cap = Mc; slab = sl; NT = nt; NB = nb; F = F_; P = P_;
+    xcd = blockIdx.x & 7;
+    slot = blockIdx.x >> 3;
+    nslot = gridDim.x >> 3;
+    f0 = (int)(((long long)F * xcd) >> 3);                  // this XCD's full chunks:
+    nf = (int)(((long long)F * (xcd + 1)) >> 3) - f0;       // ranks [f0, f0 + nf)
+    const int kr = P >> 3, rm = P & 7;     // full rounds of partial chunks, remainder
+    const int nx = nf + kr + (((kr & 1) ? 7 - xcd : xcd) < rm);   // chunks of this XCD
+    nitems = nx * NT;
+  }
   // the block's k-th item (an index into the XCD's list), or -1 past its last
-  auto item_at = [&](int k) {
+  __device__ __forceinline__ int item_at(int k) const {
     const int u = nslot * k + ((k & 1) ? nslot - 1 - slot : slot);
     return u < nitems ? u : -1;
-  };
-
-  auto locate = [&](int item, GemmTile& T) {
+  }
+  __device__ __forceinline__ void locate(int item, GemmTile& T,
+                                         const int32_t* __restrict__ expert_ends) const {
+    const int lane = threadIdx.x & 63;
     const int kq = item / NT;
     const int nt = item - kq * NT;
     const int jp = kq - nf;                                  // partial index, if >= 0
@@ -416,7 +392,131 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     T.nblk = (T.rows + 15) >> 4;
     T.cb0 = nt * (kGemmBN / 16);
     T.ncb = min(kGemmBN / 16, NB - T.cb0);
-  };
+  }
+};
+
+// The fused activation of one row block and one h group: gate column
+// blocks g0, g1 and their up blocks u0, u1 of tile row mr (lane holds
+// columns 16c + 4(lane/16) .. +3 of each block and row mr = its row), for h
+// group q of slice nt (h columns 128 nt + 32 q ..). Runs on every lane of
+// the wave (the amax reduction and the small-sigma ballot are wave-wide).
+__device__ __forceinline__ void act_epilogue_group(const v4f& g0, const v4f& g1, const v4f& u0,
+                                                   const v4f& u1, const float* s_sig,
+                                                   const GemmActOut& act, const GemmTile& T,
+                                                   int mr, int nt, int q, int slab, int ss) {
+  const int g = (threadIdx.x & 63) >> 4;
+  // gate and up rounded to bf16 (RNE, NaN -> the quiet NaN 0x7FC0: the
+  // values moe_grouped_gemm1 stores), two per conversion
+  float gv[8], uv[8];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const v4f g4 = c == 0 ? g0 : g1, u4 = c == 0 ? u0 : u1;
+    const float ga[4] = {g4.x, g4.y, g4.z, g4.w};
+    const float ua[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = bf16x2_rne_bits(ga[k], ua[k]);
+      gv[4 * c + k] = ga[k] != ga[k] ? __uint_as_float(0x7FC00000u) : __uint_as_float(w << 16);
+      uv[4 * c + k] = ua[k] != ua[k] ? __uint_as_float(0x7FC00000u) : __uint_as_float(w & 0xFFFF0000u);
+    }
+  }
+  if (act.L > 0.f) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      gv[k] = fminf(gv[k], act.L);
+      uv[k] = fminf(fmaxf(uv[k], -act.L), act.L);
+    }
+  }
+  float sig[8];
+  bool small = false;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    sig[k] = sigmoid_lookup_compact_fast(s_sig, gv[k]);
+    small |= sigmoid_is_small(gv[k]);
+  }
+  if (__builtin_amdgcn_ballot_w64(small)) {                 // rare: |g| < 2^-15
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sig[k] = sigmoid_small_fix(gv[k], sig[k]);
+  }
+  float h[2][4];
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float sg = gv[k] * sig[k];
+    h[k >> 2][k & 3] = sg * uv[k];
+    amax = fmaxf(amax, fabsf(h[k >> 2][k & 3]));
+  }
+  // the 32-column group of this row spans lanes l16 + 16 g'
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  const uint32_t bsc = ue8m0_byte_of_amax(amax);
+  const float inv = e8m0_reciprocal(bsc);
+  if (mr < T.rows) {
+    const size_t row = (size_t)(T.r0 + mr);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t w = 0;
+      w = cvt_e4m3x2<false>(h[c][0] * inv, h[c][1] * inv, w);
+      w = cvt_e4m3x2<true>(h[c][2] * inv, h[c][3] * inv, w);
+      *reinterpret_cast<uint32_t*>(act.hq + row * act.I + 128 * nt + 32 * q + 16 * c + 4 * g) = w;
+    }
+    // byte q of the row's scale word of slice nt (group 4 nt + q)
+    if (g == 0) {
+      const size_t hs0 = slab > 0 ? (size_t)T.e * (size_t)(act.I / 128 - 1) * (size_t)slab : 0;
+      reinterpret_cast<uint8_t*>(act.hs)[(hs0 + (size_t)nt * ss + row) * 4 + q] = (uint8_t)bsc;
+    }
+  }
+}
+
+// XG128: activation scales of one UE8M0 byte per 128 columns, packed four
+// k-steps to a word ([ceil(K/512)][M_cap]); the byte of k-step ks is byte
+// ks % 4 of word ks / 4 and serves all four 32-column blocks of the step.
+// NATW: the weights in their checkpoint layout (codes [E][N][K/2], scales
+// [E][N][K/32]) instead of the packed one. Each lane's 16 code bytes of a
+// k-step are then the 64-byte run [64 ks + 16 (l/16), +16) of row
+// 16 cb + l%16 (the packed chunk is exactly these bytes, so the LDS stage is
+// the same), and the tile's scales of a k-step are one dword per weight row
+// (its 4 groups), moved by waves 2-5 and gathered into the MFMA's scale word
+// by 4 byte reads. With ACT the gate/up interleaving of the packed form is
+// an address mapping (src_cb).
+template <bool ACT, bool XG128, bool NATW>
+__global__ __launch_bounds__(Gemm8::threads, 1) void grouped_mx_gemm_kernel(
+    const uint8_t* __restrict__ X, const int32_t* __restrict__ Xs,
+    const int32_t* __restrict__ expert_ends, int E_local, int A, int M_cap, int slab, int K, int N,
+    const uint8_t* __restrict__ Wp, const uint8_t* __restrict__ Sp, uint16_t* __restrict__ out,
+    GemmActOut act) {
+  using L = Gemm8;
+  constexpr int kGemmCB = L::CB, kGemmCG = L::CG, kDmaCB = L::dma_cb, kDmaXR = L::dma_xr;
+  constexpr int kDmaOps = kDmaCB + 2 * kDmaXR;
+  __shared__ GemmStage stage[kGemmStages];
+  __shared__ int s_pre[kGemmMaxE + 1];
+  __shared__ int s_tmp[L::waves];
+  // the fused epilogue's sigmoid values (the compact subset of the table)
+  __shared__ __attribute__((aligned(16))) float s_sig[ACT ? kSigRows * 128 : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int rg = wid / kGemmCG;          // MFMA rows: row blocks [MB rg, MB rg + MB)
+  const int cg = wid % kGemmCG;          // MFMA columns: column blocks [CB cg, CB cg + CB)
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int KS = K / 128;                // k-steps
+  const int NB = N / 16;                 // column blocks
+  // activation scale words per row, and the distance between a row's
+  // consecutive words: the whole buffer's rows (aligned layout) or one
+  // expert's slab (masked layout, where expert e's words start at
+  // e * XW * slab)
+  const int XW = XG128 ? (KS + 3) / 4 : KS;
+  const int ss = slab > 0 ? slab : M_cap;
+  const int NT = (N + kGemmBN - 1) / kGemmBN;
+
+  int F, P;
+  gemm_prologue<L::threads, ACT>(expert_ends, E_local, A, M_cap, slab, s_pre, s_tmp, s_sig, F, P);
+  if (F + P == 0) return;                // no live rows (uniform over the block)
+  GemmSchedule sch;
+  sch.init(s_pre, E_local, A, M_cap, slab, NT, NB, F, P);
+
   // weight column block of packed position p (the gate/up interleave of the
   // fused form; identity otherwise)
   const int half = ACT ? act.I / 16 : 0;
@@ -497,21 +597,21 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
     issue_op(q, st, sg, std::integral_constant<int, 2>{});
     issue_op(q, st, sg, std::integral_constant<int, 3>{});
     issue_op(q, st, sg, std::integral_constant<int, 4>{});
-    static_assert(kDmaOps + 1 == 5, "issue covers 5 transfers");
+    static_assert(kDmaOps + 1 == 5 && L::ops == 5, "issue covers 5 transfers");
   };
   // waits until this wave's transfers of the oldest stage in flight have
   // landed: kGemmStages - 2 stages (kDmaOps + 1 transfers each) were issued
   // after it
   constexpr int kWaitA = (kGemmStages - 2) * (kDmaOps + 1);
   static_assert(kWaitA < 64, "vmcnt field");
-  static_assert(kGemmWaves == 8, "waves 0, 1, 6, 7 move scale words, waves 2-5 weight scales");
+  static_assert(L::waves == 8, "waves 0, 1, 6, 7 move scale words, waves 2-5 weight scales");
   auto wait_stage = [&]() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWaitA) : "memory"); };
 
   int kc = 0;                            // the block's current item (k-th)
-  int item = item_at(0);
+  int item = sch.item_at(0);
   bool valid = item >= 0;
   GemmTile T{0, 0, 1, 1, 0, 0};
-  if (valid) locate(item, T);
+  if (valid) sch.locate(item, T, expert_ends);
   // the transfer walker: item kp, step pst, its sources; it runs 3 steps
   // ahead of the compute and steps into the block's next item (or past the
   // last, into sources that read nothing) at an item's end
@@ -520,9 +620,9 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
   auto advance = [&]() {
     if (++pst == KS) {
       pst = 0;
-      const int u = item_at(++kp);
+      const int u = sch.item_at(++kp);
       GemmTile U = T;
-      if (u >= 0) locate(u, U);
+      if (u >= 0) sch.locate(u, U, expert_ends);
       ps = sources(U, u >= 0);
     }
   };
@@ -699,82 +799,22 @@ __global__ __launch_bounds__(kGemmThreads, kGemmBlocksPerCU) void grouped_mx_gem
         }
       }
     } else {
-      // fused activation: lane holds h columns 32cg + 16c + 4g .. +3 (c = 0, 1)
-      // of row r0 + 16mb + l16 of the 128-column slice nt = cb0 / 16
+      // fused activation: the wave's 4 column blocks are group cg of the
+      // 128-column slice nt = cb0 / 16
       const int nt = T.cb0 >> 4;
 #pragma unroll
       for (int i = 0; i < kGemmMB; ++i) {
         if (i >= mlive) continue;                            // wave-uniform
-        const int mr = 16 * (kGemmMB * rg + i) + l16;
-        // gate and up rounded to bf16 (RNE, NaN -> the quiet NaN 0x7FC0: the
-        // values moe_grouped_gemm1 stores), two per conversion
-        float gv[8], uv[8];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const v4f g4 = acc[c][i], u4 = acc[c + 2][i];
-          const float ga[4] = {g4.x, g4.y, g4.z, g4.w};
-          const float ua[4] = {u4.x, u4.y, u4.z, u4.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t w = bf16x2_rne_bits(ga[q], ua[q]);
-            gv[4 * c + q] = ga[q] != ga[q] ? __uint_as_float(0x7FC00000u) : __uint_as_float(w << 16);
-            uv[4 * c + q] = ua[q] != ua[q] ? __uint_as_float(0x7FC00000u) : __uint_as_float(w & 0xFFFF0000u);
-          }
-        }
-        if (act.L > 0.f) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            gv[q] = fminf(gv[q], act.L);
-            uv[q] = fminf(fmaxf(uv[q], -act.L), act.L);
-          }
-        }
-        float sig[8];
-        bool small = false;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          sig[q] = sigmoid_lookup_compact_fast(s_sig, gv[q]);
-          small |= sigmoid_is_small(gv[q]);
-        }
-        if (__builtin_amdgcn_ballot_w64(small)) {                 // rare: |g| < 2^-15
-#pragma unroll
-          for (int q = 0; q < 8; ++q) sig[q] = sigmoid_small_fix(gv[q], sig[q]);
-        }
-        float h[2][4];
-        float amax = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float sg = gv[q] * sig[q];
-          h[q >> 2][q & 3] = sg * uv[q];
-          amax = fmaxf(amax, fabsf(h[q >> 2][q & 3]));
-        }
-        // the 32-column group of this row spans lanes l16 + 16 g'
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const uint32_t bsc = ue8m0_byte_of_amax(amax);
-        const float inv = e8m0_reciprocal(bsc);
-        if (mr < T.rows) {
-          const size_t row = (size_t)(T.r0 + mr);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            uint32_t w = 0;
-            w = cvt_e4m3x2<false>(h[c][0] * inv, h[c][1] * inv, w);
-            w = cvt_e4m3x2<true>(h[c][2] * inv, h[c][3] * inv, w);
-            *reinterpret_cast<uint32_t*>(act.hq + row * act.I + 128 * nt + 32 * cg + 16 * c + 4 * g) = w;
-          }
-          // byte cg of the row's scale word of slice nt (group 4 nt + cg)
-          if (g == 0) {
-            const size_t hs0 = slab > 0 ? (size_t)T.e * (size_t)(act.I / 128 - 1) * (size_t)slab : 0;
-            reinterpret_cast<uint8_t*>(act.hs)[(hs0 + (size_t)nt * ss + row) * 4 + cg] = (uint8_t)bsc;
-          }
-        }
+        act_epilogue_group(acc[0][i], acc[1][i], acc[2][i], acc[3][i], s_sig, act, T,
+                           16 * (kGemmMB * rg + i) + l16, nt, cg, slab, ss);
       }
     }
     // (the stores above share the counter with the transfers; they may
     // complete before older transfers, but the transfers complete in order,
     // so counting transfers alone in wait_stage still waits for the stage)
-    item = item_at(++kc);
+    item = sch.item_at(++kc);
     valid = item >= 0;
-    if (valid) locate(item, T);
+    if (valid) sch.locate(item, T, expert_ends);
   }
   // every transfer this block issued has landed before its LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -844,23 +884,22 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
   // one resident block per CU; each walks its XCD's share of the item list
   const int NT = (N + kGemmBN - 1) / kGemmBN;
   const long long max_items = (long long)((M_cap + kGemmBM - 1) / kGemmBM + E_local) * NT;
-  const int resident = 256 * kGemmBlocksPerCU;
+  const int resident = 256;
   int grid = max_items < resident ? (int)max_items : resident;
   grid = (grid + 7) & ~7;
   if (natw && xg128) return MOE_ERR_UNSUPPORTED;   // natural weights with group-32 activations only
+  if (act && xg128) return MOE_ERR_UNSUPPORTED;    // the fused epilogue quantises per 32 columns
+  const GemmActOut a = act ? *act : GemmActOut{nullptr, nullptr, 0, 0.f};
   if (act) {
-    if (xg128) return MOE_ERR_UNSUPPORTED;   // the fused epilogue quantises per 32 columns
     auto kernel = natw ? grouped_mx_gemm_kernel<true, false, true> : grouped_mx_gemm_kernel<true, false, false>;
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kGemmThreads), 0,
-                       (hipStream_t)stream, X, Xs, ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out,
-                       *act);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(Gemm8::threads), 0, (hipStream_t)stream, X, Xs,
+                       ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out, a);
   } else {
     auto kernel = natw ? grouped_mx_gemm_kernel<false, false, true>
                   : xg128 ? grouped_mx_gemm_kernel<false, true, false>
                           : grouped_mx_gemm_kernel<false, false, false>;
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kGemmThreads), 0, (hipStream_t)stream, X, Xs,
-                       ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out,
-                       GemmActOut{nullptr, nullptr, 0, 0.f});
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(Gemm8::threads), 0, (hipStream_t)stream, X, Xs,
+                       ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out, a);
   }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
