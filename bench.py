@@ -364,16 +364,16 @@ def main():
 
 
 def bench_g128(ops, torch, up, c, ids, wts, logits_own, own_ids, own_w, log, steps=20, warmup=5):
-    """The same layer with the group-128 activation recipe (scatter, GEMM1,
-    act-quant and GEMM2 with one UE8M0 byte per 128 columns; GEMM1 and the
-    act-quant as two launches, since no fused form exists for this recipe):
-    per-kernel HIP-event times of eager steps and the graph-replayed step."""
+    """The same layer with the group-128 activation recipe (scatter, GEMM1
+    with its fused act-quant epilogue, and GEMM2, with one UE8M0 byte per 128
+    activation columns): per-kernel HIP-event times of eager steps and the
+    graph-replayed step."""
     w = c.weights
-    w13, s13 = ops.moe_pack_mx_weights(up(w.w13), up(w.s13))
+    w13, s13 = ops.moe_pack_mx_weights_gateup(up(w.w13), up(w.s13))
     w2, s2 = ops.moe_pack_mx_weights(up(w.w2), up(w.s2))
     x = torch.from_numpy(np.ascontiguousarray(c.x).view(np.int16)).cuda().view(torch.bfloat16)
     buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, group=128)
-    names = ["route", "scatter", "gemm1", "act_quant", "gemm2", "combine"]
+    names = ["route", "scatter", "gemm1_act", "gemm2", "combine"]
 
     def step(ev=None):
         def mark(i):
@@ -385,19 +385,18 @@ def bench_g128(ops, torch, up, c, ids, wts, logits_own, own_ids, own_w, log, ste
         ops.moe_scatter_endpoints(ids, 0, c.E_local, c.A, x, buf.expert_ends, buf.route_row,
                                   buf.xq, buf.xs, buf.workspace, group=128)
         mark(2)
-        ops.moe_grouped_gemm1(buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13, buf.gateup, group=128)
+        ops.moe_grouped_gemm1_act_quant(buf.xq, buf.xs, buf.expert_ends, c.A, w13, s13, 0.0, buf.hq,
+                                        buf.hs, group=128)
         mark(3)
-        ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, 0.0, buf.hq, buf.hs, group=128)
-        mark(4)
         ops.moe_grouped_gemm2(buf.hq, buf.hs, buf.expert_ends, c.A, w2, s2, buf.down, group=128)
-        mark(5)
+        mark(4)
         ops.moe_combine(buf.down, buf.route_row, wts, c.routed_scale, buf.out)
-        mark(6)
+        mark(5)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
@@ -416,7 +415,7 @@ def bench_g128(ops, torch, up, c, ids, wts, logits_own, own_ids, own_w, log, ste
     torch.cuda.empty_cache()
     log("recipe g128", round(us, 2), dur)
     return {"us_per_layer_graph": round(us, 2), "kernels_us": dur,
-            "note": "two-call GEMM1 + act-quant (no fused form for group 128)"}
+            "note": "GEMM1 with its fused group-128 act-quant epilogue"}
 
 
 def bench_masked(ops, torch, up, up_bf16, log, c, ids, wts, logits_own, own_ids, own_w, fused,

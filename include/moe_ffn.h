@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 13
+#define MOE_ABI_VERSION 14
 
 enum moe_status {
     MOE_OK = 0,
@@ -381,7 +381,11 @@ int moe_grouped_gemm1_act_quant_natural(const uint8_t* xq, const int32_t* xs,
  * weights keep their per-32 E8M0 scales). Same arguments, requirements,
  * ownership and errors as moe_scatter_endpoints, moe_grouped_gemm1,
  * moe_act_quant_liverows and moe_grouped_gemm2 respectively, except the
- * scale layout. No fused GEMM1 + act-quant form exists for this recipe.
+ * scale layout. moe_grouped_gemm1_act_quant_g128 is
+ * moe_grouped_gemm1_act_quant with group-128 input scales xs and group-128
+ * output scales hs ([SGL] section 2.4: act + quant fused); its hq and hs are
+ * byte-identical to moe_grouped_gemm1_g128 followed by
+ * moe_act_quant_liverows_g128.
  * ------------------------------------------------------------------------ */
 int moe_scatter_endpoints_g128(const int32_t* topk_ids, int T, int k, int expert_start,
                                int E_local, int A, int M_cap, const uint16_t* x, int H,
@@ -394,6 +398,11 @@ int moe_grouped_gemm1_g128(const uint8_t* xq, const int32_t* xs, const int32_t* 
 int moe_act_quant_liverows_g128(const uint16_t* gateup, const int32_t* expert_ends, int E_local,
                                 int A, int M_cap, int I, float clamp_limit, uint8_t* hq,
                                 int32_t* hs, void* stream);
+int moe_grouped_gemm1_act_quant_g128(const uint8_t* xq, const int32_t* xs,
+                                     const int32_t* expert_ends, int E_local, int A, int M_cap,
+                                     int H, int I, const uint8_t* w13_gateup_packed,
+                                     const uint8_t* w13_gateup_scale_packed, float clamp_limit,
+                                     uint8_t* hq, int32_t* hs, void* stream);
 int moe_grouped_gemm2_g128(const uint8_t* hq, const int32_t* hs, const int32_t* expert_ends,
                            int E_local, int A, int M_cap, int I, int H,
                            const uint8_t* w2_packed, const uint8_t* w2_scale_packed,

@@ -10,7 +10,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
-ABI_VERSION = 13
+ABI_VERSION = 14
 
 c_int, c_i64, c_size, c_float, c_void = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
                                          ctypes.c_float, ctypes.c_void_p)
@@ -48,6 +48,9 @@ SIGNATURES = {
                                             c_void, c_void, c_void]),
     "moe_grouped_gemm2_g128": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int,
                                        c_void, c_void, c_void, c_void]),
+    "moe_grouped_gemm1_act_quant_g128": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int,
+                                                 c_int, c_void, c_void, c_float, c_void, c_void,
+                                                 c_void]),
     "moe_grouped_gemm1_natural": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int,
                                           c_int, c_void, c_void, c_void, c_void]),
     "moe_grouped_gemm2_natural": (c_int, [c_void, c_void, c_void, c_int, c_int, c_int, c_int,

@@ -395,16 +395,15 @@ struct GemmSchedule {
   }
 };
 
-// The fused activation of one row block and one h group: gate column
-// blocks g0, g1 and their up blocks u0, u1 of tile row mr (lane holds
-// columns 16c + 4(lane/16) .. +3 of each block and row mr = its row), for h
-// group q of slice nt (h columns 128 nt + 32 q ..). Runs on every lane of
-// the wave (the amax reduction and the small-sigma ballot are wave-wide).
-__device__ __forceinline__ void act_epilogue_group(const v4f& g0, const v4f& g1, const v4f& u0,
-                                                   const v4f& u1, const float* s_sig,
-                                                   const GemmActOut& act, const GemmTile& T,
-                                                   int mr, int nt, int q, int slab, int ss) {
-  const int g = (threadIdx.x & 63) >> 4;
+// The fused activation of one row block and one 32-column h group: gate
+// column blocks g0, g1 and their up blocks u0, u1 (lane holds columns
+// 16c + 4(lane/16) .. +3 of each block). h[c][j] receives the lane's 8
+// values of h and the return value their group's amax (the 4 lanes l16 + 16
+// g' of a row agree on it). Runs on every lane of the wave (the amax
+// reduction and the small-sigma ballot are wave-wide).
+__device__ __forceinline__ float act_h_group(const v4f& g0, const v4f& g1, const v4f& u0,
+                                             const v4f& u1, const float* s_sig,
+                                             const GemmActOut& act, float (&h)[2][4]) {
   // gate and up rounded to bf16 (RNE, NaN -> the quiet NaN 0x7FC0: the
   // values moe_grouped_gemm1 stores), two per conversion
   float gv[8], uv[8];
@@ -438,7 +437,6 @@ __device__ __forceinline__ void act_epilogue_group(const v4f& g0, const v4f& g1,
 #pragma unroll
     for (int k = 0; k < 8; ++k) sig[k] = sigmoid_small_fix(gv[k], sig[k]);
   }
-  float h[2][4];
   float amax = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -449,7 +447,15 @@ __device__ __forceinline__ void act_epilogue_group(const v4f& g0, const v4f& g1,
   // the 32-column group of this row spans lanes l16 + 16 g'
   amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-  const uint32_t bsc = ue8m0_byte_of_amax(amax);
+  return amax;
+}
+
+// The E4M3 codes of a lane's 8 h values of tile row mr with the UE8M0 byte
+// bsc, at h columns 128 nt + 32 q + 16 c + 4(lane/16) .. +3 (c = 0, 1).
+__device__ __forceinline__ void act_store_codes(const float (&h)[2][4], uint32_t bsc,
+                                                const GemmActOut& act, const GemmTile& T, int mr,
+                                                int nt, int q) {
+  const int g = (threadIdx.x & 63) >> 4;
   const float inv = e8m0_reciprocal(bsc);
   if (mr < T.rows) {
     const size_t row = (size_t)(T.r0 + mr);
@@ -460,11 +466,24 @@ __device__ __forceinline__ void act_epilogue_group(const v4f& g0, const v4f& g1,
       w = cvt_e4m3x2<true>(h[c][2] * inv, h[c][3] * inv, w);
       *reinterpret_cast<uint32_t*>(act.hq + row * act.I + 128 * nt + 32 * q + 16 * c + 4 * g) = w;
     }
-    // byte q of the row's scale word of slice nt (group 4 nt + q)
-    if (g == 0) {
-      const size_t hs0 = slab > 0 ? (size_t)T.e * (size_t)(act.I / 128 - 1) * (size_t)slab : 0;
-      reinterpret_cast<uint8_t*>(act.hs)[(hs0 + (size_t)nt * ss + row) * 4 + q] = (uint8_t)bsc;
-    }
+  }
+}
+
+// The group-32 fused activation of one row block and one h group (group q
+// of slice nt): h, its own 32-column scale byte, the codes, and byte q of
+// the row's scale word of slice nt (group 4 nt + q).
+__device__ __forceinline__ void act_epilogue_group(const v4f& g0, const v4f& g1, const v4f& u0,
+                                                   const v4f& u1, const float* s_sig,
+                                                   const GemmActOut& act, const GemmTile& T,
+                                                   int mr, int nt, int q, int slab, int ss) {
+  const int g = (threadIdx.x & 63) >> 4;
+  float h[2][4];
+  const uint32_t bsc = ue8m0_byte_of_amax(act_h_group(g0, g1, u0, u1, s_sig, act, h));
+  act_store_codes(h, bsc, act, T, mr, nt, q);
+  if (mr < T.rows && g == 0) {
+    const size_t row = (size_t)(T.r0 + mr);
+    const size_t hs0 = slab > 0 ? (size_t)T.e * (size_t)(act.I / 128 - 1) * (size_t)slab : 0;
+    reinterpret_cast<uint8_t*>(act.hs)[(hs0 + (size_t)nt * ss + row) * 4 + q] = (uint8_t)bsc;
   }
 }
 
@@ -798,7 +817,7 @@ __global__ __launch_bounds__(Gemm8::threads, 1) void grouped_mx_gemm_kernel(
           *reinterpret_cast<uint2*>(out + (size_t)(T.r0 + mr) * N + n) = o;
         }
       }
-    } else {
+    } else if constexpr (!XG128) {
       // fused activation: the wave's 4 column blocks are group cg of the
       // 128-column slice nt = cb0 / 16
       const int nt = T.cb0 >> 4;
@@ -807,6 +826,42 @@ __global__ __launch_bounds__(Gemm8::threads, 1) void grouped_mx_gemm_kernel(
         if (i >= mlive) continue;                            // wave-uniform
         act_epilogue_group(acc[0][i], acc[1][i], acc[2][i], acc[3][i], s_sig, act, T,
                            16 * (kGemmMB * rg + i) + l16, nt, cg, slab, ss);
+      }
+    } else {
+      // fused activation, group-128 output: slice nt's 128 h columns are
+      // one group, spread over the 4 column-group waves of a row group; each
+      // wave's 32-column amax per row goes through LDS. The exchange uses
+      // the stage the item's last step read: the next transfer into it is
+      // issued after the next step's barrier. The first barrier lets every
+      // wave finish that last step's reads of it.
+      const int nt = T.cb0 >> 4;
+      float* xa = reinterpret_cast<float*>(&stage[(gs + kGemmStages - 1) % kGemmStages]);
+      float hv[kGemmMB][2][4];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kGemmMB; ++i) {
+        if (i >= mlive) continue;                            // wave-uniform
+        const float amax = act_h_group(acc[0][i], acc[1][i], acc[2][i], acc[3][i], s_sig, act, hv[i]);
+        if (g == 0) xa[((kGemmMB * rg + i) * 16 + l16) * 4 + cg] = amax;
+      }
+      __syncthreads();
+      const int NTh = act.I >> 7;          // 128-column groups of h
+#pragma unroll
+      for (int i = 0; i < kGemmMB; ++i) {
+        if (i >= mlive) continue;
+        const int mr = 16 * (kGemmMB * rg + i) + l16;
+        const v4f a4 = *reinterpret_cast<const v4f*>(&xa[((kGemmMB * rg + i) * 16 + l16) * 4]);
+        const float amax = fmaxf(fmaxf(a4.x, a4.y), fmaxf(a4.z, a4.w));
+        const uint32_t bsc = ue8m0_byte_of_amax(amax);
+        act_store_codes(hv[i], bsc, act, T, mr, nt, cg);
+        // byte nt % 4 of the row's word nt / 4; the bytes of groups past I
+        // in the last word are 0
+        if (cg == 0 && g == 0 && mr < T.rows) {
+          uint8_t* hb = reinterpret_cast<uint8_t*>(act.hs) + ((size_t)(nt >> 2) * ss + T.r0 + mr) * 4;
+          hb[nt & 3] = (uint8_t)bsc;
+          if (nt == NTh - 1)
+            for (int z = (nt & 3) + 1; z < 4; ++z) hb[z] = 0;
+        }
       }
     }
     // (the stores above share the counter with the transfers; they may
@@ -888,10 +943,12 @@ static int launch_grouped_gemm(const uint8_t* X, const int32_t* Xs, const int32_
   int grid = max_items < resident ? (int)max_items : resident;
   grid = (grid + 7) & ~7;
   if (natw && xg128) return MOE_ERR_UNSUPPORTED;   // natural weights with group-32 activations only
-  if (act && xg128) return MOE_ERR_UNSUPPORTED;    // the fused epilogue quantises per 32 columns
+  if (act && xg128 && slab > 0) return MOE_ERR_UNSUPPORTED;   // group 128: aligned layout only
   const GemmActOut a = act ? *act : GemmActOut{nullptr, nullptr, 0, 0.f};
   if (act) {
-    auto kernel = natw ? grouped_mx_gemm_kernel<true, false, true> : grouped_mx_gemm_kernel<true, false, false>;
+    auto kernel = natw    ? grouped_mx_gemm_kernel<true, false, true>
+                  : xg128 ? grouped_mx_gemm_kernel<true, true, false>
+                          : grouped_mx_gemm_kernel<true, false, false>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(Gemm8::threads), 0, (hipStream_t)stream, X, Xs,
                        ends, E_local, A, M_cap, slab, K, N, Wp, Sp, out, a);
   } else {
@@ -1017,6 +1074,24 @@ extern "C" int moe_grouped_gemm1_act_quant(const uint8_t* xq, const int32_t* xs,
   return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I,
                                   w13_gateup_packed, w13_gateup_scale_packed, nullptr, stream,
                                   &act);
+}
+
+extern "C" int moe_grouped_gemm1_act_quant_g128(const uint8_t* xq, const int32_t* xs,
+                                                const int32_t* expert_ends, int E_local, int A,
+                                                int M_cap, int H, int I,
+                                                const uint8_t* w13_gateup_packed,
+                                                const uint8_t* w13_gateup_scale_packed,
+                                                float clamp_limit, uint8_t* hq, int32_t* hs,
+                                                void* stream) {
+  if (I <= 0 || I % 128 != 0) return MOE_ERR_ALIGN;
+  float L;
+  if (fused_clamp(clamp_limit, L) != MOE_OK) return MOE_ERR_UNSUPPORTED;
+  if ((long long)M_cap * I >= (1LL << 31)) return MOE_ERR_SHAPE;
+  if (E_local > 0 && M_cap > 0 && (!hq || !hs)) return MOE_ERR_NULL;
+  const moe::GemmActOut act{hq, hs, I, L};
+  return moe::launch_grouped_gemm(xq, xs, expert_ends, E_local, A, M_cap, H, 2 * I,
+                                  w13_gateup_packed, w13_gateup_scale_packed, nullptr, stream,
+                                  &act, true);
 }
 
 extern "C" int moe_grouped_gemm1_masked(const uint8_t* xq, const int32_t* xs,

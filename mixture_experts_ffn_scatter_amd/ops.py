@@ -211,23 +211,26 @@ def moe_pack_mx_weights_gateup(w13, w13_scale):
 
 
 def moe_grouped_gemm1_act_quant(xq, xs, expert_ends, A: int, w13_gateup_packed,
-                                w13_gateup_scale_packed, clamp_limit: float, hq, hs):
+                                w13_gateup_scale_packed, clamp_limit: float, hq, hs,
+                                group: int = 32):
+    """``group`` 128: moe_grouped_gemm1_act_quant_g128 (xs and hs hold one
+    UE8M0 byte per 128 columns)."""
     M_cap, H = xq.shape
     E_local, twoI, _ = w13_gateup_packed.shape
     I = twoI // 2
     _req(xq, "xq", (torch.uint8,))
-    _req(xs, "xs", (torch.int32,), (H // 128, M_cap))
+    _req(xs, "xs", (torch.int32,), (scale_words(H, group), M_cap))
     _req(expert_ends, "expert_ends", (torch.int32,), (E_local,))
     _req(w13_gateup_packed, "w13_gateup_packed", (torch.uint8,), (E_local, 2 * I, H // 2))
     _req(w13_gateup_scale_packed, "w13_gateup_scale_packed", (torch.uint8,),
          packed_scale_shape(E_local, 2 * I, H))
     _req(hq, "hq", (torch.uint8,), (M_cap, I))
-    _req(hs, "hs", (torch.int32,), (I // 128, M_cap))
-    st = lib().moe_grouped_gemm1_act_quant(_ptr(xq), _ptr(xs), _ptr(expert_ends), E_local, A, M_cap,
-                                           H, I, _ptr(w13_gateup_packed),
-                                           _ptr(w13_gateup_scale_packed), float(clamp_limit),
-                                           _ptr(hq), _ptr(hs), _stream())
-    check(st, "moe_grouped_gemm1_act_quant")
+    _req(hs, "hs", (torch.int32,), (scale_words(I, group), M_cap))
+    fn = lib().moe_grouped_gemm1_act_quant if group == 32 else lib().moe_grouped_gemm1_act_quant_g128
+    st = fn(_ptr(xq), _ptr(xs), _ptr(expert_ends), E_local, A, M_cap, H, I,
+            _ptr(w13_gateup_packed), _ptr(w13_gateup_scale_packed), float(clamp_limit), _ptr(hq),
+            _ptr(hs), _stream())
+    check(st, "moe_grouped_gemm1_act_quant" + ("" if group == 32 else "_g128"))
 
 
 def moe_grouped_gemm1(xq, xs, expert_ends, A: int, w13_packed, w13_scale_packed, gateup,

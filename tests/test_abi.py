@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 13
+    assert lib.moe_abi_version() == 14
     for s in range(0, -10, -1):
         assert lib.moe_status_string(s).decode()
     assert lib.moe_status_string(5).decode() == "unknown status"

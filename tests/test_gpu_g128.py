@@ -112,3 +112,72 @@ def test_grouped_gemm_g128(ops, gemm, K, N):
         ok, _, _ = gemm_within_bound(got[rows], exact, tsum, K, bm)
         assert ok.all(), f"expert {e}: {np.count_nonzero(~ok)} of {ok.size} outside bound"
     assert np.all(got[~live] == BF16_SENT)
+
+
+@pytest.mark.parametrize("I,clamp,H", [(128, 0.0, 256), (640, 6.0, 640), (384, 0.0, 768)])
+def test_gemm1_act_quant_fused_g128_equals_two_calls(ops, I, clamp, H):
+    """moe_grouped_gemm1_act_quant_g128 against moe_grouped_gemm1(group 128)
+    then moe_act_quant_liverows(group 128), byte for byte, on the edge
+    layouts; I = 640 ends on a word with one group and three zero bytes; the
+    two-call path itself against the oracle's group-128 act-quant."""
+    say(f"fused gemm1+act-quant g128 I={I} clamp={clamp} H={H}")
+    rng = np.random.default_rng(I + H)
+    counts, A = [0, 128, 129, 1, 300, 0, 17], 128
+    E = len(counts)
+    start, end = M.endpoints(np.array(counts, np.int64), A)
+    M_cap = M.align_up(int(end[-1]), A)
+    xq = rng.integers(0, 256, size=(M_cap, H), dtype=np.uint8)
+    xq[(xq & 0x7F) == 0x7F] = 0x3C
+    b128 = rng.integers(118, 128, size=(M_cap, H // 128), dtype=np.uint8)
+    xs = np.ascontiguousarray(M.pack_g128_words(b128).T)
+    w13 = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
+    s13 = rng.integers(118, 128, size=(E, 2 * I, H // 32), dtype=np.uint8)
+    ends_d = dev(end.astype(np.int32))
+    wp, sp = ops.moe_pack_mx_weights(dev(w13), dev(s13))
+    gp, gs = ops.moe_pack_mx_weights_gateup(dev(w13), dev(s13))
+    gateup = torch.full((M_cap, 2 * I), BF16_SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    outs = []
+    for fused in (False, True):
+        hq = torch.full((M_cap, I), BYTE_SENT, dtype=torch.uint8, device="cuda")
+        hs = torch.full((_words(I), M_cap), int(WORD_SENT), dtype=torch.int32, device="cuda")
+        if fused:
+            ops.moe_grouped_gemm1_act_quant(dev(xq), dev(xs), ends_d, A, gp, gs, clamp, hq, hs, group=128)
+        else:
+            ops.moe_grouped_gemm1(dev(xq), dev(xs), ends_d, A, wp, sp, gateup, group=128)
+            ops.moe_act_quant_liverows(gateup, ends_d, A, clamp, hq, hs, group=128)
+        outs.append((host(hq), host(hs)))
+    (hq0, hs0), (hq1, hs1) = outs
+    assert np.array_equal(hq0, hq1), "FP8 codes differ"
+    assert np.array_equal(hs0, hs1), "packed scales differ"
+    live = M.live_row_mask(start, end, M_cap)
+    assert np.all(hq1[~live] == BYTE_SENT) and np.all(hs1[:, ~live] == WORD_SENT)
+    rows = np.flatnonzero(live)
+    q, b = M.act_quant_rows_g128(host(gateup)[rows], I, clamp)
+    assert np.array_equal(hq0[rows], q) and np.array_equal(hs0[:, rows].T, M.pack_g128_words(b))
+
+
+def test_prefill_layer_fused_g128_equals_two_calls(ops):
+    """The prefill EP-share GEMM1 at full size: fused group-128 output equals
+    the two-call group-128 output byte for byte."""
+    c = W.prefill()
+    w = c.weights
+    ids, _ = M.route_softmax(c.logits, c.k)
+    say("fused gemm1+act-quant g128, prefill EP share")
+    buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, fill=True, group=128)
+    xs = buf.xs
+    ops.moe_scatter_endpoints(dev(ids), 0, c.E_local, c.A, dev_bf16(c.x), buf.expert_ends, buf.route_row,
+                              buf.xq, xs, buf.workspace, group=128)
+    wp, sp = ops.moe_pack_mx_weights(dev(w.w13), dev(w.s13))
+    gp, gs = ops.moe_pack_mx_weights_gateup(dev(w.w13), dev(w.s13))
+    outs = []
+    for fused in (False, True):
+        hq = torch.full((c.M_cap, c.I), BYTE_SENT, dtype=torch.uint8, device="cuda")
+        hs = torch.full((_words(c.I), c.M_cap), int(WORD_SENT), dtype=torch.int32, device="cuda")
+        if fused:
+            ops.moe_grouped_gemm1_act_quant(buf.xq, xs, buf.expert_ends, c.A, gp, gs, c.clamp, hq, hs,
+                                            group=128)
+        else:
+            ops.moe_grouped_gemm1(buf.xq, xs, buf.expert_ends, c.A, wp, sp, buf.gateup, group=128)
+            ops.moe_act_quant_liverows(buf.gateup, buf.expert_ends, c.A, c.clamp, hq, hs, group=128)
+        outs.append((host(hq), host(hs)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
