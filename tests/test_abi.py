@@ -136,6 +136,15 @@ def test_host_validation_returns_errors_without_gpu_work(lib):
     assert lib.moe_grouped_gemm1_act_quant_natural(NULL, NULL, NULL, 8, 128, 1152, 256, 128,
                                                    NULL, NULL, ctypes.c_float(7.3), NULL, NULL,
                                                    NULL) == -5
+    # fused group-128 GEMM1 + act-quant: I not a multiple of 128, a clamp
+    # the sigma table does not cover, no output buffers
+    g = lib.moe_grouped_gemm1_act_quant_g128
+    assert g(NULL, NULL, NULL, 8, 128, 1152, 256, 200, NULL, NULL, ctypes.c_float(0.0), NULL, NULL,
+             NULL) == -3
+    assert g(NULL, NULL, NULL, 8, 128, 1152, 256, 128, NULL, NULL, ctypes.c_float(7.3), NULL, NULL,
+             NULL) == -5
+    assert g(NULL, NULL, NULL, 8, 128, 1152, 256, 128, NULL, NULL, ctypes.c_float(0.0), NULL, NULL,
+             NULL) == -1
     # masked slab forms: m_pad not a multiple of 4, E_local * m_pad too
     # large, m_pad 0 with experts (scatter), then the aligned forms' checks
     ms = [NULL, 64, 2, 0, 8, 130, NULL, 256, NULL, NULL, NULL, NULL, NULL, 0, NULL]
