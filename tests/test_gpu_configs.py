@@ -4,6 +4,7 @@
   of 256, this GPU's 32 experts, H=4,096, I=2,048): every live row of both
   GEMMs within the derived bound, act-quant and combine bit-exact, the final
   output of all 4,096 tokens against the oracle, and two runs bitwise equal;
+  the same layer at 64 and 1,024 tokens per GPU end to end;
 * the sparse decode layer (32 resident experts, H=2,880, top-4) at
   T = 1, 2, 4, 8 with FP8 and MXFP4 weights: each GEMV stage within a bound
   derived from the oracle's sum of |terms|, the GLU within one bf16 step,
@@ -128,6 +129,40 @@ def test_ep_share_layer_end_to_end(ops):
     assert ok, (mx, mean)
     no_local = ~np.any((ids >= 0) & (ids < c.E_local), axis=1)
     assert np.all(r["out"][no_local] == 0)
+
+
+@pytest.mark.parametrize("tokens_per_gpu", [64, 1024])
+def test_ep_share_layer_token_counts(ops, tokens_per_gpu):
+    """The same EP-share layer at 64 and 1,024 tokens per GPU (512- and
+    8,192-token groups): thin one-chunk experts, and many-chunk experts that
+    the schedule spreads over XCDs. Endpoints and route rows exact, combine
+    bit-exact from the GPU's down rows, the output against the oracle, and
+    tokens with no local route exactly zero."""
+    c = W.prefill(tokens_per_gpu=tokens_per_gpu)
+    w = c.weights
+    ids, wts = M.route_softmax(c.logits, c.k)
+    say(f"EP-share layer at {tokens_per_gpu} tokens/GPU: oracle")
+    ref = M.prefill_expert_major(c.x, ids, wts, 0, c.E_local, c.A, c.I, w.w13, w.s13, w.w2,
+                                 w.s2, workers=8)
+    sc = ref.scatter
+    live = M.live_row_mask(sc.start, sc.end, c.M_cap)
+    say(f"EP-share layer at {tokens_per_gpu} tokens/GPU: fused chain, T={c.T} M_cap={c.M_cap}")
+    gp = ops.moe_pack_mx_weights_gateup(dev(w.w13), dev(w.s13))
+    w2p = ops.moe_pack_mx_weights(dev(w.w2), dev(w.s2))
+    buf = ops.alloc_grouped(c.T, c.k, c.E_local, c.M_cap, c.H, c.I, fill=True)
+    y = ops.moe_ffn_prefill_fused(dev_bf16(c.x), dev(ids), dev(wts), 0, c.A, *gp, *w2p, buf)
+    out, down, rr = host(y), host(buf.down), host(buf.route_row)
+    assert np.array_equal(host(buf.expert_ends), sc.end.astype(np.int32))
+    assert np.array_equal(rr, sc.route_row)
+    assert np.all(down[~live] == BF16_SENT)
+    rows_f32 = F.bf16_to_f32(down).astype(np.float32)
+    rows_f32[~live] = 0.0
+    assert np.array_equal(out, M.combine(rows_f32, rr, wts, 1.0))
+    ok, mx, mean = end_to_end_ok(out, ref.out)
+    say(f"  max |d| / max |ref| = {mx:.3e}, mean |d| / rms(ref) = {mean:.3e}")
+    assert ok, (mx, mean)
+    no_local = ~np.any((ids >= 0) & (ids < c.E_local), axis=1)
+    assert np.all(out[no_local] == 0)
 
 
 # ------------------------------------------------------------ sparse decode
